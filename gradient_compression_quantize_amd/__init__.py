@@ -1,0 +1,317 @@
+"""gradient_compression_quantize_amd -- gradient quantization kernels for MI355X.
+
+Python binding of ``libgcq.so`` (HIP kernels for gfx950 behind the C ABI of
+``include/gcq.h``). Each function has the name of the C entry point it calls
+and only marshals arguments: torch tensors supply device memory and the
+stream, and every step of the computation runs in the library's kernels.
+There is no fallback: if ``libgcq.so`` is missing, ``load()`` raises.
+
+Two method families (see include/gcq.h for exact semantics):
+  * 2-bit threshold quantization with residual error feedback (apache MXNet
+    pull request #8342): compress_2bit, decompress_2bit, decompress_2bit_sum,
+    Plan2bitMulti / compress_2bit_multi;
+  * QSGDMaxNorm stochastic quantization and GlobalRandK (vineeths96
+    "Gradient-Compression"): qsgd_global_maxnorm, qsgd_maxnorm_quantize,
+    qsgd_dequant_sum, grandk_indices, gather_f32.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+from typing import Sequence
+
+LIB_PATH = pathlib.Path(__file__).resolve().parent / "libgcq.so"
+
+GC_OK = 0
+GC_EINVAL = -1
+GC_EHIP = -2
+GC_EUNSUPPORTED = -3
+GC_MAX_WORKERS = 64
+
+
+class GcqError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_f = ctypes.c_float
+_i = ctypes.c_int
+
+
+def load() -> ctypes.CDLL:
+    """Load libgcq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                "(or python gradient_compression_quantize_amd/build.py)")
+        _lib = _declare(ctypes.CDLL(str(LIB_PATH)))
+    return _lib
+
+
+def _declare(L):
+    L.gc_last_error.argtypes = []
+    L.gc_last_error.restype = ctypes.c_char_p
+    L.gc_compressed_2bit_words.argtypes = [_sz]
+    L.gc_compressed_2bit_words.restype = _sz
+    L.compress_2bit.argtypes = [_vp, _vp, _sz, _f, _f, _vp, _vp]
+    L.decompress_2bit.argtypes = [_vp, _sz, _vp, _i, _vp]
+    L.decompress_2bit_sum.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _vp]
+    L.gc_plan_2bit_multi_create.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                            ctypes.POINTER(_sz), _i, ctypes.POINTER(_vp)]
+    L.gc_plan_compressed_words.argtypes = [_vp]
+    L.gc_plan_compressed_words.restype = _sz
+    L.gc_plan_block_offsets.argtypes = [_vp, ctypes.POINTER(_sz)]
+    L.compress_2bit_multi.argtypes = [_vp, _f, _f, _vp, _vp]
+    L.gc_plan_destroy.argtypes = [_vp]
+    L.gc_plan_destroy.restype = None
+    L.qsgd_global_maxnorm.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _vp,
+                                      ctypes.POINTER(_sz), _vp]
+    L.qsgd_maxnorm_quantize.argtypes = [_vp, _sz, _vp, _i, ctypes.c_uint64, ctypes.c_uint32,
+                                        _vp, _vp]
+    L.qsgd_dequant_sum.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _i, _vp, _vp, _vp, _sz,
+                                   _vp]
+    L.grandk_indices.argtypes = [_sz, ctypes.c_uint32, ctypes.c_uint64, _vp, _vp,
+                                 ctypes.POINTER(_sz), _vp]
+    L.gather_f32.argtypes = [_vp, _vp, _sz, _vp, _vp]
+    for name in ("compress_2bit", "decompress_2bit", "decompress_2bit_sum",
+                 "gc_plan_2bit_multi_create", "gc_plan_block_offsets", "compress_2bit_multi",
+                 "qsgd_global_maxnorm", "qsgd_maxnorm_quantize", "qsgd_dequant_sum",
+                 "grandk_indices", "gather_f32"):
+        getattr(L, name).restype = _i
+    return L
+
+
+def last_error() -> str:
+    return load().gc_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != GC_OK:
+        raise GcqError(rc, last_error())
+
+
+# ---- marshalling helpers -------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return _vp(s.cuda_stream)
+
+
+def _dev(t, dtype, what: str) -> ctypes.c_void_p:
+    """Device pointer of a contiguous CUDA tensor of the given dtype."""
+    if t is None:
+        return _vp(None)
+    if not t.is_cuda:
+        raise TypeError(f"{what}: expected a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{what}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise TypeError(f"{what}: expected a contiguous tensor")
+    return _vp(t.data_ptr())
+
+
+def _ptr_array(ts, dtype, what: str):
+    arr = (_vp * len(ts))()
+    for k, t in enumerate(ts):
+        arr[k] = _dev(t, dtype, f"{what}[{k}]").value
+    return arr
+
+
+# ---- 2-bit threshold quantization -----------------------------------------
+
+def gc_compressed_2bit_words(n: int) -> int:
+    return int(load().gc_compressed_2bit_words(n))
+
+
+compressed_2bit_words = gc_compressed_2bit_words
+
+
+def compress_2bit(grad, residual, neg_threshold: float, pos_threshold: float, compr,
+                  stream=None) -> None:
+    torch = _torch()
+    n = grad.numel()
+    if residual.numel() != n:
+        raise ValueError("compress_2bit: grad and residual differ in size")
+    if compr.numel() < gc_compressed_2bit_words(n):
+        raise ValueError("compress_2bit: compr too small")
+    _check(load().compress_2bit(_dev(grad, torch.float32, "grad"),
+                                _dev(residual, torch.float32, "residual"), n,
+                                float(neg_threshold), float(pos_threshold),
+                                _dev(compr, torch.int32, "compr"), _stream(stream)))
+
+
+def decompress_2bit(compr, n: int, out, accumulate: bool = False, stream=None) -> None:
+    torch = _torch()
+    if compr.numel() < gc_compressed_2bit_words(n) or out.numel() < n:
+        raise ValueError("decompress_2bit: buffer too small")
+    _check(load().decompress_2bit(_dev(compr, torch.int32, "compr"), n,
+                                  _dev(out, torch.float32, "out"), int(bool(accumulate)),
+                                  _stream(stream)))
+
+
+def decompress_2bit_sum(comprs: Sequence, n: int, out, stream=None) -> None:
+    torch = _torch()
+    for c in comprs:
+        if c.numel() < gc_compressed_2bit_words(n):
+            raise ValueError("decompress_2bit_sum: compr too small")
+    if out.numel() < n:
+        raise ValueError("decompress_2bit_sum: out too small")
+    arr = _ptr_array(comprs, torch.int32, "compr")
+    _check(load().decompress_2bit_sum(arr, len(comprs), n, _dev(out, torch.float32, "out"),
+                                      _stream(stream)))
+
+
+class Plan2bitMulti:
+    """gc_plan_2bit_multi_create / compress_2bit_multi / gc_plan_destroy.
+    Holds references to the tensors so their memory outlives the plan."""
+
+    def __init__(self, grads: Sequence, residuals: Sequence):
+        torch = _torch()
+        if len(grads) != len(residuals) or not grads:
+            raise ValueError("Plan2bitMulti: need matching, non-empty tensor lists")
+        T = len(grads)
+        ns = (_sz * T)(*[g.numel() for g in grads])
+        for g, r in zip(grads, residuals):
+            if g.numel() != r.numel():
+                raise ValueError("Plan2bitMulti: grad and residual differ in size")
+        self._keep = (list(grads), list(residuals))
+        self.sizes = [g.numel() for g in grads]
+        handle = _vp()
+        _check(load().gc_plan_2bit_multi_create(_ptr_array(grads, torch.float32, "grads"),
+                                                _ptr_array(residuals, torch.float32, "residuals"),
+                                                ns, T, ctypes.byref(handle)))
+        self._handle = handle
+
+    @property
+    def compressed_words(self) -> int:
+        return int(load().gc_plan_compressed_words(self._handle))
+
+    def block_offsets(self) -> list[int]:
+        T = len(self.sizes)
+        out = (_sz * T)()
+        _check(load().gc_plan_block_offsets(self._handle, out))
+        return list(out)
+
+    def compress(self, neg_threshold: float, pos_threshold: float, compr_base,
+                 stream=None) -> None:
+        torch = _torch()
+        if compr_base.numel() < self.compressed_words:
+            raise ValueError("compress_2bit_multi: compr_base too small")
+        _check(load().compress_2bit_multi(self._handle, float(neg_threshold),
+                                          float(pos_threshold),
+                                          _dev(compr_base, torch.int32, "compr_base"),
+                                          _stream(stream)))
+
+    def destroy(self) -> None:
+        if getattr(self, "_handle", None) is not None and self._handle.value:
+            load().gc_plan_destroy(self._handle)
+        self._handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def compress_2bit_multi(plan: Plan2bitMulti, neg_threshold: float, pos_threshold: float,
+                        compr_base, stream=None) -> None:
+    plan.compress(neg_threshold, pos_threshold, compr_base, stream)
+
+
+# ---- QSGDMaxNorm ----------------------------------------------------------
+
+def qsgd_maxnorm_ws_bytes(W: int, n: int) -> int:
+    size = _sz(0)
+    _check(load().qsgd_global_maxnorm(None, W, n, None, None, ctypes.byref(size), None))
+    return int(size.value)
+
+
+def qsgd_global_maxnorm(grads: Sequence, norm, ws, stream=None) -> None:
+    """norm: 1-element float32 device tensor; ws: uint8 device tensor of at
+    least qsgd_maxnorm_ws_bytes(W, n) bytes."""
+    torch = _torch()
+    n = grads[0].numel()
+    for g in grads:
+        if g.numel() != n:
+            raise ValueError("qsgd_global_maxnorm: gradients differ in size")
+    size = _sz(ws.numel())
+    _check(load().qsgd_global_maxnorm(_ptr_array(grads, torch.float32, "grads"), len(grads), n,
+                                      _dev(norm, torch.float32, "norm"),
+                                      _dev(ws, torch.uint8, "ws"), ctypes.byref(size),
+                                      _stream(stream)))
+
+
+def qsgd_maxnorm_quantize(grad, norm, s: int, seed: int, worker: int, levels,
+                          stream=None) -> None:
+    torch = _torch()
+    n = grad.numel()
+    if levels.numel() < n:
+        raise ValueError("qsgd_maxnorm_quantize: levels too small")
+    _check(load().qsgd_maxnorm_quantize(_dev(grad, torch.float32, "grad"), n,
+                                        _dev(norm, torch.float32, "norm"), int(s), int(seed),
+                                        int(worker), _dev(levels, torch.int8, "levels"),
+                                        _stream(stream)))
+
+
+def qsgd_dequant_sum(levels: Sequence, norm, s: int, out, sums=None, scatter_idx=None,
+                     dense_n: int = 0, stream=None) -> None:
+    torch = _torch()
+    n = levels[0].numel()
+    for q in levels:
+        if q.numel() != n:
+            raise ValueError("qsgd_dequant_sum: level arrays differ in size")
+    if scatter_idx is None:
+        if out.numel() < n or (sums is not None and sums.numel() < n):
+            raise ValueError("qsgd_dequant_sum: output too small")
+    else:
+        if scatter_idx.numel() != n or out.numel() < dense_n:
+            raise ValueError("qsgd_dequant_sum: scatter_idx / out size mismatch")
+    _check(load().qsgd_dequant_sum(_ptr_array(levels, torch.int8, "levels"), len(levels), n,
+                                   _dev(norm, torch.float32, "norm"), int(s),
+                                   _dev(sums, torch.int32, "sums"),
+                                   _dev(out, torch.float32, "out"),
+                                   _dev(scatter_idx, torch.int32, "scatter_idx"),
+                                   int(dense_n), _stream(stream)))
+
+
+# ---- GlobalRandK ------------------------------------------------------------
+
+def grandk_ws_bytes(n: int, K: int) -> int:
+    size = _sz(0)
+    _check(load().grandk_indices(n, K, 0, None, None, ctypes.byref(size), None))
+    return int(size.value)
+
+
+def grandk_indices(n: int, K: int, seed: int, idx, ws, stream=None) -> None:
+    """idx: int32 device tensor of K elements (holding uint32 values < 2^31
+    for any n a torch int32 tensor can index); ws: uint8 device tensor."""
+    torch = _torch()
+    if idx.numel() < K:
+        raise ValueError("grandk_indices: idx too small")
+    size = _sz(ws.numel())
+    _check(load().grandk_indices(n, K, int(seed), _dev(idx, torch.int32, "idx"),
+                                 _dev(ws, torch.uint8, "ws"), ctypes.byref(size),
+                                 _stream(stream)))
+
+
+def gather_f32(x, idx, out, stream=None) -> None:
+    torch = _torch()
+    K = idx.numel()
+    if out.numel() < K:
+        raise ValueError("gather_f32: out too small")
+    _check(load().gather_f32(_dev(x, torch.float32, "x"), _dev(idx, torch.int32, "idx"), K,
+                             _dev(out, torch.float32, "out"), _stream(stream)))

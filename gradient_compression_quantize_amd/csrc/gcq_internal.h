@@ -1,0 +1,62 @@
+// gcq_internal.h -- shared pieces of libgcq.so (not installed, not part of
+// the ABI): error state, launch checks, and CDNA4 wavefront helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "gcq.h"
+
+#define GCQ_API extern "C" __attribute__((visibility("default")))
+
+namespace gcq {
+
+// Wavefront size of CDNA (gfx9 family, gfx950 included).
+constexpr int kWave = 64;
+
+// ---- error state ---------------------------------------------------------
+void set_error(const std::string& msg);
+void clear_error();
+int fail(gc_status code, const std::string& msg);
+// Checks the launch that was just enqueued on this thread.
+int check_launch(const char* what);
+const char* last_error();
+
+// ---- host helpers ----------------------------------------------------------
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+inline size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
+
+// Grid x-dimension cap for grid-stride kernels. Launch sizes stay far below
+// the 2^32 work-item limit; larger problems loop inside the kernel.
+constexpr size_t kMaxGridX = size_t(1) << 20;
+
+// W device pointers passed by value in the kernel argument segment.
+template <typename T>
+struct PtrTable {
+    const T* p[GC_MAX_WORKERS];
+};
+
+// ---- device helpers --------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
+
+// OR of a 32-bit value over the 4 lanes of a DPP quad (lanes 4k..4k+3);
+// every lane of the quad gets the result. Two quad_perm moves, no LDS.
+// quad_perm selectors: [1,0,3,2] = 0xB1 (xor 1), [2,3,0,1] = 0x4E (xor 2).
+__device__ __forceinline__ uint32_t quad_or(uint32_t x)
+{
+    x |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(x), 0xB1, 0xF, 0xF, true));
+    x |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(x), 0x4E, 0xF, 0xF, true));
+    return x;
+}
+
+}  // namespace gcq

@@ -1,0 +1,524 @@
+// qsgd.hip -- QSGDMaxNorm stochastic quantization, the simulated all-reduce
+// of its integer levels, and the GlobalRandK sparsified variant.
+//
+// Method: vineeths96 "Gradient-Compression" page ("Quantization for
+// Distributed Optimization"). "About The Project": the QSGDMaxNorm family is
+// all-reduce compatible -- every worker scales by the same max-norm, so the
+// integer levels of all workers can be summed and dequantized once.
+// "Results": GRandK-MN sparsifies to K = 10000 indices shared by all workers
+// before quantizing.
+//
+// Per element: level = sign(g) * floor(|g| / norm * s + u), u uniform from a
+// counter-based Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11), so every
+// element's random number is a pure function of (seed, worker, index).
+#include "gcq_internal.h"
+
+#include <algorithm>
+#include <cmath>
+
+namespace gcq {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---- Philox4x32-10 ---------------------------------------------------------
+// Round: two 32x32->64 products (counter words 0 and 2 with the Philox-4x32
+// multipliers); new words (hi_b ^ c1 ^ k0, lo_b, hi_a ^ c3 ^ k1, lo_a); the
+// key advances by the two Weyl increments between rounds.
+struct U4 {
+    uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t pa = uint64_t(0xD2511F53u) * c.x;
+        const uint64_t pb = uint64_t(0xCD9E8D57u) * c.z;
+        c = U4{uint32_t(pb >> 32) ^ c.y ^ k0, uint32_t(pb), uint32_t(pa >> 32) ^ c.w ^ k1,
+               uint32_t(pa)};
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+// ---- max |g| ---------------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float m)
+{
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1)
+        m = fmaxf(m, __shfl_xor(m, off));
+    return m;
+}
+
+// Workgroup max of m; valid in thread 0.
+template <int NT>
+__device__ __forceinline__ float block_max(float m)
+{
+    __shared__ float lds[NT / kWave];
+    m = wave_max(m);
+    const int wave = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0)
+        lds[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int k = 1; k < NT / kWave; ++k)
+            m = fmaxf(m, lds[k]);
+    }
+    return m;
+}
+
+constexpr unsigned kMaxPartialsPerWorker = 512;
+constexpr int kMaxAbsUnroll = 4;
+
+unsigned maxnorm_grid_x(size_t n)
+{
+    const size_t per_block = size_t(kThreads) * 4 * kMaxAbsUnroll;  // values per pass
+    return unsigned(std::max<size_t>(1, std::min<size_t>(ceil_div(n, per_block),
+                                                          kMaxPartialsPerWorker)));
+}
+
+// blockIdx.y = worker. Each workgroup writes the max |g| of its share.
+__global__ __launch_bounds__(kThreads) void maxabs_partial_kernel(PtrTable<float> tab, size_t n,
+                                                                  float* __restrict__ partials)
+{
+    const float* __restrict__ g = tab.p[blockIdx.y];
+    const size_t tid = size_t(blockIdx.x) * kThreads + threadIdx.x;
+    const size_t stride = size_t(gridDim.x) * kThreads;
+    float m = 0.0f;
+    if ((reinterpret_cast<uintptr_t>(g) & 15u) == 0) {
+        const f32x4* g4 = reinterpret_cast<const f32x4*>(g);
+        const size_t nfull = n >> 2;
+        size_t q = tid;
+        for (; q + (kMaxAbsUnroll - 1) * stride < nfull; q += kMaxAbsUnroll * stride) {
+            f32x4 v[kMaxAbsUnroll];
+#pragma unroll
+            for (int u = 0; u < kMaxAbsUnroll; ++u)
+                v[u] = __builtin_nontemporal_load(g4 + q + u * stride);
+#pragma unroll
+            for (int u = 0; u < kMaxAbsUnroll; ++u)
+                m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)),
+                                   fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
+        }
+        for (; q < nfull; q += stride) {
+            const f32x4 v = __builtin_nontemporal_load(g4 + q);
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+        for (size_t i = nfull * 4 + tid; i < n; i += stride)
+            m = fmaxf(m, fabsf(g[i]));
+    } else {
+        for (size_t i = tid; i < n; i += stride)
+            m = fmaxf(m, fabsf(g[i]));
+    }
+    m = block_max<kThreads>(m);
+    if (threadIdx.x == 0)
+        partials[size_t(blockIdx.y) * gridDim.x + blockIdx.x] = m;
+}
+
+constexpr int kFinalThreads = 1024;
+
+__global__ __launch_bounds__(kFinalThreads) void max_final_kernel(const float* __restrict__ partials,
+                                                                  unsigned count,
+                                                                  float* __restrict__ norm)
+{
+    float m = 0.0f;
+    for (unsigned i = threadIdx.x; i < count; i += kFinalThreads)
+        m = fmaxf(m, partials[i]);
+    m = block_max<kFinalThreads>(m);
+    if (threadIdx.x == 0)
+        *norm = m;
+}
+
+// ---- quantize --------------------------------------------------------------
+
+// floor(x + u) exactly, for x = (|g| / norm) * s (two fp32 roundings) and
+// u = (r >> 8) * 2^-24: with l = floor(x) and p = x - l (exact), the level
+// is l + 1 iff p >= 1 - u, and 1 - u = (2^24 - (r >> 8)) * 2^-24 is exact.
+__device__ __forceinline__ int qsgd_level(float g, uint32_t r, float norm, float s_f)
+{
+    const float a = fabsf(g);
+    const float x = (a / norm) * s_f;
+    const float l = floorf(x);
+    const float p = x - l;
+    const float one_minus_u = float(16777216u - (r >> 8)) * 0x1p-24f;
+    const int m = int(l) + (p >= one_minus_u ? 1 : 0);
+    return g < 0.0f ? -m : m;
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d)
+{
+    return (uint32_t(a) & 0xFFu) | ((uint32_t(b) & 0xFFu) << 8) | ((uint32_t(c) & 0xFFu) << 16) |
+           (uint32_t(d) << 24);
+}
+
+// One float4 slot q per lane per pass: Philox counter (q lo, q hi, worker, 0)
+// gives the four words of elements 4q .. 4q+3.
+__global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
+    const float* __restrict__ grad, size_t n, const float* __restrict__ norm_ptr, float s_f,
+    uint32_t k0, uint32_t k1, uint32_t worker, int8_t* __restrict__ levels, int vec)
+{
+    const float norm = *norm_ptr;
+    const size_t nslots = (n + 3) >> 2;
+    const size_t nfull = n >> 2;
+    const size_t stride = size_t(gridDim.x) * kThreads;
+    for (size_t q = size_t(blockIdx.x) * kThreads + threadIdx.x; q < nslots; q += stride) {
+        const bool full = vec && q < nfull;
+        f32x4 g;
+        if (full) {
+            g = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(grad) + q);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                g[k] = (q * 4 + k < n) ? grad[q * 4 + k] : 0.0f;
+        }
+        int lv0 = 0, lv1 = 0, lv2 = 0, lv3 = 0;
+        if (norm != 0.0f) {
+            const U4 r = philox4x32_10(U4{uint32_t(q), uint32_t(q >> 32), worker, 0u}, k0, k1);
+            lv0 = qsgd_level(g.x, r.x, norm, s_f);
+            lv1 = qsgd_level(g.y, r.y, norm, s_f);
+            lv2 = qsgd_level(g.z, r.z, norm, s_f);
+            lv3 = qsgd_level(g.w, r.w, norm, s_f);
+        }
+        if (full) {
+            __builtin_nontemporal_store(pack4(lv0, lv1, lv2, lv3),
+                                        reinterpret_cast<uint32_t*>(levels) + q);
+        } else {
+            const int lv[4] = {lv0, lv1, lv2, lv3};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (q * 4 + k < n)
+                    levels[q * 4 + k] = int8_t(lv[k]);
+        }
+    }
+}
+
+// ---- level sum + dequantize ------------------------------------------------
+
+__device__ __forceinline__ float dequant(float norm, int S, float s_f)
+{
+    const float t = norm * float(S);
+    return t / s_f;
+}
+
+__device__ __forceinline__ int sbyte(uint32_t w, int k)
+{
+    return int32_t(w << (24 - 8 * k)) >> 24;
+}
+
+// Dense form. vec: every level pointer 4-byte aligned, out 16-byte aligned,
+// sums NULL or 16-byte aligned.
+__global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_kernel(
+    PtrTable<int8_t> tab, int W, size_t n, const float* __restrict__ norm_ptr, float s_f,
+    int32_t* __restrict__ sums, float* __restrict__ out, int vec)
+{
+    const float norm = *norm_ptr;
+    const size_t nslots = (n + 3) >> 2;
+    const size_t nfull = n >> 2;
+    const size_t stride = size_t(gridDim.x) * kThreads;
+    for (size_t q = size_t(blockIdx.x) * kThreads + threadIdx.x; q < nslots; q += stride) {
+        if (vec && q < nfull) {
+            i32x4 S = {0, 0, 0, 0};
+            for (int w = 0; w < W; ++w) {
+                const uint32_t word =
+                    __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tab.p[w]) + q);
+                S.x += sbyte(word, 0);
+                S.y += sbyte(word, 1);
+                S.z += sbyte(word, 2);
+                S.w += sbyte(word, 3);
+            }
+            if (sums)
+                __builtin_nontemporal_store(S, reinterpret_cast<i32x4*>(sums) + q);
+            const f32x4 o = {dequant(norm, S.x, s_f), dequant(norm, S.y, s_f),
+                             dequant(norm, S.z, s_f), dequant(norm, S.w, s_f)};
+            __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(out) + q);
+        } else {
+            for (size_t i = q * 4; i < q * 4 + 4 && i < n; ++i) {
+                int S = 0;
+                for (int w = 0; w < W; ++w)
+                    S += int(tab.p[w][i]);
+                if (sums)
+                    sums[i] = S;
+                out[i] = dequant(norm, S, s_f);
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__ out, size_t n,
+                                                             int vec)
+{
+    const size_t stride = size_t(gridDim.x) * kThreads;
+    const size_t tid = size_t(blockIdx.x) * kThreads + threadIdx.x;
+    if (vec) {
+        const size_t nfull = n >> 2;
+        f32x4* o4 = reinterpret_cast<f32x4*>(out);
+        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (size_t q = tid; q < nfull; q += stride)
+            __builtin_nontemporal_store(z, o4 + q);
+        for (size_t i = nfull * 4 + tid; i < n; i += stride)
+            out[i] = 0.0f;
+    } else {
+        for (size_t i = tid; i < n; i += stride)
+            out[i] = 0.0f;
+    }
+}
+
+// Sparse form: value k lands at out[idx[k]] (out already zeroed).
+__global__ __launch_bounds__(kThreads) void qsgd_dequant_scatter_kernel(
+    PtrTable<int8_t> tab, int W, size_t K, const float* __restrict__ norm_ptr, float s_f,
+    int32_t* __restrict__ sums, float* __restrict__ out, const uint32_t* __restrict__ idx)
+{
+    const float norm = *norm_ptr;
+    const size_t stride = size_t(gridDim.x) * kThreads;
+    for (size_t k = size_t(blockIdx.x) * kThreads + threadIdx.x; k < K; k += stride) {
+        int S = 0;
+        for (int w = 0; w < W; ++w)
+            S += int(tab.p[w][k]);
+        if (sums)
+            sums[k] = S;
+        out[idx[k]] = dequant(norm, S, s_f);
+    }
+}
+
+// ---- GlobalRandK index draw -------------------------------------------------
+//
+// The draw is a partial Fisher-Yates shuffle of 0..n-1: step t swaps
+// positions t and j[t] >= t, and the index taken at step t is the value at
+// position j[t] just before step t. Position p >= T is changed before step T
+// only by earlier steps that targeted it, so its value before step T is:
+//   the value position t' held before step t', for the last t' < T with
+//   j[t'] == p; or p itself if no earlier step targeted it.
+// Following that rule from (p, T) = (j[t], t) down to a position nobody
+// targeted gives the index of step t, for every t in parallel. Draws are
+// hashed by target position (chained buckets) to find "the last t' < T".
+constexpr int kRandKThreads = 1024;
+
+__device__ __forceinline__ uint32_t slot_of(uint32_t p, int hbits)
+{
+    return (p * 0x9E3779B1u) >> (32 - hbits);
+}
+
+__global__ __launch_bounds__(kRandKThreads) void grandk_indices_kernel(
+    size_t n, uint32_t K, uint32_t k0, uint32_t k1, uint32_t* __restrict__ idx,
+    uint32_t* __restrict__ target, int32_t* __restrict__ next, int32_t* __restrict__ heads,
+    int hbits)
+{
+    const uint32_t nheads = 1u << hbits;
+    // draws; clear the buckets
+    for (uint32_t t = threadIdx.x; t < K; t += kRandKThreads) {
+        const U4 r = philox4x32_10(U4{t, 0u, 0u, 1u}, k0, k1);
+        const uint64_t R = (uint64_t(r.y) << 32) | r.x;
+        const uint64_t span = uint64_t(n) - t;
+        target[t] = t + uint32_t(__umul64hi(R, span));
+    }
+    for (uint32_t h = threadIdx.x; h < nheads; h += kRandKThreads)
+        heads[h] = -1;
+    __threadfence();
+    __syncthreads();
+    __threadfence();
+    // bucket every step by its target position
+    for (uint32_t t = threadIdx.x; t < K; t += kRandKThreads)
+        next[t] = atomicExch(&heads[slot_of(target[t], hbits)], int32_t(t));
+    __threadfence();
+    __syncthreads();
+    __threadfence();
+    // resolve
+    for (uint32_t t = threadIdx.x; t < K; t += kRandKThreads) {
+        uint32_t p = target[t];
+        int32_t T = int32_t(t);
+        for (;;) {
+            int32_t best = -1;
+            for (int32_t e = heads[slot_of(p, hbits)]; e >= 0; e = next[e])
+                if (target[e] == p && e < T && e > best)
+                    best = e;
+            if (best < 0)
+                break;
+            p = uint32_t(best);
+            T = best;
+        }
+        idx[t] = p;
+    }
+}
+
+int randk_hash_bits(uint32_t K)
+{
+    int b = 6;
+    while ((uint64_t(1) << b) < 2 * uint64_t(K))
+        ++b;
+    return b;
+}
+
+size_t randk_ws_bytes(uint32_t K)
+{
+    return 4 * ((size_t(1) << randk_hash_bits(K)) + 2 * size_t(K));
+}
+
+__global__ __launch_bounds__(kThreads) void gather_kernel(const float* __restrict__ x,
+                                                          const uint32_t* __restrict__ idx,
+                                                          size_t K, float* __restrict__ out)
+{
+    const size_t stride = size_t(gridDim.x) * kThreads;
+    for (size_t k = size_t(blockIdx.x) * kThreads + threadIdx.x; k < K; k += stride)
+        out[k] = x[idx[k]];
+}
+
+size_t grid_for(size_t items)
+{
+    return std::max<size_t>(1, std::min(ceil_div(items, kThreads), kMaxGridX));
+}
+
+}  // namespace
+}  // namespace gcq
+
+using namespace gcq;
+
+GCQ_API int qsgd_global_maxnorm(const float* const* grads, int W, size_t n, float* norm, void* ws,
+                                size_t* ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (W < 1 || W > GC_MAX_WORKERS)
+        return fail(GC_EINVAL, "qsgd_global_maxnorm: W must be in [1, 64]");
+    if (!ws_bytes)
+        return fail(GC_EINVAL, "qsgd_global_maxnorm: ws_bytes is NULL");
+    const unsigned gx = maxnorm_grid_x(n);
+    const size_t need = size_t(gx) * size_t(W) * sizeof(float);
+    if (!ws) {
+        *ws_bytes = need;
+        return GC_OK;
+    }
+    if (*ws_bytes < need || !aligned4(ws))
+        return fail(GC_EINVAL, "qsgd_global_maxnorm: workspace too small or misaligned");
+    if (!grads || !norm || !aligned4(norm))
+        return fail(GC_EINVAL, "qsgd_global_maxnorm: NULL or misaligned pointer");
+    PtrTable<float> tab{};
+    for (int w = 0; w < W; ++w) {
+        if ((n > 0 && !grads[w]) || !aligned4(grads[w]))
+            return fail(GC_EINVAL, "qsgd_global_maxnorm: a gradient pointer is NULL or misaligned");
+        tab.p[w] = grads[w];
+    }
+    float* partials = static_cast<float*>(ws);
+    hipLaunchKernelGGL(maxabs_partial_kernel, dim3(gx, unsigned(W)), dim3(kThreads), 0, stream,
+                       tab, n, partials);
+    if (int rc = check_launch("qsgd_global_maxnorm (partials)"))
+        return rc;
+    hipLaunchKernelGGL(max_final_kernel, dim3(1), dim3(kFinalThreads), 0, stream, partials,
+                       gx * unsigned(W), norm);
+    return check_launch("qsgd_global_maxnorm (final)");
+}
+
+GCQ_API int qsgd_maxnorm_quantize(const float* grad, size_t n, const float* norm, int s,
+                                  uint64_t seed, uint32_t worker, int8_t* levels,
+                                  hipStream_t stream)
+{
+    clear_error();
+    if (s < 1 || s > 127)
+        return fail(GC_EINVAL, "qsgd_maxnorm_quantize: s must be in [1, 127]");
+    if (!norm || !aligned4(norm))
+        return fail(GC_EINVAL, "qsgd_maxnorm_quantize: norm is NULL or misaligned");
+    if (n > 0 && (!grad || !levels))
+        return fail(GC_EINVAL, "qsgd_maxnorm_quantize: grad or levels is NULL with n > 0");
+    if (!aligned4(grad))
+        return fail(GC_EINVAL, "qsgd_maxnorm_quantize: grad must be 4-byte aligned");
+    if (n == 0)
+        return GC_OK;
+    const int vec = (aligned16(grad) && aligned4(levels)) ? 1 : 0;
+    hipLaunchKernelGGL(qsgd_quantize_kernel, dim3(grid_for(ceil_div(n, 4))), dim3(kThreads), 0,
+                       stream, grad, n, norm, float(s), uint32_t(seed), uint32_t(seed >> 32),
+                       worker, levels, vec);
+    return check_launch("qsgd_maxnorm_quantize");
+}
+
+GCQ_API int qsgd_dequant_sum(const int8_t* const* levels, int W, size_t n, const float* norm,
+                             int s, int32_t* sums, float* out, const uint32_t* scatter_idx,
+                             size_t dense_n, hipStream_t stream)
+{
+    clear_error();
+    if (W < 1 || W > GC_MAX_WORKERS)
+        return fail(GC_EINVAL, "qsgd_dequant_sum: W must be in [1, 64]");
+    if (s < 1 || s > 127)
+        return fail(GC_EINVAL, "qsgd_dequant_sum: s must be in [1, 127]");
+    if (!levels || !norm || !aligned4(norm))
+        return fail(GC_EINVAL, "qsgd_dequant_sum: NULL or misaligned pointer");
+    if (!aligned4(out) || !aligned4(sums) || !aligned4(scatter_idx))
+        return fail(GC_EINVAL, "qsgd_dequant_sum: out, sums and scatter_idx must be 4-byte aligned");
+    const size_t out_n = scatter_idx ? dense_n : n;
+    if (out_n > 0 && !out)
+        return fail(GC_EINVAL, "qsgd_dequant_sum: out is NULL");
+    if (scatter_idx && n > dense_n)
+        return fail(GC_EINVAL, "qsgd_dequant_sum: more scattered values than dense_n");
+    PtrTable<int8_t> tab{};
+    bool lv_aligned = true;
+    for (int w = 0; w < W; ++w) {
+        if (n > 0 && !levels[w])
+            return fail(GC_EINVAL, "qsgd_dequant_sum: a level pointer is NULL");
+        tab.p[w] = levels[w];
+        lv_aligned = lv_aligned && aligned4(levels[w]);
+    }
+    const float s_f = float(s);
+    if (!scatter_idx) {
+        if (n == 0)
+            return GC_OK;
+        const int vec = (lv_aligned && aligned16(out) && (!sums || aligned16(sums))) ? 1 : 0;
+        hipLaunchKernelGGL(qsgd_dequant_sum_kernel, dim3(grid_for(ceil_div(n, 4))),
+                           dim3(kThreads), 0, stream, tab, W, n, norm, s_f, sums, out, vec);
+        return check_launch("qsgd_dequant_sum");
+    }
+    if (dense_n > 0) {
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(ceil_div(dense_n, 4))), dim3(kThreads),
+                           0, stream, out, dense_n, aligned16(out) ? 1 : 0);
+        if (int rc = check_launch("qsgd_dequant_sum (fill)"))
+            return rc;
+    }
+    if (n == 0)
+        return GC_OK;
+    hipLaunchKernelGGL(qsgd_dequant_scatter_kernel, dim3(grid_for(n)), dim3(kThreads), 0, stream,
+                       tab, W, n, norm, s_f, sums, out, scatter_idx);
+    return check_launch("qsgd_dequant_sum (scatter)");
+}
+
+GCQ_API int grandk_indices(size_t n, uint32_t K, uint64_t seed, uint32_t* idx, void* ws,
+                           size_t* ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (!ws_bytes)
+        return fail(GC_EINVAL, "grandk_indices: ws_bytes is NULL");
+    if (n < 1 || n > (size_t(1) << 32) || size_t(K) > n)
+        return fail(GC_EINVAL, "grandk_indices: need 1 <= n <= 2^32 and K <= n");
+    if (K > (1u << 30))
+        return fail(GC_EUNSUPPORTED, "grandk_indices: K above 2^30");
+    const size_t need = randk_ws_bytes(K);
+    if (!ws) {
+        *ws_bytes = need;
+        return GC_OK;
+    }
+    if (*ws_bytes < need || !aligned4(ws))
+        return fail(GC_EINVAL, "grandk_indices: workspace too small or misaligned");
+    if (K > 0 && (!idx || !aligned4(idx)))
+        return fail(GC_EINVAL, "grandk_indices: idx is NULL or misaligned");
+    if (K == 0)
+        return GC_OK;
+    const int hbits = randk_hash_bits(K);
+    int32_t* heads = static_cast<int32_t*>(ws);
+    uint32_t* target = reinterpret_cast<uint32_t*>(heads + (size_t(1) << hbits));
+    int32_t* next = reinterpret_cast<int32_t*>(target + K);
+    hipLaunchKernelGGL(grandk_indices_kernel, dim3(1), dim3(kRandKThreads), 0, stream, n, K,
+                       uint32_t(seed), uint32_t(seed >> 32), idx, target, next, heads, hbits);
+    return check_launch("grandk_indices");
+}
+
+GCQ_API int gather_f32(const float* x, const uint32_t* idx, size_t K, float* out,
+                       hipStream_t stream)
+{
+    clear_error();
+    if (K > 0 && (!x || !idx || !out))
+        return fail(GC_EINVAL, "gather_f32: NULL pointer with K > 0");
+    if (!aligned4(x) || !aligned4(idx) || !aligned4(out))
+        return fail(GC_EINVAL, "gather_f32: buffers must be 4-byte aligned");
+    if (K == 0)
+        return GC_OK;
+    hipLaunchKernelGGL(gather_kernel, dim3(grid_for(K)), dim3(kThreads), 0, stream, x, idx, K,
+                       out);
+    return check_launch("gather_f32");
+}

@@ -1,0 +1,524 @@
+// twobit.hip -- 2-bit threshold quantization with residual error feedback,
+// its dequantization / W-worker sum, and the many-tensor launcher.
+//
+// Method: apache/incubator-mxnet PR #8342 "[WIP] 2bit gradient compression",
+// sections "Approach" (quantize before sending, keep the error as a
+// residual added to the next gradient), "Two bit quantization" (inclusive
+// thresholds, codes 01 / 10 / 00), "Format of compressed gradient" (header
+// of neg threshold, pos threshold, size; 16 codes per 32-bit element, first
+// value in the most significant pair), "Local kvstore" (every worker's
+// buffer is dequantized and summed on the reducing device).
+//
+// Layout and mapping (HBM-bound, ~12.25 bytes moved per element):
+//  - one wave owns a tile of kUnroll float4 slots per lane, lane-contiguous,
+//    so each load/store instruction moves 1 KiB of grad / residual;
+//  - the 4 codes of a lane's float4 form one byte; a DPP quad-OR joins the
+//    4 bytes of lanes 4k..4k+3 into the 32-bit word of 16 codes, and lane
+//    4k stores it: every payload word is written exactly once, with no
+//    atomics and no pre-zeroing of the output;
+//  - a float4 slot that straddles n is handled by scalar loads in the same
+//    lane; values past n take code 00 and are never read or written.
+#include "gcq_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+namespace gcq {
+namespace {
+
+constexpr int kThreads = 256;                          // 4 waves
+constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kUnroll = 4;                             // float4 per lane per tile
+constexpr size_t kTileF4 = size_t(kWave) * kUnroll;    // 256 float4 slots
+constexpr size_t kTileElems = kTileF4 * 4;             // 1024 values
+constexpr size_t kBlockElems = kTileElems * kWavesPerBlock;  // 4096 values
+
+__device__ __forceinline__ float code_value(uint32_t c, float neg, float pos)
+{
+    return c == 1u ? pos : (c == 2u ? neg : 0.0f);
+}
+
+// Code and residual of four values. Thresholds satisfy neg < 0 < pos, so at
+// most one of the two comparisons holds and value 0 is always code 00.
+__device__ __forceinline__ void classify4(f32x4 g, f32x4 r, float neg, float pos,
+                                          f32x4& rn, uint32_t& byte)
+{
+    byte = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float v = g[k] + r[k];
+        bool up = v >= pos;
+        bool dn = v <= neg;
+        float d = up ? pos : (dn ? neg : 0.0f);
+        rn[k] = v - d;
+        uint32_t c = up ? 1u : (dn ? 2u : 0u);
+        byte |= c << (6 - 2 * k);
+    }
+}
+
+// One wave tile: float4 slots q0 .. q0 + kTileF4 - 1 of a tensor of n values.
+// `payload` is the block's element 3 (first word of codes). kFull: every slot
+// of the tile lies below n / 4, so no lane needs a bounds check.
+template <bool kFull>
+__device__ __forceinline__ void compress_wave_tile(const float* __restrict__ grad,
+                                                   float* __restrict__ residual, size_t n,
+                                                   float neg, float pos,
+                                                   uint32_t* __restrict__ payload, size_t q0,
+                                                   int lane)
+{
+    const size_t nfull = n >> 2;           // float4 slots entirely below n
+    const size_t nwords = (n + 15) >> 4;
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(grad);
+    f32x4* r4 = reinterpret_cast<f32x4*>(residual);
+
+    f32x4 g[kUnroll], r[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const size_t q = q0 + size_t(u) * kWave + lane;
+        if (kFull || q < nfull) {
+            g[u] = __builtin_nontemporal_load(g4 + q);
+            r[u] = r4[q];
+        } else {
+            g[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            r[u] = g[u];
+            const size_t e = q * 4;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (e + k < n) {
+                    g[u][k] = grad[e + k];
+                    r[u][k] = residual[e + k];
+                }
+            }
+        }
+    }
+
+    const uint32_t shift = 24u - 8u * uint32_t(lane & 3);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const size_t q = q0 + size_t(u) * kWave + lane;
+        f32x4 rn;
+        uint32_t byte;
+        classify4(g[u], r[u], neg, pos, rn, byte);
+        if (kFull || q < nfull) {
+            __builtin_nontemporal_store(rn, r4 + q);
+        } else {
+            const size_t e = q * 4;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (e + k < n)
+                    residual[e + k] = rn[k];
+        }
+        // all 64 lanes reach this point together
+        const uint32_t word = quad_or(byte << shift);
+        const size_t j = q >> 2;
+        if ((lane & 3) == 0 && (kFull || j < nwords))
+            __builtin_nontemporal_store(word, payload + j);
+    }
+}
+
+__device__ __forceinline__ void compress_tile(const float* __restrict__ grad,
+                                              float* __restrict__ residual, size_t n, float neg,
+                                              float pos, uint32_t* __restrict__ payload,
+                                              size_t q0, int lane)
+{
+    if (q0 + kTileF4 <= (n >> 2))
+        compress_wave_tile<true>(grad, residual, n, neg, pos, payload, q0, lane);
+    else
+        compress_wave_tile<false>(grad, residual, n, neg, pos, payload, q0, lane);
+}
+
+__device__ __forceinline__ void write_header(uint32_t* blk, float neg, float pos, float n_f)
+{
+    blk[0] = f2u(neg);
+    blk[1] = f2u(pos);
+    blk[2] = f2u(n_f);
+}
+
+// 16-byte-aligned grad and residual.
+__global__ __launch_bounds__(kThreads) void compress_2bit_vec_kernel(
+    const float* __restrict__ grad, float* __restrict__ residual, size_t n, float neg,
+    float pos, float n_f, uint32_t* __restrict__ compr, size_t ntiles)
+{
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        write_header(compr, neg, pos, n_f);
+    const int lane = threadIdx.x & (kWave - 1);
+    const size_t stride = size_t(gridDim.x) * kWavesPerBlock;
+    for (size_t t = size_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; t < ntiles;
+         t += stride)
+        compress_tile(grad, residual, n, neg, pos, compr + 3, t * kTileF4, lane);
+}
+
+// One word of codes (16 values) by one thread, scalar accesses.
+__device__ __forceinline__ uint32_t compress_word_scalar(const float* __restrict__ grad,
+                                                         float* __restrict__ residual, size_t n,
+                                                         float neg, float pos, size_t j)
+{
+    uint32_t word = 0;
+    for (int k = 0; k < 16; ++k) {
+        const size_t i = j * 16 + k;
+        if (i >= n)
+            break;
+        const float v = grad[i] + residual[i];
+        const bool up = v >= pos;
+        const bool dn = v <= neg;
+        const float d = up ? pos : (dn ? neg : 0.0f);
+        residual[i] = v - d;
+        const uint32_t c = up ? 1u : (dn ? 2u : 0u);
+        word |= c << (30 - 2 * k);
+    }
+    return word;
+}
+
+// Any 4-byte alignment: one thread per word.
+__global__ __launch_bounds__(kThreads) void compress_2bit_scalar_kernel(
+    const float* __restrict__ grad, float* __restrict__ residual, size_t n, float neg,
+    float pos, float n_f, uint32_t* __restrict__ compr)
+{
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        write_header(compr, neg, pos, n_f);
+    const size_t nwords = (n + 15) >> 4;
+    const size_t stride = size_t(gridDim.x) * blockDim.x;
+    for (size_t j = size_t(blockIdx.x) * blockDim.x + threadIdx.x; j < nwords; j += stride)
+        compr[3 + j] = compress_word_scalar(grad, residual, n, neg, pos, j);
+}
+
+// One wave tile of the W-block dequantize-and-sum (see compress_wave_tile).
+template <bool kFull>
+__device__ __forceinline__ void decompress_wave_tile(const PtrTable<uint32_t>& tab, int W,
+                                                     size_t n, float* __restrict__ out,
+                                                     int accumulate, size_t q0, int lane)
+{
+    const size_t nfull = n >> 2;
+    const size_t nwords = (n + 15) >> 4;
+    const uint32_t shift = 24u - 8u * uint32_t(lane & 3);
+    f32x4* o4 = reinterpret_cast<f32x4*>(out);
+    f32x4 acc[kUnroll];
+    for (int w = 0; w < W; ++w) {
+        const uint32_t* __restrict__ b = tab.p[w];
+        const float neg = u2f(b[0]);
+        const float pos = u2f(b[1]);
+        uint32_t words[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const size_t j = (q0 + size_t(u) * kWave + lane) >> 2;
+            words[u] = (kFull || j < nwords) ? b[3 + j] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t byte = (words[u] >> shift) & 0xFFu;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float d = code_value((byte >> (6 - 2 * k)) & 3u, neg, pos);
+                acc[u][k] = (w == 0) ? d : acc[u][k] + d;
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const size_t q = q0 + size_t(u) * kWave + lane;
+        if (kFull || q < nfull) {
+            f32x4 v = acc[u];
+            if (accumulate)
+                v = o4[q] + v;
+            __builtin_nontemporal_store(v, o4 + q);
+        } else {
+            const size_t e = q * 4;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (e + k < n)
+                    out[e + k] = accumulate ? out[e + k] + acc[u][k] : acc[u][k];
+        }
+    }
+}
+
+// Dequantize-and-sum of W blocks into a 16-byte-aligned out.
+__global__ __launch_bounds__(kThreads) void decompress_2bit_vec_kernel(
+    PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, int accumulate,
+    size_t ntiles)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const size_t stride = size_t(gridDim.x) * kWavesPerBlock;
+    for (size_t t = size_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; t < ntiles;
+         t += stride) {
+        const size_t q0 = t * kTileF4;
+        if (q0 + kTileF4 <= (n >> 2))
+            decompress_wave_tile<true>(tab, W, n, out, accumulate, q0, lane);
+        else
+            decompress_wave_tile<false>(tab, W, n, out, accumulate, q0, lane);
+    }
+}
+
+// Any 4-byte-aligned out: one thread per value.
+__global__ __launch_bounds__(kThreads) void decompress_2bit_scalar_kernel(
+    PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, int accumulate)
+{
+    const size_t stride = size_t(gridDim.x) * blockDim.x;
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const uint32_t sh = 30u - 2u * uint32_t(i & 15);
+        float acc = 0.0f;
+        for (int w = 0; w < W; ++w) {
+            const uint32_t* b = tab.p[w];
+            const float d = code_value((b[3 + (i >> 4)] >> sh) & 3u, u2f(b[0]), u2f(b[1]));
+            acc = (w == 0) ? d : acc + d;
+        }
+        out[i] = accumulate ? out[i] + acc : acc;
+    }
+}
+
+// ---- many tensors ----------------------------------------------------------
+
+struct TensorDesc {
+    const float* grad;
+    float* residual;
+    uint64_t n;
+    uint64_t word_off;  // first uint32 element of this tensor's block
+    float n_f;          // (float)n, converted on the host
+    uint32_t vec_ok;    // grad and residual both 16-byte aligned
+};
+
+// One workgroup's share: kBlockElems values of one tensor.
+struct ChunkDesc {
+    uint32_t tensor;
+    uint32_t chunk;  // index of the kBlockElems-sized chunk inside the tensor
+};
+
+__global__ __launch_bounds__(kThreads) void compress_2bit_multi_kernel(
+    const TensorDesc* __restrict__ tensors, const ChunkDesc* __restrict__ chunks,
+    size_t nchunks, float neg, float pos, uint32_t* __restrict__ compr_base)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    for (size_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const ChunkDesc cd = chunks[c];
+        const TensorDesc td = tensors[cd.tensor];
+        uint32_t* blk = compr_base + td.word_off;
+        if (cd.chunk == 0 && threadIdx.x == 0)
+            write_header(blk, neg, pos, td.n_f);
+        if (td.vec_ok) {
+            const size_t q0 = size_t(cd.chunk) * (kBlockElems / 4) +
+                              size_t(threadIdx.x / kWave) * kTileF4;
+            compress_tile(td.grad, td.residual, td.n, neg, pos, blk + 3, q0, lane);
+        } else {
+            const size_t j = size_t(cd.chunk) * (kBlockElems / 16) + threadIdx.x;
+            if (j < ((td.n + 15) >> 4))
+                blk[3 + j] = compress_word_scalar(td.grad, td.residual, td.n, neg, pos, j);
+        }
+    }
+}
+
+static_assert(kBlockElems / 16 == kThreads, "scalar multi path: one word per thread");
+
+int check_thresholds(float neg, float pos)
+{
+    if (!(std::isfinite(neg) && std::isfinite(pos) && neg < 0.0f && pos > 0.0f))
+        return fail(GC_EINVAL, "thresholds must be finite with neg_threshold < 0 < pos_threshold");
+    return GC_OK;
+}
+
+size_t grid_for_tiles(size_t ntiles)
+{
+    return std::max<size_t>(1, std::min(ceil_div(ntiles, kWavesPerBlock), kMaxGridX));
+}
+
+}  // namespace
+}  // namespace gcq
+
+struct gc_plan {
+    int device = 0;
+    int T = 0;
+    size_t nchunks = 0;
+    size_t total_words = 0;
+    std::vector<size_t> offsets;
+    gcq::TensorDesc* d_tensors = nullptr;
+    gcq::ChunkDesc* d_chunks = nullptr;
+};
+
+using namespace gcq;
+
+GCQ_API size_t gc_compressed_2bit_words(size_t n) { return 3 + (n + 15) / 16; }
+
+GCQ_API int compress_2bit(const float* grad, float* residual, size_t n, float neg_threshold,
+                          float pos_threshold, uint32_t* compr, hipStream_t stream)
+{
+    clear_error();
+    if (!compr)
+        return fail(GC_EINVAL, "compress_2bit: compr is NULL");
+    if (n > 0 && (!grad || !residual))
+        return fail(GC_EINVAL, "compress_2bit: grad or residual is NULL with n > 0");
+    if (int rc = check_thresholds(neg_threshold, pos_threshold))
+        return rc;
+    if (!aligned4(compr) || !aligned4(grad) || !aligned4(residual))
+        return fail(GC_EINVAL, "compress_2bit: buffers must be 4-byte aligned");
+    const float n_f = static_cast<float>(n);
+    if (n == 0 || (aligned16(grad) && aligned16(residual))) {
+        const size_t ntiles = ceil_div(n, kTileElems);
+        hipLaunchKernelGGL(compress_2bit_vec_kernel, dim3(grid_for_tiles(ntiles)),
+                           dim3(kThreads), 0, stream, grad, residual, n, neg_threshold,
+                           pos_threshold, n_f, compr, ntiles);
+    } else {
+        const size_t blocks = std::min(ceil_div(ceil_div(n, 16), kThreads), kMaxGridX);
+        hipLaunchKernelGGL(compress_2bit_scalar_kernel, dim3(blocks), dim3(kThreads), 0,
+                           stream, grad, residual, n, neg_threshold, pos_threshold, n_f, compr);
+    }
+    return check_launch("compress_2bit");
+}
+
+static int launch_decompress(const PtrTable<uint32_t>& tab, int W, size_t n, float* out,
+                             int accumulate, hipStream_t stream, const char* what)
+{
+    if (n == 0)
+        return GC_OK;
+    if (aligned16(out)) {
+        const size_t ntiles = ceil_div(n, kTileElems);
+        hipLaunchKernelGGL(decompress_2bit_vec_kernel, dim3(grid_for_tiles(ntiles)),
+                           dim3(kThreads), 0, stream, tab, W, n, out, accumulate, ntiles);
+    } else {
+        const size_t blocks = std::min(ceil_div(n, kThreads), kMaxGridX);
+        hipLaunchKernelGGL(decompress_2bit_scalar_kernel, dim3(blocks), dim3(kThreads), 0,
+                           stream, tab, W, n, out, accumulate);
+    }
+    return check_launch(what);
+}
+
+GCQ_API int decompress_2bit(const uint32_t* compr, size_t n, float* out, int accumulate,
+                            hipStream_t stream)
+{
+    clear_error();
+    if (!compr)
+        return fail(GC_EINVAL, "decompress_2bit: compr is NULL");
+    if (n > 0 && !out)
+        return fail(GC_EINVAL, "decompress_2bit: out is NULL with n > 0");
+    if (accumulate != 0 && accumulate != 1)
+        return fail(GC_EINVAL, "decompress_2bit: accumulate must be 0 or 1");
+    if (!aligned4(compr) || !aligned4(out))
+        return fail(GC_EINVAL, "decompress_2bit: buffers must be 4-byte aligned");
+    PtrTable<uint32_t> tab{};
+    tab.p[0] = compr;
+    return launch_decompress(tab, 1, n, out, accumulate, stream, "decompress_2bit");
+}
+
+GCQ_API int decompress_2bit_sum(const uint32_t* const* compr, int W, size_t n, float* out,
+                                hipStream_t stream)
+{
+    clear_error();
+    if (!compr)
+        return fail(GC_EINVAL, "decompress_2bit_sum: compr is NULL");
+    if (W < 1 || W > GC_MAX_WORKERS)
+        return fail(GC_EINVAL, "decompress_2bit_sum: W must be in [1, 64]");
+    if (n > 0 && !out)
+        return fail(GC_EINVAL, "decompress_2bit_sum: out is NULL with n > 0");
+    if (!aligned4(out))
+        return fail(GC_EINVAL, "decompress_2bit_sum: out must be 4-byte aligned");
+    PtrTable<uint32_t> tab{};
+    for (int w = 0; w < W; ++w) {
+        if (!compr[w] || !aligned4(compr[w]))
+            return fail(GC_EINVAL, "decompress_2bit_sum: a block pointer is NULL or misaligned");
+        tab.p[w] = compr[w];
+    }
+    return launch_decompress(tab, W, n, out, 0, stream, "decompress_2bit_sum");
+}
+
+GCQ_API int gc_plan_2bit_multi_create(const float* const* grads, float* const* residuals,
+                                      const size_t* ns, int T, gc_plan** plan)
+{
+    clear_error();
+    if (!plan)
+        return fail(GC_EINVAL, "gc_plan_2bit_multi_create: plan is NULL");
+    *plan = nullptr;
+    if (T < 1 || !grads || !residuals || !ns)
+        return fail(GC_EINVAL, "gc_plan_2bit_multi_create: need T >= 1 and host arrays");
+
+    std::vector<TensorDesc> tensors(static_cast<size_t>(T));
+    std::vector<ChunkDesc> chunks;
+    std::vector<size_t> offsets(static_cast<size_t>(T));
+    size_t off = 0;
+    for (int t = 0; t < T; ++t) {
+        const size_t n = ns[t];
+        if (n > 0 && (!grads[t] || !residuals[t]))
+            return fail(GC_EINVAL, "gc_plan_2bit_multi_create: NULL tensor with n > 0");
+        if (!aligned4(grads[t]) || !aligned4(residuals[t]))
+            return fail(GC_EINVAL, "gc_plan_2bit_multi_create: tensors must be 4-byte aligned");
+        const size_t nch = std::max<size_t>(1, ceil_div(n, kBlockElems));
+        if (nch > 0xFFFFFFFFull)
+            return fail(GC_EUNSUPPORTED, "gc_plan_2bit_multi_create: tensor too large");
+        TensorDesc& d = tensors[static_cast<size_t>(t)];
+        d.grad = grads[t];
+        d.residual = residuals[t];
+        d.n = n;
+        d.word_off = off;
+        d.n_f = static_cast<float>(n);
+        d.vec_ok = (aligned16(grads[t]) && aligned16(residuals[t])) ? 1u : 0u;
+        offsets[static_cast<size_t>(t)] = off;
+        off += gc_compressed_2bit_words(n);
+        for (size_t c = 0; c < nch; ++c)
+            chunks.push_back(ChunkDesc{static_cast<uint32_t>(t), static_cast<uint32_t>(c)});
+    }
+
+    gc_plan* p = new gc_plan();
+    p->T = T;
+    p->nchunks = chunks.size();
+    p->total_words = off;
+    p->offsets = std::move(offsets);
+    if (hipGetDevice(&p->device) != hipSuccess ||
+        hipMalloc(&p->d_tensors, tensors.size() * sizeof(TensorDesc)) != hipSuccess ||
+        hipMalloc(&p->d_chunks, chunks.size() * sizeof(ChunkDesc)) != hipSuccess ||
+        hipMemcpy(p->d_tensors, tensors.data(), tensors.size() * sizeof(TensorDesc),
+                  hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(p->d_chunks, chunks.data(), chunks.size() * sizeof(ChunkDesc),
+                  hipMemcpyHostToDevice) != hipSuccess) {
+        const hipError_t e = hipGetLastError();
+        gc_plan_destroy(p);
+        return fail(GC_EHIP, std::string("gc_plan_2bit_multi_create: ") + hipGetErrorString(e));
+    }
+    *plan = p;
+    return GC_OK;
+}
+
+GCQ_API size_t gc_plan_compressed_words(const gc_plan* plan)
+{
+    return plan ? plan->total_words : 0;
+}
+
+GCQ_API int gc_plan_block_offsets(const gc_plan* plan, size_t* offsets)
+{
+    clear_error();
+    if (!plan || !offsets)
+        return fail(GC_EINVAL, "gc_plan_block_offsets: NULL argument");
+    std::copy(plan->offsets.begin(), plan->offsets.end(), offsets);
+    return GC_OK;
+}
+
+GCQ_API int compress_2bit_multi(gc_plan* plan, float neg_threshold, float pos_threshold,
+                                uint32_t* compr_base, hipStream_t stream)
+{
+    clear_error();
+    if (!plan || !compr_base)
+        return fail(GC_EINVAL, "compress_2bit_multi: NULL plan or compr_base");
+    if (int rc = check_thresholds(neg_threshold, pos_threshold))
+        return rc;
+    if (!aligned4(compr_base))
+        return fail(GC_EINVAL, "compress_2bit_multi: compr_base must be 4-byte aligned");
+    const size_t blocks = std::min(plan->nchunks, kMaxGridX);
+    hipLaunchKernelGGL(compress_2bit_multi_kernel, dim3(blocks), dim3(kThreads), 0, stream,
+                       plan->d_tensors, plan->d_chunks, plan->nchunks, neg_threshold,
+                       pos_threshold, compr_base);
+    return check_launch("compress_2bit_multi");
+}
+
+GCQ_API void gc_plan_destroy(gc_plan* plan)
+{
+    if (!plan)
+        return;
+    if (plan->d_tensors || plan->d_chunks) {
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(plan->device);
+        (void)hipDeviceSynchronize();
+        if (plan->d_tensors)
+            (void)hipFree(plan->d_tensors);
+        if (plan->d_chunks)
+            (void)hipFree(plan->d_chunks);
+        (void)hipSetDevice(cur);
+    }
+    delete plan;
+}

@@ -1,0 +1,132 @@
+"""The C-ABI boundary, without a GPU: libgcq.so loads, exports every entry
+point include/gcq.h declares (and nothing else), sizes its outputs like the
+oracle, and rejects bad arguments on the host before enqueuing anything.
+
+Only host-side paths are called here: validation failures and workspace-size
+queries return before any HIP call.
+"""
+import ctypes
+import math
+import pathlib
+import re
+import subprocess
+
+import pytest
+
+import gradient_compression_quantize_amd as gcq
+import oracle
+
+ROOT = pathlib.Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "gcq.h"
+
+NULL = None
+FAKE = 0x10000  # a 16-byte-aligned address that is never dereferenced
+
+
+def declared_functions() -> set[str]:
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return set(names)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not gcq.LIB_PATH.exists():
+        pytest.fail("libgcq.so is not built (run __graft_entry__.build())")
+    return gcq.load()
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for must in ("compress_2bit", "decompress_2bit", "decompress_2bit_sum",
+                 "qsgd_maxnorm_quantize", "qsgd_dequant_sum", "qsgd_global_maxnorm",
+                 "grandk_indices", "gather_f32", "compress_2bit_multi",
+                 "gc_plan_2bit_multi_create", "gc_plan_destroy", "gc_compressed_2bit_words",
+                 "gc_plan_compressed_words", "gc_plan_block_offsets", "gc_last_error"):
+        assert must in names, must
+
+
+def test_library_exports_exactly_the_declared_symbols(lib):
+    names = declared_functions()
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in gcq.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", str(gcq.LIB_PATH)],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert exported == names, (exported - names, names - exported)
+
+
+@pytest.mark.parametrize("n", [0, 1, 15, 16, 17, 4096, 25_557_032, 2 ** 33 + 5])
+def test_compressed_words_matches_oracle(lib, n):
+    assert lib.gc_compressed_2bit_words(n) == 3 + (n + 15) // 16
+    if n < 10 ** 8:
+        assert lib.gc_compressed_2bit_words(n) == oracle.compressed_2bit_words(n)
+
+
+def _rc_compress(lib, grad, res, n, neg, pos, compr):
+    return lib.compress_2bit(grad, res, n, neg, pos, compr, None)
+
+
+@pytest.mark.parametrize("neg,pos", [(0.0, 1.0), (-1.0, 0.0), (1.0, 2.0), (-2.0, -1.0),
+                                     (-math.inf, 1.0), (-1.0, math.inf), (math.nan, 1.0),
+                                     (-1.0, math.nan)])
+def test_compress_rejects_bad_thresholds(lib, neg, pos):
+    assert _rc_compress(lib, FAKE, FAKE, 16, neg, pos, FAKE) == gcq.GC_EINVAL
+    assert b"threshold" in lib.gc_last_error()
+    assert lib.compress_2bit_multi(FAKE, neg, pos, FAKE, None) == gcq.GC_EINVAL
+
+
+def test_compress_rejects_null_and_misaligned(lib):
+    assert _rc_compress(lib, FAKE, FAKE, 16, -1.0, 1.0, NULL) == gcq.GC_EINVAL
+    assert _rc_compress(lib, NULL, FAKE, 16, -1.0, 1.0, FAKE) == gcq.GC_EINVAL
+    assert _rc_compress(lib, FAKE, NULL, 16, -1.0, 1.0, FAKE) == gcq.GC_EINVAL
+    assert _rc_compress(lib, FAKE + 2, FAKE, 16, -1.0, 1.0, FAKE) == gcq.GC_EINVAL
+    assert _rc_compress(lib, FAKE, FAKE, 16, -1.0, 1.0, FAKE + 1) == gcq.GC_EINVAL
+
+
+def test_decompress_rejects_bad_arguments(lib):
+    assert lib.decompress_2bit(NULL, 16, FAKE, 0, None) == gcq.GC_EINVAL
+    assert lib.decompress_2bit(FAKE, 16, NULL, 0, None) == gcq.GC_EINVAL
+    assert lib.decompress_2bit(FAKE, 16, FAKE, 2, None) == gcq.GC_EINVAL
+    arr = (ctypes.c_void_p * 65)(*([FAKE] * 65))
+    assert lib.decompress_2bit_sum(arr, 0, 16, FAKE, None) == gcq.GC_EINVAL
+    assert lib.decompress_2bit_sum(arr, 65, 16, FAKE, None) == gcq.GC_EINVAL
+    arr[1] = None
+    assert lib.decompress_2bit_sum(arr, 2, 16, FAKE, None) == gcq.GC_EINVAL
+
+
+def test_qsgd_rejects_bad_arguments(lib):
+    for s in (0, 128, -1):
+        assert lib.qsgd_maxnorm_quantize(FAKE, 16, FAKE, s, 0, 0, FAKE, None) == gcq.GC_EINVAL
+    assert lib.qsgd_maxnorm_quantize(FAKE, 16, NULL, 7, 0, 0, FAKE, None) == gcq.GC_EINVAL
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    for W in (0, 65):
+        assert lib.qsgd_dequant_sum(arr, W, 16, FAKE, 7, NULL, FAKE, NULL, 0, None) == gcq.GC_EINVAL
+    assert lib.qsgd_dequant_sum(arr, 2, 16, FAKE, 0, NULL, FAKE, NULL, 0, None) == gcq.GC_EINVAL
+    # more scattered values than the dense output holds
+    assert lib.qsgd_dequant_sum(arr, 2, 16, FAKE, 7, NULL, FAKE, FAKE, 8, None) == gcq.GC_EINVAL
+
+
+def test_workspace_queries(lib):
+    size = ctypes.c_size_t(0)
+    assert lib.qsgd_global_maxnorm(None, 8, 138_357_544, None, None, ctypes.byref(size), None) == 0
+    assert 0 < size.value <= 8 * 512 * 4
+    small = ctypes.c_size_t(size.value - 4)
+    arr = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    assert lib.qsgd_global_maxnorm(arr, 8, 138_357_544, FAKE, FAKE, ctypes.byref(small),
+                                   None) == gcq.GC_EINVAL
+    assert lib.grandk_indices(25_557_032, 10_000, 0, None, None, ctypes.byref(size), None) == 0
+    assert size.value == 4 * (32768 + 2 * 10_000)
+    assert lib.grandk_indices(10, 11, 0, None, None, ctypes.byref(size), None) == gcq.GC_EINVAL
+    assert lib.grandk_indices(2 ** 32 + 1, 1, 0, None, None, ctypes.byref(size), None) == gcq.GC_EINVAL
+
+
+def test_plan_rejects_bad_arguments(lib):
+    handle = ctypes.c_void_p()
+    ns = (ctypes.c_size_t * 1)(16)
+    ptrs = (ctypes.c_void_p * 1)(None)
+    assert lib.gc_plan_2bit_multi_create(ptrs, ptrs, ns, 1, ctypes.byref(handle)) == gcq.GC_EINVAL
+    assert lib.gc_plan_2bit_multi_create(ptrs, ptrs, ns, 0, ctypes.byref(handle)) == gcq.GC_EINVAL
+    assert handle.value is None

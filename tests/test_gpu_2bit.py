@@ -1,0 +1,211 @@
+"""GPU parity of the 2-bit error-feedback path against the oracle.
+
+The HIP library is called through its C ABI (the ctypes binding) on device
+buffers; the oracle runs on the same input bytes on the CPU. Packed words and
+residuals must match bit for bit; dequantized sums within 1e-6 relative error
+(they are in fact bit-exact: same fp32 operations in the same order).
+
+Workloads: the page's worked example (thresholds +-2, 8 values); the small
+error-feedback case (4096 values ~ N(0, 0.5^2), thresholds +-0.5, 10
+iterations with fresh gradients, seeds 0..9); ragged sizes around every tile
+boundary, 16-byte-aligned and 4-byte-misaligned; the ResNet-50-sized flat
+gradient (25,557,032 values ~ N(0, 0.01^2), thresholds +-0.01, 5 iterations,
+then the W = 8 dequantize-and-sum) in the launch configuration the benchmark
+times; and the BERT-Base parameter list through the many-tensor launcher
+(198 tensors, 109,482,240 values ~ N(0, 0.005^2), thresholds +-0.005, 3
+iterations).
+"""
+import json
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from conftest import announce
+
+pytestmark = pytest.mark.gpu
+
+gu = pytest.importorskip("gpu_util")
+
+SIZES = [0, 1, 2, 3, 4, 5, 15, 16, 17, 31, 63, 64, 65, 255, 256, 257, 1023, 1024, 1025,
+         4095, 4096, 4097, 4111, 8191, 65536 + 7, (1 << 20) + 3]
+
+
+def gpu_compress(gcq, g_np, r_np, neg, pos, misalign=False, poison=True):
+    n = g_np.size
+    g = gu.dev(g_np, misalign)
+    r = gu.dev(r_np, misalign)
+    words = gcq.gc_compressed_2bit_words(n)
+    compr = gu.empty(words, torch.int32, misalign=misalign, fill=-1 if poison else None)
+    gcq.compress_2bit(g, r, neg, pos, compr)
+    gu.sync()
+    return gu.host(compr, np.uint32), gu.host(r)
+
+
+def test_worked_example(gcq, golden_dir):
+    announce("2-bit worked example")
+    ex = json.loads((golden_dir / "worked_example_2bit.json").read_text())
+    g = np.array(ex["constructed_grad"], np.float32)
+    r = np.zeros(8, np.float32)
+    compr, r_gpu = gpu_compress(gcq, g, r, ex["neg_threshold"], ex["pos_threshold"])
+    r_or = np.zeros(8, np.float32)
+    compr_or = oracle.quantize_2bit(g, r_or, ex["neg_threshold"], ex["pos_threshold"])
+    assert compr.tolist() == compr_or.tolist()
+    assert int(compr[3]) == int(ex["printed_last_element_bits"].replace(" ", ""), 2)
+    np.testing.assert_array_equal(r_gpu.view(np.uint32), r_or.view(np.uint32))
+
+
+def test_small_error_feedback_10_iterations(gcq):
+    announce("2-bit n=4096 sigma=0.5 thr=0.5 x10 iterations")
+    n = 4096
+    g_dev = gu.empty(n, torch.float32)
+    r_dev = torch.zeros(n, dtype=torch.float32, device=gu.DEV)
+    compr = gu.empty(gcq.gc_compressed_2bit_words(n), torch.int32, fill=-1)
+    r_or = np.zeros(n, np.float32)
+    for t in range(10):
+        g = si.normal_f32(si.grad_seed(0, t), n, 0.5)
+        g_dev.copy_(torch.from_numpy(g))
+        gcq.compress_2bit(g_dev, r_dev, -0.5, 0.5, compr)
+        c_or = oracle.quantize_2bit(g, r_or, -0.5, 0.5)
+        gu.sync()
+        np.testing.assert_array_equal(gu.host(compr, np.uint32), c_or, err_msg=f"iter {t}")
+        np.testing.assert_array_equal(gu.host(r_dev).view(np.uint32), r_or.view(np.uint32))
+        out = gu.empty(n, torch.float32, fill=float("nan"))
+        gcq.decompress_2bit(compr, n, out)
+        gu.sync()
+        np.testing.assert_array_equal(gu.host(out), oracle.dequantize_2bit(c_or, n))
+
+
+@pytest.mark.parametrize("misalign", [False, True])
+@pytest.mark.parametrize("n", SIZES)
+def test_ragged_sizes(gcq, n, misalign):
+    announce(f"2-bit compress n={n} misalign={misalign}")
+    g = si.normal_f32(1000 + n, n, 0.5)
+    r0 = si.normal_f32(2000 + n, n, 0.25)
+    compr, r_gpu = gpu_compress(gcq, g, r0.copy(), -0.5, 0.5, misalign)
+    r_or = r0.copy()
+    c_or = oracle.quantize_2bit(g, r_or, -0.5, 0.5)
+    np.testing.assert_array_equal(compr, c_or)
+    np.testing.assert_array_equal(r_gpu.view(np.uint32), r_or.view(np.uint32))
+    # decompress (overwrite and accumulate) into aligned and misaligned outputs
+    c_dev = gu.dev(c_or)
+    base = si.normal_f32(3000 + n, n, 1.0)
+    out = gu.dev(base, misalign)
+    gcq.decompress_2bit(c_dev, n, out, accumulate=True)
+    out2 = gu.empty(n, torch.float32, misalign=misalign, fill=float("nan"))
+    gcq.decompress_2bit(c_dev, n, out2)
+    gu.sync()
+    d_or = oracle.dequantize_2bit(c_or, n)
+    np.testing.assert_array_equal(gu.host(out2), d_or)
+    np.testing.assert_array_equal(gu.host(out), (base + d_or).astype(np.float32))
+
+
+@pytest.mark.parametrize("thr", [0.5, 0.01, 2.0, 1e-30])
+def test_threshold_edges(gcq, thr):
+    announce(f"2-bit threshold edges thr={thr}")
+    pos = np.float32(thr)
+    up = np.nextafter(pos, np.float32(np.inf))
+    dn = np.nextafter(pos, np.float32(0))
+    v = np.array([pos, up, dn, -pos, -up, -dn, 0.0, -0.0] * 9, np.float32)
+    compr, r_gpu = gpu_compress(gcq, v, np.zeros_like(v), -pos, pos)
+    r_or = np.zeros_like(v)
+    np.testing.assert_array_equal(compr, oracle.quantize_2bit(v, r_or, -pos, pos))
+    np.testing.assert_array_equal(r_gpu.view(np.uint32), r_or.view(np.uint32))
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 8, 64])
+@pytest.mark.parametrize("n", [1, 17, 1000, 4097, 100_003])
+def test_dequantize_sum(gcq, W, n):
+    announce(f"2-bit dequantize-sum W={W} n={n}")
+    comprs = []
+    for w in range(W):
+        thr = 0.05 + 0.01 * (w % 7)
+        g = si.normal_f32(si.grad_seed(w, 7), n, 0.05)
+        comprs.append(oracle.quantize_2bit(g, np.zeros(n, np.float32), -thr, thr))
+    expect = oracle.dequantize_2bit_sum(comprs, n)
+    for misalign in (False, True):
+        out = gu.empty(n, torch.float32, misalign=misalign, fill=float("nan"))
+        gcq.decompress_2bit_sum([gu.dev(c) for c in comprs], n, out)
+        gu.sync()
+        got = gu.host(out)
+        assert np.all(np.abs(got - expect) <= 1e-6 * np.abs(expect))
+        np.testing.assert_array_equal(got, expect)  # same order -> bit-exact
+
+
+@pytest.mark.slow
+def test_resnet50_flat_gradient_full_size(gcq):
+    """25,557,032 values, W = 8 workers x 5 error-feedback iterations, then
+    the dequantize-and-sum -- the benchmark's workload and launch shapes."""
+    n, W, T, thr = si.RESNET50_PARAMS, 8, 5, 0.01
+    words = gcq.gc_compressed_2bit_words(n)
+    g_dev = gu.empty(n, torch.float32)
+    r_dev = [torch.zeros(n, dtype=torch.float32, device=gu.DEV) for _ in range(W)]
+    c_dev = [gu.empty(words, torch.int32) for _ in range(W)]
+    r_or = [np.zeros(n, np.float32) for _ in range(W)]
+    c_or = [None] * W
+    for t in range(T):
+        for w in range(W):
+            announce(f"2-bit full size n={n} iter={t} worker={w}")
+            g = si.normal_f32(si.grad_seed(w, t), n, 0.01)
+            g_dev.copy_(torch.from_numpy(g))
+            c_dev[w].fill_(-1)
+            gcq.compress_2bit(g_dev, r_dev[w], -thr, thr, c_dev[w])
+            c_or[w] = oracle.quantize_2bit(g, r_or[w], -thr, thr)
+            gu.sync()
+            assert np.array_equal(gu.host(c_dev[w], np.uint32), c_or[w]), (t, w)
+            assert np.array_equal(gu.host(r_dev[w]).view(np.uint32), r_or[w].view(np.uint32)), (t, w)
+    announce("2-bit full size dequantize-sum W=8")
+    out = gu.empty(n, torch.float32, fill=float("nan"))
+    gcq.decompress_2bit_sum(c_dev, n, out)
+    gu.sync()
+    got = gu.host(out)
+    expect = oracle.dequantize_2bit_sum(c_or, n)
+    assert np.all(np.abs(got - expect) <= 1e-6 * np.abs(expect))
+    assert np.array_equal(got, expect)
+
+
+def _multi_case(gcq, sizes, iters, sigma, thr, misalign_every=0, seed0=0):
+    T = len(sizes)
+    grads_dev, res_dev = [], []
+    for t, n in enumerate(sizes):
+        mis = bool(misalign_every) and t % misalign_every == 1
+        grads_dev.append(gu.empty(n, torch.float32, misalign=mis))
+        r = gu.empty(n, torch.float32, misalign=(mis and t % 3 == 1))
+        r.zero_()
+        res_dev.append(r)
+    plan = gcq.Plan2bitMulti(grads_dev, res_dev)
+    offsets = plan.block_offsets()
+    assert plan.compressed_words == sum(oracle.compressed_2bit_words(n) for n in sizes)
+    compr = gu.empty(plan.compressed_words, torch.int32)
+    r_or = [np.zeros(n, np.float32) for n in sizes]
+    for it in range(iters):
+        announce(f"multi-tensor T={T} iter={it}")
+        blocks = []
+        for t, n in enumerate(sizes):
+            g = si.normal_f32(seed0 + 7919 * t + it, n, sigma)
+            grads_dev[t].copy_(torch.from_numpy(g))
+            blocks.append(oracle.quantize_2bit(g, r_or[t], -thr, thr))
+        compr.fill_(-1)
+        plan.compress(-thr, thr, compr)
+        gu.sync()
+        got = gu.host(compr, np.uint32)
+        for t, n in enumerate(sizes):
+            blk = got[offsets[t]:offsets[t] + oracle.compressed_2bit_words(n)]
+            assert np.array_equal(blk, blocks[t]), (it, t, n)
+            assert np.array_equal(gu.host(res_dev[t]).view(np.uint32), r_or[t].view(np.uint32)), (it, t)
+    plan.destroy()
+
+
+def test_multi_tensor_ragged(gcq):
+    sizes = [0, 1, 5, 16, 17, 4095, 4096, 4097, 8192 + 3, 100_000, 0, 3]
+    sizes += si.random_sizes(11, 20, 50_000)
+    _multi_case(gcq, sizes, 2, 0.5, 0.5, misalign_every=4)
+
+
+@pytest.mark.slow
+def test_multi_tensor_bert_base_full_size(gcq):
+    sizes = si.bert_base_sizes()
+    assert len(sizes) == 198 and sum(sizes) == si.BERT_BASE_PARAMS
+    _multi_case(gcq, sizes, 3, 0.005, 0.005)

@@ -1,0 +1,208 @@
+"""GPU parity of the QSGD max-norm path and GlobalRandK against the oracle.
+
+Bit-exact: the global max-norm, the int8 levels, the int32 level sums, the
+rand-K indices and the gathered values. Dequantized fp32 values: within 1e-6
+relative error (in fact bit-exact: the same two fp32 roundings).
+
+Workloads: ragged sizes and worker counts; the VGG16-sized heavy-tailed
+gradient (W = 8 workers x 138,357,544 values ~ N(0, 0.02^2), each entry
+scaled by 50 with probability 0.001, s = 127) in the launch configuration the
+benchmark times, checked on sampled elements plus properties over every
+element; and GlobalRandK at the ResNet-50 size (25,557,032 values ~
+N(0, 0.01^2), K = 10000, W = 8, s = 7), checked in full.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from conftest import announce
+
+pytestmark = pytest.mark.gpu
+
+gu = pytest.importorskip("gpu_util")
+
+
+def run_qsgd(gcq, grads, s, seed, misalign=False, scatter_idx=None, dense_n=0):
+    """Full QSGD-MN step on the device: norm -> levels per worker -> sums ->
+    dequantized output. Returns host copies."""
+    W, n = len(grads), grads[0].size
+    g_dev = [gu.dev(g, misalign) for g in grads]
+    norm = torch.empty(1, dtype=torch.float32, device=gu.DEV)
+    ws = torch.empty(gcq.qsgd_maxnorm_ws_bytes(W, n), dtype=torch.uint8, device=gu.DEV)
+    gcq.qsgd_global_maxnorm(g_dev, norm, ws)
+    levels = [gu.empty(n, torch.int8, misalign=misalign, fill=99) for _ in range(W)]
+    for w in range(W):
+        gcq.qsgd_maxnorm_quantize(g_dev[w], norm, s, seed, w, levels[w])
+    sums = gu.empty(n, torch.int32, misalign=misalign, fill=-7)
+    if scatter_idx is None:
+        out = gu.empty(n, torch.float32, misalign=misalign, fill=float("nan"))
+        gcq.qsgd_dequant_sum(levels, norm, s, out, sums=sums)
+    else:
+        out = gu.empty(dense_n, torch.float32, misalign=misalign, fill=float("nan"))
+        gcq.qsgd_dequant_sum(levels, norm, s, out, sums=sums, scatter_idx=scatter_idx,
+                             dense_n=dense_n)
+    gu.sync()
+    return (np.float32(gu.host(norm)[0]), [gu.host(q) for q in levels], gu.host(sums),
+            gu.host(out))
+
+
+def check_deq(got, expect):
+    assert np.all(np.abs(got.astype(np.float64) - expect) <= 1e-6 * np.abs(expect.astype(np.float64)))
+    np.testing.assert_array_equal(got, expect)
+
+
+@pytest.mark.parametrize("misalign", [False, True])
+@pytest.mark.parametrize("W,n,s", [(1, 1, 127), (2, 5, 7), (3, 4097, 127), (8, 1000, 1),
+                                   (5, 65536 + 3, 15), (64, 777, 127), (8, 1 << 20, 127)])
+def test_qsgd_step_small(gcq, W, n, s, misalign):
+    announce(f"qsgd W={W} n={n} s={s} misalign={misalign}")
+    seed = 0xABCDEF0123 + n
+    grads = [si.heavy_tailed_f32(si.grad_seed(w, 1), n, 0.02) for w in range(W)]
+    norm, levels, sums, out = run_qsgd(gcq, grads, s, seed, misalign)
+    norm_or = oracle.maxnorm(grads)
+    assert norm.view(np.uint32) == norm_or.view(np.uint32)
+    lv_or = [oracle.qsgd_quantize(g, norm_or, s, seed, w) for w, g in enumerate(grads)]
+    for w in range(W):
+        np.testing.assert_array_equal(levels[w], lv_or[w], err_msg=f"worker {w}")
+    s_or = oracle.level_sum(lv_or)
+    np.testing.assert_array_equal(sums, s_or)
+    check_deq(out, oracle.qsgd_dequantize(s_or, norm_or, s))
+
+
+def test_qsgd_zero_gradient(gcq):
+    announce("qsgd all-zero gradients")
+    grads = [np.zeros(1000, np.float32), np.array([-0.0] * 1000, np.float32)]
+    norm, levels, sums, out = run_qsgd(gcq, grads, 127, 5)
+    assert norm == 0.0
+    assert all(np.all(q == 0) for q in levels)
+    assert np.all(sums == 0) and np.all(out == 0)
+
+
+def test_qsgd_norm_element_is_s(gcq):
+    announce("qsgd |g| = norm -> s")
+    g = si.normal_f32(4, 4099, 1.0)
+    j = int(np.argmax(np.abs(g)))
+    for seed in range(5):
+        norm, levels, _, _ = run_qsgd(gcq, [g], 127, seed)
+        assert abs(int(levels[0][j])) == 127
+
+
+@pytest.mark.slow
+def test_qsgd_vgg16_full_size_sampled(gcq):
+    """8 workers x 138,357,544 heavy-tailed values, s = 127, seed 0."""
+    n, W, s, seed = si.VGG16_PARAMS, 8, 127, 0
+    grads = []
+    for w in range(W):
+        announce(f"qsgd full size: generating worker {w}")
+        grads.append(si.heavy_tailed_f32(si.grad_seed(w, 0), n, 0.02))
+    announce("qsgd full size: device step")
+    norm, levels, sums, out = run_qsgd(gcq, grads, s, seed)
+    announce("qsgd full size: oracle on samples")
+    norm_or = oracle.maxnorm(grads)
+    assert norm.view(np.uint32) == norm_or.view(np.uint32)
+    rng = np.random.default_rng(123)
+    samp = np.unique(np.concatenate([rng.integers(0, n, 400_000),
+                                     np.arange(0, 64), np.arange(n - 64, n)])).astype(np.uint64)
+    si_ = samp.astype(np.int64)
+    lv_or = []
+    for w in range(W):
+        q = oracle.qsgd_quantize_at(grads[w][si_], samp, norm_or, s, seed, w)
+        np.testing.assert_array_equal(levels[w][si_], q, err_msg=f"worker {w}")
+        lv_or.append(q)
+    s_or = oracle.level_sum(lv_or)
+    np.testing.assert_array_equal(sums[si_], s_or)
+    check_deq(out[si_], oracle.qsgd_dequantize(s_or, norm_or, s))
+    # every element: level range, sign, bracket of the scaled value
+    announce("qsgd full size: properties over every element")
+    total = np.zeros(n, np.int32)
+    for w in range(W):
+        q = levels[w].astype(np.int32)
+        assert np.all(np.abs(q) <= s)
+        g = grads[w]
+        assert np.all((q == 0) | (np.sign(q) == np.sign(g)))
+        x = (np.abs(g) / norm_or).astype(np.float32) * np.float32(s)
+        fl = np.floor(x).astype(np.int32)
+        m = np.abs(q)
+        assert np.all((m == fl) | (m == fl + 1))
+        total += q
+    np.testing.assert_array_equal(sums, total)
+    check_deq(out, oracle.qsgd_dequantize(total, norm_or, s))
+
+
+@pytest.mark.parametrize("n,K", [(1, 1), (1, 0), (7, 7), (1000, 1000), (100_000, 10_000),
+                                 (1 << 20, 1), (3, 2)])
+def test_grandk_indices(gcq, n, K):
+    for seed in (0, 1, 0xDEADBEEFCAFE):
+        announce(f"grandk_indices n={n} K={K} seed={seed}")
+        idx = gu.empty(max(K, 1), torch.int32, fill=-1)
+        ws = torch.empty(gcq.grandk_ws_bytes(n, K), dtype=torch.uint8, device=gu.DEV)
+        gcq.grandk_indices(n, K, seed, idx[:K], ws)
+        gu.sync()
+        np.testing.assert_array_equal(gu.host(idx, np.uint32)[:K], oracle.randk_indices(n, K, seed))
+
+
+def test_grandk_indices_collisions(gcq):
+    """Small n with K close to n forces chains of earlier swaps."""
+    for n, K in [(50, 49), (64, 64), (300, 250), (5000, 4000)]:
+        for seed in range(20):
+            announce(f"grandk_indices n={n} K={K} seed={seed}")
+            idx = gu.empty(K, torch.int32)
+            ws = torch.empty(gcq.grandk_ws_bytes(n, K), dtype=torch.uint8, device=gu.DEV)
+            gcq.grandk_indices(n, K, seed, idx, ws)
+            gu.sync()
+            np.testing.assert_array_equal(gu.host(idx, np.uint32), oracle.randk_indices(n, K, seed))
+
+
+def test_gather(gcq):
+    announce("gather_f32")
+    x = si.normal_f32(3, 100_001, 1.0)
+    idx = oracle.randk_indices(x.size, 5000, 8)
+    for misalign in (False, True):
+        out = gu.empty(5000, torch.float32, misalign=misalign)
+        gcq.gather_f32(gu.dev(x, misalign), gu.dev(idx), out)
+        gu.sync()
+        np.testing.assert_array_equal(gu.host(out), oracle.gather(x, idx))
+
+
+@pytest.mark.parametrize("full", [False, pytest.param(True, marks=pytest.mark.slow)])
+def test_grandk_step(gcq, full):
+    """GRandK-MN: shared K indices -> gather per worker -> QSGD-MN at s = 7 ->
+    level sum -> scatter-dequantize into a dense buffer."""
+    n = si.RESNET50_PARAMS if full else 200_003
+    K, W, s, seed = 10_000, 8, 7, 0
+    announce(f"grandk step n={n} K={K} W={W}")
+    grads = [si.normal_f32(si.grad_seed(w, 0), n, 0.01) for w in range(W)]
+    g_dev = [gu.dev(g) for g in grads]
+    idx = gu.empty(K, torch.int32)
+    ws = torch.empty(gcq.grandk_ws_bytes(n, K), dtype=torch.uint8, device=gu.DEV)
+    gcq.grandk_indices(n, K, seed, idx, ws)
+    gathered = [gu.empty(K, torch.float32) for _ in range(W)]
+    for w in range(W):
+        gcq.gather_f32(g_dev[w], idx, gathered[w])
+    norm = torch.empty(1, dtype=torch.float32, device=gu.DEV)
+    mws = torch.empty(gcq.qsgd_maxnorm_ws_bytes(W, K), dtype=torch.uint8, device=gu.DEV)
+    gcq.qsgd_global_maxnorm(gathered, norm, mws)
+    levels = [gu.empty(K, torch.int8) for _ in range(W)]
+    for w in range(W):
+        gcq.qsgd_maxnorm_quantize(gathered[w], norm, s, seed, w, levels[w])
+    sums = gu.empty(K, torch.int32)
+    dense = gu.empty(n, torch.float32, fill=float("nan"))
+    gcq.qsgd_dequant_sum(levels, norm, s, dense, sums=sums, scatter_idx=idx, dense_n=n)
+    gu.sync()
+
+    idx_or = oracle.randk_indices(n, K, seed)
+    np.testing.assert_array_equal(gu.host(idx, np.uint32), idx_or)
+    gk_or = [oracle.gather(g, idx_or) for g in grads]
+    for w in range(W):
+        np.testing.assert_array_equal(gu.host(gathered[w]), gk_or[w])
+    norm_or = oracle.maxnorm(gk_or)
+    assert np.float32(gu.host(norm)[0]).view(np.uint32) == norm_or.view(np.uint32)
+    lv_or = [oracle.qsgd_quantize(gk_or[w], norm_or, s, seed, w) for w in range(W)]
+    for w in range(W):
+        np.testing.assert_array_equal(gu.host(levels[w]), lv_or[w])
+    s_or = oracle.level_sum(lv_or)
+    np.testing.assert_array_equal(gu.host(sums), s_or)
+    dense_or = oracle.scatter_dense(oracle.qsgd_dequantize(s_or, norm_or, s), idx_or, n)
+    check_deq(gu.host(dense), dense_or)
