@@ -1,0 +1,342 @@
+#!/usr/bin/env python3
+"""Benchmark of the gradient-quantization hot path on one MI355X.
+
+Step (the workload of the headline metric): one data-parallel step of 2-bit
+error-feedback compression on a ResNet-50-sized flat fp32 gradient,
+25,557,032 values per worker, W = 8 simulated workers, thresholds +-0.01:
+compress_2bit for each worker (residual carried across steps), then
+decompress_2bit_sum of the 8 blocks into one fp32 array in worker order.
+`value` is the step's algorithmic bytes over its wall time on the device.
+
+The metric's second half, QSGD-MN elements/s, is measured in the same run on
+its own workload (VGG16-sized heavy-tailed gradient, 138,357,544 values x 8
+workers, s = 127): global max-norm, 8 quantizes, level sum + dequantize.
+
+Inputs are synthetic (seeded N(0, sigma^2) fp32, see synthetic_inputs.py) and
+resident in HBM before timing starts. Per-kernel durations come from HIP
+events recorded on the stream the kernels are launched on.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import pathlib
+import platform
+import re
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+N_C2 = 25_557_032              # ResNet-50 parameter count
+W_C2 = 8
+THR_C2 = 0.01
+SIGMA_C2 = 0.01
+N_C3 = 138_357_544             # VGG16 parameter count
+W_C3 = 8
+S_C3 = 127
+SIGMA_C3 = 0.02
+
+PROFILE_TRAFFIC = ROOT / "profiles" / "compress_2bit_resnet50_traffic.md"
+KERNEL_SOURCE = ROOT / "gradient_compression_quantize_amd" / "csrc" / "twobit.hip"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def compress_bytes(n: int) -> int:
+    """Algorithmic HBM bytes of one compress_2bit call: read grad and residual,
+    write residual (12 B per value) and the block of 3 + ceil(n/16) words."""
+    return 12 * n + 4 * (3 + (n + 15) // 16)
+
+
+def dequant_sum_bytes(n: int, W: int) -> int:
+    """Read W packed blocks, write n fp32 values."""
+    return 4 * W * (3 + (n + 15) // 16) + 4 * n
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--qsgd-steps", type=int, default=10)
+    ap.add_argument("--skip-qsgd", action="store_true", help="time only the 2-bit step")
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time budget of the oracle baseline sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 1 GiB (counter calibration)")
+    return ap.parse_args()
+
+
+def traffic_from_profile() -> int | None:
+    """HBM bytes per compress_2bit launch measured with rocprofv3 counters,
+    if the committed measurement was taken on the current kernel source."""
+    if not PROFILE_TRAFFIC.exists():
+        return None
+    text = PROFILE_TRAFFIC.read_text()
+    m_b = re.search(r"^traffic_bytes_per_launch:\s*([0-9]+)", text, re.M)
+    m_h = re.search(r"^kernel_source_sha256:\s*([0-9a-f]+)", text, re.M)
+    if not (m_b and m_h):
+        return None
+    cur = hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()
+    return int(m_b.group(1)) if m_h.group(1) == cur else None
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def calibrate_copy() -> None:
+    import torch
+    n = 1 << 28  # 1 GiB of fp32
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": 4 * n,
+                      "bytes_written": 4 * n, "launches": 3}), flush=True)
+
+
+def bench_2bit(gcq, torch, np, si, steps: int, warmup: int):
+    n, W = N_C2, W_C2
+    dev = "cuda"
+    log(f"2-bit: generating {W} x {n} fp32 gradients")
+    grads = [torch.from_numpy(si.normal_f32(si.grad_seed(w, 0), n, SIGMA_C2)).to(dev)
+             for w in range(W)]
+    res = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(W)]
+    words = gcq.gc_compressed_2bit_words(n)
+    comprs = [torch.empty(words, dtype=torch.int32, device=dev) for _ in range(W)]
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for w in range(W):
+            if ev is not None:
+                ev[0][w].record(stream)
+            gcq.compress_2bit(grads[w], res[w], -THR_C2, THR_C2, comprs[w], stream)
+            if ev is not None:
+                ev[1][w].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
+        gcq.decompress_2bit_sum(comprs, n, out, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    log(f"2-bit: warmup {warmup} steps")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    # timed pass: K plain steps between two events
+    t0, t1 = mk(), mk()
+    log(f"2-bit: timing {steps} steps")
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / steps
+    # kernel pass: K more steps with an event pair around every launch
+    evs = [([mk() for _ in range(W)], [mk() for _ in range(W)], mk(), mk()) for _ in range(steps)]
+    log(f"2-bit: per-launch events over {steps} more steps")
+    for k in range(steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    comp_ms = [evs[k][0][w].elapsed_time(evs[k][1][w]) for k in range(steps) for w in range(W)]
+    deq_ms = [evs[k][2].elapsed_time(evs[k][3]) for k in range(steps)]
+    del grads, res, comprs, out
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms_step, "wall_s": wall, "compress_ms": comp_ms, "dequant_sum_ms": deq_ms}
+
+
+def bench_qsgd(gcq, torch, np, si, steps: int):
+    n, W, s = N_C3, W_C3, S_C3
+    dev = "cuda"
+    grads = []
+    for w in range(W):
+        log(f"qsgd: generating worker {w} ({n} heavy-tailed fp32)")
+        grads.append(torch.from_numpy(si.heavy_tailed_f32(si.grad_seed(w, 0), n, SIGMA_C3)).to(dev))
+    norm = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(gcq.qsgd_maxnorm_ws_bytes(W, n), dtype=torch.uint8, device=dev)
+    levels = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(W)]
+    sums = torch.empty(n, dtype=torch.int32, device=dev)
+    out = torch.empty(n, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(seed, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        gcq.qsgd_global_maxnorm(grads, norm, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        for w in range(W):
+            gcq.qsgd_maxnorm_quantize(grads[w], norm, s, seed, w, levels[w], stream)
+        if ev is not None:
+            ev[2].record(stream)
+        gcq.qsgd_dequant_sum(levels, norm, s, out, sums=sums, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(2):
+        step(0)
+    torch.cuda.synchronize()
+    evs = [[mk() for _ in range(4)] for _ in range(steps)]
+    log(f"qsgd: timing {steps} steps")
+    for k in range(steps):
+        step(0, evs[k])
+    torch.cuda.synchronize()
+    tot = [e[0].elapsed_time(e[3]) for e in evs]
+    mx = [e[0].elapsed_time(e[1]) for e in evs]
+    qz = [e[1].elapsed_time(e[2]) for e in evs]
+    ds = [e[2].elapsed_time(e[3]) for e in evs]
+    del grads, levels, sums, out
+    torch.cuda.empty_cache()
+    mean = lambda v: sum(v) / len(v)  # noqa: E731
+    t = mean(tot) / 1e3
+    return {
+        "elems_per_s": W * n / t,
+        "ms_per_step": mean(tot),
+        "workload": f"QSGD-MN s={s}, {W} workers x {n} heavy-tailed fp32 (VGG16-sized): "
+                    "global max-norm, quantize, int32 level sum, dequantize",
+        "stages_ms": {"maxnorm": mean(mx), "quantize_x8": mean(qz), "dequant_sum": mean(ds)},
+        "stages_gbs": {"maxnorm": 4 * W * n / (mean(mx) / 1e3) / 1e9,
+                       "quantize_x8": 5 * W * n / (mean(qz) / 1e3) / 1e9,
+                       "dequant_sum": (W + 8) * n / (mean(ds) / 1e3) / 1e9},
+        "algorithmic_bytes": (4 * W + 5 * W + W + 8) * n,
+        "steps": steps,
+    }
+
+
+def cpu_baseline(np, si, budget_s: float):
+    """The oracle, untouched, on the same 2-bit step (8 workers' compress +
+    the W = 8 dequantize-sum), repeated until the time budget is spent."""
+    import oracle
+    n, W = N_C2, W_C2
+    log("cpu baseline: generating inputs")
+    grads = [si.normal_f32(si.grad_seed(w, 0), n, SIGMA_C2) for w in range(W)]
+    res = [np.zeros(n, np.float32) for _ in range(W)]
+    oracle.lib()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        blocks = [oracle.quantize_2bit(grads[w], res[w], -THR_C2, THR_C2) for w in range(W)]
+        oracle.dequantize_2bit_sum(blocks, n)
+        reps += 1
+        el = time.perf_counter() - t0
+        log(f"cpu baseline: step {reps} done ({el:.1f} s)")
+        if el >= budget_s:
+            break
+    step_s = el / reps
+    gbs = (W * compress_bytes(n) + dequant_sum_bytes(n, W)) / step_s / 1e9
+    return {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full 2-bit steps (8 x {n} values compressed + W=8 dequantize-sum) "
+                      f"in {el:.1f} s, single-threaded C oracle on one host core "
+                      f"({cpu_model()}, {os.cpu_count()} visible)",
+            "ms_per_step": step_s * 1e3}
+
+
+def main() -> int:
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this library runs on one GPU; multi-GPU runs are not part of it "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return 0
+
+    import gradient_compression_quantize_amd as gcq
+    import synthetic_inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    gcq.load()
+
+    r2 = bench_2bit(gcq, torch, np, si, args.steps, args.warmup)
+    step_bytes = W_C2 * compress_bytes(N_C2) + dequant_sum_bytes(N_C2, W_C2)
+    ms = r2["ms_per_step"]
+    value = step_bytes / (ms / 1e3) / 1e9
+    comp_ms = sum(r2["compress_ms"]) / len(r2["compress_ms"])
+    deq_ms = sum(r2["dequant_sum_ms"]) / len(r2["dequant_sum_ms"])
+    comp_gbs = compress_bytes(N_C2) / (comp_ms / 1e3) / 1e9
+    traffic = traffic_from_profile()
+
+    result = {
+        "metric": "2-bit EF quantize+pack GB/s and % HBM peak, 25.6M fp32; QSGD-MN elems/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "config": {
+            "workload": "2-bit EF step: compress_2bit x 8 workers (25,557,032 fp32 each, "
+                        "ResNet-50-sized flat gradient, thresholds +-0.01, residual carried) "
+                        "+ decompress_2bit_sum W=8",
+            "n": N_C2, "workers": W_C2, "neg_threshold": -THR_C2, "pos_threshold": THR_C2,
+            "sigma": SIGMA_C2, "step_algorithmic_bytes": step_bytes,
+        },
+        "kernels": {
+            "compress_2bit": {"avg_ms": round(comp_ms, 5), "gbs": round(comp_gbs, 1),
+                              "algorithmic_bytes": compress_bytes(N_C2),
+                              "launches": len(r2["compress_ms"])},
+            "decompress_2bit_sum": {"avg_ms": round(deq_ms, 5),
+                                    "gbs": round(dequant_sum_bytes(N_C2, W_C2) / (deq_ms / 1e3) / 1e9, 1),
+                                    "algorithmic_bytes": dequant_sum_bytes(N_C2, W_C2),
+                                    "launches": len(r2["dequant_sum_ms"])},
+        },
+        "roofline": {"bound": "hbm", "kernel": "compress_2bit",
+                     "achieved": round(comp_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(comp_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+    }
+
+    if not args.skip_qsgd:
+        q = bench_qsgd(gcq, torch, np, si, args.qsgd_steps)
+        result["qsgd_mn_elems_per_s"] = q["elems_per_s"]
+        result["qsgd_mn"] = q
+
+    if not args.skip_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(np, si, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -30,9 +30,11 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 inline size_t ceil_div(size_t a, size_t b) { return (a + b - 1) / b; }
 
-// Grid x-dimension cap for grid-stride kernels. Launch sizes stay far below
-// the 2^32 work-item limit; larger problems loop inside the kernel.
-constexpr size_t kMaxGridX = size_t(1) << 20;
+// Cap on the workgroups of one launch: larger problems make the kernels
+// stride. 2^20 workgroups keep launches far below the 2^32 work-item limit.
+// The environment variable GCQ_MAX_GRID_BLOCKS, read once per process, can
+// lower it (tests use it to reach the striding paths at small sizes).
+size_t max_grid_blocks();
 
 // W device pointers passed by value in the kernel argument segment.
 template <typename T>

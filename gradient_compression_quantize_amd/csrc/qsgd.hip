@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const float* __restric
 
 size_t grid_for(size_t items)
 {
-    return std::max<size_t>(1, std::min(ceil_div(items, kThreads), kMaxGridX));
+    return std::max<size_t>(1, std::min(ceil_div(items, kThreads), max_grid_blocks()));
 }
 
 }  // namespace

@@ -1,6 +1,8 @@
 // status.hip -- per-thread error state of libgcq.so.
 #include "gcq_internal.h"
 
+#include <cstdlib>
+
 namespace gcq {
 
 namespace {
@@ -26,6 +28,20 @@ int check_launch(const char* what)
 }
 
 const char* last_error() { return g_last_error.c_str(); }
+
+size_t max_grid_blocks()
+{
+    static const size_t cap = [] {
+        size_t c = size_t(1) << 20;
+        if (const char* env = std::getenv("GCQ_MAX_GRID_BLOCKS")) {
+            const long long v = std::atoll(env);
+            if (v >= 1 && size_t(v) < c)
+                c = size_t(v);
+        }
+        return c;
+    }();
+    return cap;
+}
 
 }  // namespace gcq
 

@@ -13,9 +13,10 @@
 //  - one wave owns a tile of kUnroll float4 slots per lane, lane-contiguous,
 //    so each load/store instruction moves 1 KiB of grad / residual;
 //  - the 4 codes of a lane's float4 form one byte; a DPP quad-OR joins the
-//    4 bytes of lanes 4k..4k+3 into the 32-bit word of 16 codes, and lane
-//    4k stores it: every payload word is written exactly once, with no
-//    atomics and no pre-zeroing of the output;
+//    4 bytes of lanes 4k..4k+3 into the 32-bit word of 16 codes, and one
+//    ds_bpermute lines the tile's 64 words up so that lane L stores word L:
+//    every payload word is written exactly once, in one coalesced store per
+//    tile, with no atomics and no pre-zeroing of the output;
 //  - a float4 slot that straddles n is handled by scalar loads in the same
 //    lane; values past n take code 00 and are never read or written.
 #include "gcq_internal.h"
@@ -33,6 +34,9 @@ constexpr int kUnroll = 4;                             // float4 per lane per ti
 constexpr size_t kTileF4 = size_t(kWave) * kUnroll;    // 256 float4 slots
 constexpr size_t kTileElems = kTileF4 * 4;             // 1024 values
 constexpr size_t kBlockElems = kTileElems * kWavesPerBlock;  // 4096 values
+// A tile is 64 words of codes, one per lane: the cross-lane moves that
+// gather and scatter words rely on it.
+static_assert(kUnroll == 4 && kTileF4 == 256, "one tile = 64 words of codes");
 
 __device__ __forceinline__ float code_value(uint32_t c, float neg, float pos)
 {
@@ -57,104 +61,16 @@ __device__ __forceinline__ void classify4(f32x4 g, f32x4 r, float neg, float pos
     }
 }
 
-// One wave tile: float4 slots q0 .. q0 + kTileF4 - 1 of a tensor of n values.
-// `payload` is the block's element 3 (first word of codes). kFull: every slot
-// of the tile lies below n / 4, so no lane needs a bounds check.
-template <bool kFull>
-__device__ __forceinline__ void compress_wave_tile(const float* __restrict__ grad,
-                                                   float* __restrict__ residual, size_t n,
-                                                   float neg, float pos,
-                                                   uint32_t* __restrict__ payload, size_t q0,
-                                                   int lane)
-{
-    const size_t nfull = n >> 2;           // float4 slots entirely below n
-    const size_t nwords = (n + 15) >> 4;
-    const f32x4* g4 = reinterpret_cast<const f32x4*>(grad);
-    f32x4* r4 = reinterpret_cast<f32x4*>(residual);
-
-    f32x4 g[kUnroll], r[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const size_t q = q0 + size_t(u) * kWave + lane;
-        if (kFull || q < nfull) {
-            g[u] = __builtin_nontemporal_load(g4 + q);
-            r[u] = r4[q];
-        } else {
-            g[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            r[u] = g[u];
-            const size_t e = q * 4;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                if (e + k < n) {
-                    g[u][k] = grad[e + k];
-                    r[u][k] = residual[e + k];
-                }
-            }
-        }
-    }
-
-    const uint32_t shift = 24u - 8u * uint32_t(lane & 3);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        const size_t q = q0 + size_t(u) * kWave + lane;
-        f32x4 rn;
-        uint32_t byte;
-        classify4(g[u], r[u], neg, pos, rn, byte);
-        if (kFull || q < nfull) {
-            __builtin_nontemporal_store(rn, r4 + q);
-        } else {
-            const size_t e = q * 4;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (e + k < n)
-                    residual[e + k] = rn[k];
-        }
-        // all 64 lanes reach this point together
-        const uint32_t word = quad_or(byte << shift);
-        const size_t j = q >> 2;
-        if ((lane & 3) == 0 && (kFull || j < nwords))
-            __builtin_nontemporal_store(word, payload + j);
-    }
-}
-
-__device__ __forceinline__ void compress_tile(const float* __restrict__ grad,
-                                              float* __restrict__ residual, size_t n, float neg,
-                                              float pos, uint32_t* __restrict__ payload,
-                                              size_t q0, int lane)
-{
-    if (q0 + kTileF4 <= (n >> 2))
-        compress_wave_tile<true>(grad, residual, n, neg, pos, payload, q0, lane);
-    else
-        compress_wave_tile<false>(grad, residual, n, neg, pos, payload, q0, lane);
-}
-
-__device__ __forceinline__ void write_header(uint32_t* blk, float neg, float pos, float n_f)
-{
-    blk[0] = f2u(neg);
-    blk[1] = f2u(pos);
-    blk[2] = f2u(n_f);
-}
-
-// 16-byte-aligned grad and residual.
-__global__ __launch_bounds__(kThreads) void compress_2bit_vec_kernel(
-    const float* __restrict__ grad, float* __restrict__ residual, size_t n, float neg,
-    float pos, float n_f, uint32_t* __restrict__ compr, size_t ntiles)
-{
-    if (blockIdx.x == 0 && threadIdx.x == 0)
-        write_header(compr, neg, pos, n_f);
-    const int lane = threadIdx.x & (kWave - 1);
-    const size_t stride = size_t(gridDim.x) * kWavesPerBlock;
-    for (size_t t = size_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; t < ntiles;
-         t += stride)
-        compress_tile(grad, residual, n, neg, pos, compr + 3, t * kTileF4, lane);
-}
-
 // One word of codes (16 values) by one thread, scalar accesses.
 __device__ __forceinline__ uint32_t compress_word_scalar(const float* __restrict__ grad,
                                                          float* __restrict__ residual, size_t n,
                                                          float neg, float pos, size_t j)
 {
     uint32_t word = 0;
+    // kept rolled: this path serves misaligned buffers and the one partial
+    // tile of a tensor, and unrolling it would raise the register count of
+    // the vector kernels that inline it
+#pragma unroll 1
     for (int k = 0; k < 16; ++k) {
         const size_t i = j * 16 + k;
         if (i >= n)
@@ -170,6 +86,90 @@ __device__ __forceinline__ uint32_t compress_word_scalar(const float* __restrict
     return word;
 }
 
+// One full wave tile: float4 slots q0 .. q0 + kTileF4 - 1, all below n / 4.
+// `payload` is the block's element 3 (first word of codes).
+__device__ __forceinline__ void compress_full_tile(const float* __restrict__ grad,
+                                                   float* __restrict__ residual, float neg,
+                                                   float pos, uint32_t* __restrict__ payload,
+                                                   size_t q0, int lane)
+{
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(grad);
+    f32x4* r4 = reinterpret_cast<f32x4*>(residual);
+    f32x4 g[kUnroll], r[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const size_t q = q0 + size_t(u) * kWave + lane;
+        // both streams are touched once: non-temporal loads keep them from
+        // displacing each other in the caches
+        g[u] = __builtin_nontemporal_load(g4 + q);
+        r[u] = __builtin_nontemporal_load(r4 + q);
+    }
+    const uint32_t shift = 24u - 8u * uint32_t(lane & 3);
+    uint32_t kept = 0;  // lane 4k + m keeps its quad's word of slot m
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const size_t q = q0 + size_t(u) * kWave + lane;
+        f32x4 rn;
+        uint32_t byte;
+        classify4(g[u], r[u], neg, pos, rn, byte);
+        __builtin_nontemporal_store(rn, r4 + q);
+        const uint32_t word = quad_or(byte << shift);
+        if ((lane & 3) == u)
+            kept = word;
+    }
+    // The tile's 64 words leave in one coalesced 256-byte store: word L
+    // covers slots 4L..4L+3, i.e. quad L % 16 of slot u = L / 16, which lane
+    // 4 (L % 16) + L / 16 kept.
+    const uint32_t mine = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(
+        (4 * (lane & 15) + (lane >> 4)) * 4, static_cast<int>(kept)));
+    __builtin_nontemporal_store(mine, payload + (q0 >> 2) + lane);
+}
+
+// Tile q0 of a tensor of n values: the vector path when the whole tile lies
+// below n / 4, else (only the last tile) lane L encodes word q0/4 + L with
+// scalar accesses, touching no value at or past n.
+__device__ __forceinline__ void compress_tile(const float* __restrict__ grad,
+                                              float* __restrict__ residual, size_t n, float neg,
+                                              float pos, uint32_t* __restrict__ payload,
+                                              size_t q0, int lane)
+{
+    if (q0 + kTileF4 <= (n >> 2)) {
+        compress_full_tile(grad, residual, neg, pos, payload, q0, lane);
+    } else {
+        const size_t j = (q0 >> 2) + lane;
+        if (j < ((n + 15) >> 4))
+            payload[j] = compress_word_scalar(grad, residual, n, neg, pos, j);
+    }
+}
+
+__device__ __forceinline__ void write_header(uint32_t* blk, float neg, float pos, float n_f)
+{
+    blk[0] = f2u(neg);
+    blk[1] = f2u(pos);
+    blk[2] = f2u(n_f);
+}
+
+// 16-byte-aligned grad and residual. kLoop = false: the grid has one wave
+// per tile (the usual case); true: a capped grid strides over the tiles.
+template <bool kLoop>
+__global__ __launch_bounds__(kThreads) void compress_2bit_vec_kernel(
+    const float* __restrict__ grad, float* __restrict__ residual, size_t n, float neg,
+    float pos, float n_f, uint32_t* __restrict__ compr, size_t ntiles)
+{
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        write_header(compr, neg, pos, n_f);
+    const int lane = threadIdx.x & (kWave - 1);
+    const size_t stride = size_t(gridDim.x) * kWavesPerBlock;
+    // Tiles are taken last-first: the one partial tile (slow scalar path)
+    // goes to the first wave dispatched and overlaps the streaming ones.
+    for (size_t t = size_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; t < ntiles;
+         t += stride) {
+        compress_tile(grad, residual, n, neg, pos, compr + 3, (ntiles - 1 - t) * kTileF4, lane);
+        if (!kLoop)
+            break;
+    }
+}
+
 // Any 4-byte alignment: one thread per word.
 __global__ __launch_bounds__(kThreads) void compress_2bit_scalar_kernel(
     const float* __restrict__ grad, float* __restrict__ residual, size_t n, float neg,
@@ -183,69 +183,130 @@ __global__ __launch_bounds__(kThreads) void compress_2bit_scalar_kernel(
         compr[3 + j] = compress_word_scalar(grad, residual, n, neg, pos, j);
 }
 
-// One wave tile of the W-block dequantize-and-sum (see compress_wave_tile).
-template <bool kFull>
-__device__ __forceinline__ void decompress_wave_tile(const PtrTable<uint32_t>& tab, int W,
-                                                     size_t n, float* __restrict__ out,
-                                                     int accumulate, size_t q0, int lane)
+// Dequantization table in LDS: for worker w and a 4-bit nibble v (two codes,
+// the earlier value in the high pair), entry 16w + v holds the two values.
+// One worker's 16 entries span 128 bytes -- every LDS bank once -- so a
+// wave's lookups into it never conflict.
+__device__ __forceinline__ void build_nibble_table(float2* lut, const PtrTable<uint32_t>& tab,
+                                                   int W)
 {
-    const size_t nfull = n >> 2;
-    const size_t nwords = (n + 15) >> 4;
+    for (int w = 0; w < W; ++w) {
+        if (threadIdx.x < 16) {
+            const uint32_t* b = tab.p[w];
+            const float neg = u2f(b[0]);
+            const float pos = u2f(b[1]);
+            const uint32_t v = threadIdx.x;
+            lut[16 * w + v] = make_float2(code_value(v >> 2, neg, pos), code_value(v & 3u, neg, pos));
+        }
+    }
+    __syncthreads();
+}
+
+// One wave tile of the W-block dequantize-and-sum (see compress_wave_tile).
+// The tile's 1024 values are 64 words of each block: lane L loads word L
+// (one coalesced 256-byte load per worker), and a ds_bpermute hands each
+// lane the word of its float4 slot (word 16u + L/4 for slot u), so no word
+// is fetched from memory twice. Decoding goes through the LDS nibble table.
+// WC > 0: W == WC is known at compile time, so every worker's word is loaded
+// before any is decoded; WC == 0: W read at run time, in groups of four.
+template <int WC, bool kAcc>
+__device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& tab, int W_rt,
+                                                     const float2* lut,
+                                                     float* __restrict__ out, size_t q0,
+                                                     int lane)
+{
+    const int W = WC > 0 ? WC : W_rt;
+    const size_t jmine = (q0 >> 2) + lane;  // the word this lane fetches
     const uint32_t shift = 24u - 8u * uint32_t(lane & 3);
     f32x4* o4 = reinterpret_cast<f32x4*>(out);
     f32x4 acc[kUnroll];
-    for (int w = 0; w < W; ++w) {
-        const uint32_t* __restrict__ b = tab.p[w];
-        const float neg = u2f(b[0]);
-        const float pos = u2f(b[1]);
-        uint32_t words[kUnroll];
+    constexpr int kGroup = WC > 0 ? WC : 4;  // workers whose words are in flight together
+    for (int w0 = 0; w0 < W; w0 += kGroup) {
+        uint32_t mine[kGroup];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const size_t j = (q0 + size_t(u) * kWave + lane) >> 2;
-            words[u] = (kFull || j < nwords) ? b[3 + j] : 0u;
+        for (int dw = 0; dw < kGroup; ++dw) {
+            mine[dw] = (WC == 0 && w0 + dw >= W)
+                           ? 0u
+                           : __builtin_nontemporal_load(tab.p[w0 + dw] + 3 + jmine);
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t byte = (words[u] >> shift) & 0xFFu;
+        for (int dw = 0; dw < kGroup; ++dw) {
+            const int w = w0 + dw;
+            if (WC == 0 && w >= W)
+                break;
+            const float2* t = lut + 16 * w;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float d = code_value((byte >> (6 - 2 * k)) & 3u, neg, pos);
-                acc[u][k] = (w == 0) ? d : acc[u][k] + d;
+            for (int u = 0; u < kUnroll; ++u) {
+                // all 64 lanes take part: lane 16u + L/4 holds this slot's word
+                const uint32_t word = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(
+                    (16 * u + (lane >> 2)) * 4, static_cast<int>(mine[dw])));
+                const uint32_t byte = (word >> shift) & 0xFFu;
+                const float2 hi = t[byte >> 4];
+                const float2 lo = t[byte & 15u];
+                const f32x4 d = {hi.x, hi.y, lo.x, lo.y};
+                acc[u] = (w == 0) ? d : acc[u] + d;
             }
         }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         const size_t q = q0 + size_t(u) * kWave + lane;
-        if (kFull || q < nfull) {
-            f32x4 v = acc[u];
-            if (accumulate)
-                v = o4[q] + v;
-            __builtin_nontemporal_store(v, o4 + q);
-        } else {
-            const size_t e = q * 4;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (e + k < n)
-                    out[e + k] = accumulate ? out[e + k] + acc[u][k] : acc[u][k];
-        }
+        f32x4 v = acc[u];
+        if (kAcc)
+            v = o4[q] + v;
+        __builtin_nontemporal_store(v, o4 + q);
     }
 }
 
-// Dequantize-and-sum of W blocks into a 16-byte-aligned out.
-__global__ __launch_bounds__(kThreads) void decompress_2bit_vec_kernel(
-    PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, int accumulate,
-    size_t ntiles)
+// The last, partial tile: lane L decodes word q0/4 + L through the nibble
+// table, one word load per worker, and writes the values below n.
+__device__ __forceinline__ void decompress_tail_tile(const PtrTable<uint32_t>& tab, int W,
+                                                     const float2* lut, size_t n,
+                                                     float* __restrict__ out, int accumulate,
+                                                     size_t q0, int lane)
 {
+    const size_t j = (q0 >> 2) + lane;
+    if (j >= ((n + 15) >> 4))
+        return;
+    float acc[16];
+#pragma unroll 1
+    for (int w = 0; w < W; ++w) {
+        const uint32_t word = tab.p[w][3 + j];
+#pragma unroll
+        for (int k = 0; k < 16; k += 2) {
+            const float2 v = lut[16 * w + ((word >> (28 - 2 * k)) & 15u)];
+            acc[k] = (w == 0) ? v.x : acc[k] + v.x;
+            acc[k + 1] = (w == 0) ? v.y : acc[k + 1] + v.y;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const size_t i = j * 16 + k;
+        if (i < n)
+            out[i] = accumulate ? out[i] + acc[k] : acc[k];
+    }
+}
+
+// Dequantize-and-sum of W blocks into a 16-byte-aligned out (kAcc: added to
+// what out holds).
+template <int WC, bool kAcc, bool kLoop>
+__global__ __launch_bounds__(kThreads) void decompress_2bit_vec_kernel(
+    PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, size_t ntiles)
+{
+    __shared__ float2 lut[16 * GC_MAX_WORKERS];
+    build_nibble_table(lut, tab, WC > 0 ? WC : W);
     const int lane = threadIdx.x & (kWave - 1);
     const size_t stride = size_t(gridDim.x) * kWavesPerBlock;
+    // last tile first, as in compress_2bit_vec_kernel
     for (size_t t = size_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; t < ntiles;
          t += stride) {
-        const size_t q0 = t * kTileF4;
+        const size_t q0 = (ntiles - 1 - t) * kTileF4;
         if (q0 + kTileF4 <= (n >> 2))
-            decompress_wave_tile<true>(tab, W, n, out, accumulate, q0, lane);
+            decompress_full_tile<WC, kAcc>(tab, W, lut, out, q0, lane);
         else
-            decompress_wave_tile<false>(tab, W, n, out, accumulate, q0, lane);
+            decompress_tail_tile(tab, WC > 0 ? WC : W, lut, n, out, kAcc ? 1 : 0, q0, lane);
+        if (!kLoop)
+            break;
     }
 }
 
@@ -283,6 +344,7 @@ struct ChunkDesc {
     uint32_t chunk;  // index of the kBlockElems-sized chunk inside the tensor
 };
 
+template <bool kLoop>
 __global__ __launch_bounds__(kThreads) void compress_2bit_multi_kernel(
     const TensorDesc* __restrict__ tensors, const ChunkDesc* __restrict__ chunks,
     size_t nchunks, float neg, float pos, uint32_t* __restrict__ compr_base)
@@ -303,6 +365,8 @@ __global__ __launch_bounds__(kThreads) void compress_2bit_multi_kernel(
             if (j < ((td.n + 15) >> 4))
                 blk[3 + j] = compress_word_scalar(td.grad, td.residual, td.n, neg, pos, j);
         }
+        if (!kLoop)
+            break;
     }
 }
 
@@ -317,7 +381,13 @@ int check_thresholds(float neg, float pos)
 
 size_t grid_for_tiles(size_t ntiles)
 {
-    return std::max<size_t>(1, std::min(ceil_div(ntiles, kWavesPerBlock), kMaxGridX));
+    return std::max<size_t>(1, std::min(ceil_div(ntiles, kWavesPerBlock), max_grid_blocks()));
+}
+
+// Whether a grid_for_tiles grid must stride (more tiles than waves).
+bool tiles_need_loop(size_t ntiles)
+{
+    return ceil_div(ntiles, kWavesPerBlock) > max_grid_blocks();
 }
 
 }  // namespace
@@ -352,15 +422,51 @@ GCQ_API int compress_2bit(const float* grad, float* residual, size_t n, float ne
     const float n_f = static_cast<float>(n);
     if (n == 0 || (aligned16(grad) && aligned16(residual))) {
         const size_t ntiles = ceil_div(n, kTileElems);
-        hipLaunchKernelGGL(compress_2bit_vec_kernel, dim3(grid_for_tiles(ntiles)),
-                           dim3(kThreads), 0, stream, grad, residual, n, neg_threshold,
-                           pos_threshold, n_f, compr, ntiles);
+        const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
+        if (tiles_need_loop(ntiles))
+            hipLaunchKernelGGL(compress_2bit_vec_kernel<true>, grid, block, 0, stream, grad,
+                               residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles);
+        else
+            hipLaunchKernelGGL(compress_2bit_vec_kernel<false>, grid, block, 0, stream, grad,
+                               residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles);
     } else {
-        const size_t blocks = std::min(ceil_div(ceil_div(n, 16), kThreads), kMaxGridX);
+        const size_t blocks = std::min(ceil_div(ceil_div(n, 16), kThreads), max_grid_blocks());
         hipLaunchKernelGGL(compress_2bit_scalar_kernel, dim3(blocks), dim3(kThreads), 0,
                            stream, grad, residual, n, neg_threshold, pos_threshold, n_f, compr);
     }
     return check_launch("compress_2bit");
+}
+
+template <bool kLoop>
+static void launch_decompress_vec(const PtrTable<uint32_t>& tab, int W, size_t n, float* out,
+                                  int accumulate, size_t ntiles, dim3 grid, dim3 block,
+                                  hipStream_t stream)
+{
+    if (accumulate) {
+        // only decompress_2bit accumulates (W == 1)
+        hipLaunchKernelGGL((decompress_2bit_vec_kernel<1, true, kLoop>), grid, block, 0, stream,
+                           tab, W, n, out, ntiles);
+        return;
+    }
+    switch (W) {
+#define GCQ_DEC_CASE(k)                                                                    \
+    case k:                                                                                \
+        hipLaunchKernelGGL((decompress_2bit_vec_kernel<k, false, kLoop>), grid, block, 0,  \
+                           stream, tab, W, n, out, ntiles);                                \
+        break;
+        GCQ_DEC_CASE(1)
+        GCQ_DEC_CASE(2)
+        GCQ_DEC_CASE(3)
+        GCQ_DEC_CASE(4)
+        GCQ_DEC_CASE(5)
+        GCQ_DEC_CASE(6)
+        GCQ_DEC_CASE(7)
+        GCQ_DEC_CASE(8)
+#undef GCQ_DEC_CASE
+    default:
+        hipLaunchKernelGGL((decompress_2bit_vec_kernel<0, false, kLoop>), grid, block, 0, stream,
+                           tab, W, n, out, ntiles);
+    }
 }
 
 static int launch_decompress(const PtrTable<uint32_t>& tab, int W, size_t n, float* out,
@@ -370,10 +476,13 @@ static int launch_decompress(const PtrTable<uint32_t>& tab, int W, size_t n, flo
         return GC_OK;
     if (aligned16(out)) {
         const size_t ntiles = ceil_div(n, kTileElems);
-        hipLaunchKernelGGL(decompress_2bit_vec_kernel, dim3(grid_for_tiles(ntiles)),
-                           dim3(kThreads), 0, stream, tab, W, n, out, accumulate, ntiles);
+        const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
+        if (tiles_need_loop(ntiles))
+            launch_decompress_vec<true>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
+        else
+            launch_decompress_vec<false>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
     } else {
-        const size_t blocks = std::min(ceil_div(n, kThreads), kMaxGridX);
+        const size_t blocks = std::min(ceil_div(n, kThreads), max_grid_blocks());
         hipLaunchKernelGGL(decompress_2bit_scalar_kernel, dim3(blocks), dim3(kThreads), 0,
                            stream, tab, W, n, out, accumulate);
     }
@@ -429,7 +538,7 @@ GCQ_API int gc_plan_2bit_multi_create(const float* const* grads, float* const* r
         return fail(GC_EINVAL, "gc_plan_2bit_multi_create: need T >= 1 and host arrays");
 
     std::vector<TensorDesc> tensors(static_cast<size_t>(T));
-    std::vector<ChunkDesc> chunks;
+    std::vector<ChunkDesc> chunks, first;
     std::vector<size_t> offsets(static_cast<size_t>(T));
     size_t off = 0;
     for (int t = 0; t < T; ++t) {
@@ -450,9 +559,15 @@ GCQ_API int gc_plan_2bit_multi_create(const float* const* grads, float* const* r
         d.vec_ok = (aligned16(grads[t]) && aligned16(residuals[t])) ? 1u : 0u;
         offsets[static_cast<size_t>(t)] = off;
         off += gc_compressed_2bit_words(n);
-        for (size_t c = 0; c < nch; ++c)
+        // a chunk holding a partial tile takes the slow scalar path: those go
+        // first in the launch so that they overlap the streaming chunks
+        const bool ragged = (n % kTileElems) != 0 || n == 0;
+        if (ragged)
+            first.push_back(ChunkDesc{static_cast<uint32_t>(t), static_cast<uint32_t>(nch - 1)});
+        for (size_t c = 0; c + (ragged ? 1 : 0) < nch; ++c)
             chunks.push_back(ChunkDesc{static_cast<uint32_t>(t), static_cast<uint32_t>(c)});
     }
+    chunks.insert(chunks.begin(), first.begin(), first.end());
 
     gc_plan* p = new gc_plan();
     p->T = T;
@@ -498,10 +613,15 @@ GCQ_API int compress_2bit_multi(gc_plan* plan, float neg_threshold, float pos_th
         return rc;
     if (!aligned4(compr_base))
         return fail(GC_EINVAL, "compress_2bit_multi: compr_base must be 4-byte aligned");
-    const size_t blocks = std::min(plan->nchunks, kMaxGridX);
-    hipLaunchKernelGGL(compress_2bit_multi_kernel, dim3(blocks), dim3(kThreads), 0, stream,
-                       plan->d_tensors, plan->d_chunks, plan->nchunks, neg_threshold,
-                       pos_threshold, compr_base);
+    const size_t blocks = std::min(plan->nchunks, max_grid_blocks());
+    if (blocks < plan->nchunks)
+        hipLaunchKernelGGL(compress_2bit_multi_kernel<true>, dim3(blocks), dim3(kThreads), 0,
+                           stream, plan->d_tensors, plan->d_chunks, plan->nchunks, neg_threshold,
+                           pos_threshold, compr_base);
+    else
+        hipLaunchKernelGGL(compress_2bit_multi_kernel<false>, dim3(blocks), dim3(kThreads), 0,
+                           stream, plan->d_tensors, plan->d_chunks, plan->nchunks, neg_threshold,
+                           pos_threshold, compr_base);
     return check_launch("compress_2bit_multi");
 }
 

@@ -1,0 +1,114 @@
+"""Parity of the striding kernel paths, run in a child process whose
+GCQ_MAX_GRID_BLOCKS caps every launch at a few workgroups (the library reads
+the variable once, when it is first used). Exits 0 when every result matches
+the oracle; prints the failing case otherwise.
+"""
+import os
+import pathlib
+import sys
+
+ROOT = pathlib.Path(__file__).resolve().parent.parent
+sys.path.insert(0, str(ROOT))
+sys.path.insert(0, str(ROOT / "tests"))
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import gradient_compression_quantize_amd as gcq  # noqa: E402
+import oracle  # noqa: E402
+import synthetic_inputs as si  # noqa: E402
+import gpu_util as gu  # noqa: E402
+
+
+def check(cond, what):
+    if not cond:
+        print(f"FAIL: {what}", flush=True)
+        sys.exit(1)
+
+
+def main():
+    assert os.environ.get("GCQ_MAX_GRID_BLOCKS"), "run with GCQ_MAX_GRID_BLOCKS set"
+    gcq.load()
+    # 2-bit: vector path over many more tiles than waves, ragged tail
+    for n in (40_000 + 5, 123_457):
+        print(f"[case] capped compress/decompress n={n}", flush=True)
+        g = si.normal_f32(n, n, 0.5)
+        r0 = si.normal_f32(n + 1, n, 0.2)
+        r_dev = gu.dev(r0)
+        compr = gu.empty(gcq.gc_compressed_2bit_words(n), torch.int32, fill=-1)
+        gcq.compress_2bit(gu.dev(g), r_dev, -0.5, 0.5, compr)
+        r_or = r0.copy()
+        c_or = oracle.quantize_2bit(g, r_or, -0.5, 0.5)
+        gu.sync()
+        check(np.array_equal(gu.host(compr, np.uint32), c_or), f"compress words n={n}")
+        check(np.array_equal(gu.host(r_dev).view(np.uint32), r_or.view(np.uint32)),
+              f"compress residual n={n}")
+        base = si.normal_f32(n + 2, n, 1.0)
+        out = gu.dev(base)
+        gcq.decompress_2bit(gu.dev(c_or), n, out, accumulate=True)
+        gu.sync()
+        check(np.array_equal(gu.host(out), (base + oracle.dequantize_2bit(c_or, n)).astype(np.float32)),
+              f"decompress accumulate n={n}")
+        for W in (8, 9):
+            comprs = [oracle.quantize_2bit(si.normal_f32(7 * w + n, n, 0.5), np.zeros(n, np.float32),
+                                           -0.3 - 0.01 * w, 0.3 + 0.01 * w) for w in range(W)]
+            out = gu.empty(n, torch.float32, fill=float("nan"))
+            gcq.decompress_2bit_sum([gu.dev(c) for c in comprs], n, out)
+            gu.sync()
+            check(np.array_equal(gu.host(out), oracle.dequantize_2bit_sum(comprs, n)),
+                  f"decompress sum W={W} n={n}")
+    # many tensors, more chunks than workgroups
+    print("[case] capped multi-tensor", flush=True)
+    sizes = [5000, 0, 17, 70_001, 4096 * 3, 33]
+    grads = [gu.empty(n, torch.float32) for n in sizes]
+    res = [torch.zeros(n, dtype=torch.float32, device=gu.DEV) for n in sizes]
+    plan = gcq.Plan2bitMulti(grads, res)
+    blocks = []
+    for t, n in enumerate(sizes):
+        g = si.normal_f32(300 + t, n, 0.5)
+        grads[t].copy_(torch.from_numpy(g))
+        blocks.append(oracle.quantize_2bit(g, np.zeros(n, np.float32), -0.5, 0.5))
+    compr = gu.empty(plan.compressed_words, torch.int32, fill=-1)
+    plan.compress(-0.5, 0.5, compr)
+    gu.sync()
+    check(np.array_equal(gu.host(compr, np.uint32), np.concatenate(blocks)), "multi-tensor blocks")
+    plan.destroy()
+    # QSGD step and GRandK gather with a capped grid
+    print("[case] capped qsgd", flush=True)
+    n, W, s, seed = 50_003, 3, 127, 11
+    gs = [si.heavy_tailed_f32(400 + w, n, 0.02) for w in range(W)]
+    g_dev = [gu.dev(g) for g in gs]
+    norm = torch.empty(1, dtype=torch.float32, device=gu.DEV)
+    ws = torch.empty(gcq.qsgd_maxnorm_ws_bytes(W, n), dtype=torch.uint8, device=gu.DEV)
+    gcq.qsgd_global_maxnorm(g_dev, norm, ws)
+    lv = [gu.empty(n, torch.int8) for _ in range(W)]
+    for w in range(W):
+        gcq.qsgd_maxnorm_quantize(g_dev[w], norm, s, seed, w, lv[w])
+    sums = gu.empty(n, torch.int32)
+    out = gu.empty(n, torch.float32)
+    gcq.qsgd_dequant_sum(lv, norm, s, out, sums=sums)
+    gu.sync()
+    norm_or = oracle.maxnorm(gs)
+    lv_or = [oracle.qsgd_quantize(g, norm_or, s, seed, w) for w, g in enumerate(gs)]
+    for w in range(W):
+        check(np.array_equal(gu.host(lv[w]), lv_or[w]), f"qsgd levels worker {w}")
+    s_or = oracle.level_sum(lv_or)
+    check(np.array_equal(gu.host(sums), s_or), "qsgd sums")
+    check(np.array_equal(gu.host(out), oracle.qsgd_dequantize(s_or, norm_or, s)), "qsgd dequantized")
+    idx = oracle.randk_indices(n, 5000, 3)
+    gk = gu.empty(5000, torch.float32)
+    gcq.gather_f32(g_dev[0], gu.dev(idx), gk)
+    dense = gu.empty(n, torch.float32, fill=float("nan"))
+    gcq.qsgd_dequant_sum([gu.dev(q[:5000].copy()) for q in lv_or], norm, s, dense,
+                         scatter_idx=gu.dev(idx), dense_n=n)
+    gu.sync()
+    check(np.array_equal(gu.host(gk), oracle.gather(gs[0], idx)), "gather")
+    sk = oracle.level_sum([q[:5000].copy() for q in lv_or])
+    check(np.array_equal(gu.host(dense),
+                         oracle.scatter_dense(oracle.qsgd_dequantize(sk, norm_or, s), idx, n)),
+          "scatter-dequantize")
+    print("OK", flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -209,3 +209,18 @@ def test_multi_tensor_bert_base_full_size(gcq):
     sizes = si.bert_base_sizes()
     assert len(sizes) == 198 and sum(sizes) == si.BERT_BASE_PARAMS
     _multi_case(gcq, sizes, 3, 0.005, 0.005)
+
+
+def test_striding_paths_with_capped_grid(gcq):
+    """Every kernel family with its grid capped at 3 workgroups (so each one
+    strides over many tiles), in a child process; see grid_cap_check.py."""
+    import os
+    import subprocess
+    import sys
+    announce("capped-grid parity (child process, GCQ_MAX_GRID_BLOCKS=3)")
+    env = dict(os.environ, GCQ_MAX_GRID_BLOCKS="3")
+    script = os.path.join(os.path.dirname(__file__), "grid_cap_check.py")
+    res = subprocess.run([sys.executable, "-u", script], env=env, capture_output=True,
+                         text=True, timeout=110)
+    print(res.stdout[-2000:], res.stderr[-2000:])
+    assert res.returncode == 0 and res.stdout.strip().endswith("OK")
