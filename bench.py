@@ -44,8 +44,27 @@ W_C3 = 8
 S_C3 = 127
 SIGMA_C3 = 0.02
 
-PROFILE_TRAFFIC = ROOT / "profiles" / "compress_2bit_resnet50_traffic.md"
-KERNEL_SOURCE = ROOT / "gradient_compression_quantize_amd" / "csrc" / "twobit.hip"
+PROFILE_TRAFFIC = ROOT / "profiles" / "hbm_traffic_resnet50_vgg16.md"
+PROFILE_STATS = ROOT / "profiles" / "kernel_stats_resnet50_vgg16.md"
+KERNEL_SOURCES = [ROOT / "gradient_compression_quantize_amd" / "csrc" / f
+                  for f in ("gcq_internal.h", "twobit.hip", "qsgd.hip")]
+
+# The rocprofv3 runs the committed summaries come from (run from the repo
+# root; the output directories are scratch).
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -T -d gpurun_out/prof_bench -o bench "
+             "--output-format csv -- python3 -u bench.py --steps 20 --warmup 5 --qsgd-steps 5 "
+             "--skip-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_fetch -o fetch --output-format csv "
+             "-- python3 -u bench.py --steps 3 --warmup 1 --qsgd-steps 1 --skip-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_write -o write --output-format csv "
+             "-- python3 -u bench.py --steps 3 --warmup 1 --qsgd-steps 1 --skip-cpu-baseline",
+    "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_cal_fetch -o cal "
+                 "--output-format csv -- python3 -u bench.py --calibrate-copy",
+    "cal_write": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_cal_write -o cal "
+                 "--output-format csv -- python3 -u bench.py --calibrate-copy",
+    "summary": "python3 bench.py --summarize-profiles gpurun_out",
+}
 
 
 def log(msg: str) -> None:
@@ -75,21 +94,130 @@ def parse_args():
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB (counter calibration)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write the profiles/ summaries from rocprofv3 output under DIR")
     return ap.parse_args()
 
 
-def traffic_from_profile() -> int | None:
-    """HBM bytes per compress_2bit launch measured with rocprofv3 counters,
-    if the committed measurement was taken on the current kernel source."""
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(f.read_bytes())
+    return h.hexdigest()
+
+
+def traffic_from_profile(kernel: str) -> int | None:
+    """HBM bytes per launch of `kernel` measured with rocprofv3 counters, if
+    the committed measurement was taken on the current kernel sources."""
     if not PROFILE_TRAFFIC.exists():
         return None
     text = PROFILE_TRAFFIC.read_text()
-    m_b = re.search(r"^traffic_bytes_per_launch:\s*([0-9]+)", text, re.M)
     m_h = re.search(r"^kernel_source_sha256:\s*([0-9a-f]+)", text, re.M)
-    if not (m_b and m_h):
+    m_b = re.search(rf"^traffic_bytes_per_launch\[{kernel}\]:\s*([0-9]+)", text, re.M)
+    if not (m_b and m_h) or m_h.group(1) != kernel_source_hash():
         return None
-    cur = hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()
-    return int(m_b.group(1)) if m_h.group(1) == cur else None
+    return int(m_b.group(1))
+
+
+def _read_counters(path: pathlib.Path):
+    import csv
+    import collections
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize_profiles(out_dir: str) -> None:
+    """Write the two profiles/ summaries from rocprofv3 CSV output."""
+    import csv
+    d = pathlib.Path(out_dir)
+    n2, W2, n3, W3 = N_C2, W_C2, N_C3, W_C3
+    algo = {
+        "compress_2bit_vec_kernel": (8 * n2, 4 * n2 + 4 * (3 + (n2 + 15) // 16)),
+        "decompress_2bit_vec_kernel": (4 * W2 * (3 + (n2 + 15) // 16), 4 * n2),
+        "maxabs_partial_kernel": (4 * W3 * n3, 0),
+        "qsgd_quantize_kernel": (4 * n3, n3),
+        "qsgd_dequant_sum_kernel": (W3 * n3, 8 * n3),
+    }
+    cal_f = _read_counters(next((d / "pmc_cal_fetch").glob("*counter_collection.csv")))
+    cal_w = _read_counters(next((d / "pmc_cal_write").glob("*counter_collection.csv")))
+    copy_name = max(cal_w, key=lambda k: sum(cal_w[k]))
+    copy_bytes = 4 << 28
+    f_kib = sum(cal_f[copy_name]) / len(cal_f[copy_name])
+    w_kib = sum(cal_w[copy_name]) / len(cal_w[copy_name])
+    f_scale = copy_bytes / (f_kib * 1024)
+    w_scale = copy_bytes / (w_kib * 1024)
+    fetch = _read_counters(next((d / "pmc_fetch").glob("*counter_collection.csv")))
+    write = _read_counters(next((d / "pmc_write").glob("*counter_collection.csv")))
+    lines = [
+        "# HBM traffic per launch from rocprofv3 counters",
+        "",
+        "Workloads: the 2-bit step on the ResNet-50-sized flat gradient "
+        f"({n2:,} fp32 values, {W2} workers, thresholds +-0.01) and the QSGD-MN step on the "
+        f"VGG16-sized gradient ({n3:,} fp32 values, {W3} workers, s = 127).",
+        "",
+        "Commands (repo root, one counter per run):",
+        "",
+        *[f"    {PROFILE_COMMANDS[k]}" for k in ("fetch", "write", "cal_fetch", "cal_write",
+                                                 "summary")],
+        "",
+        "Calibration: a plain device copy of 1 GiB (`bench.py --calibrate-copy`, "
+        f"kernel `{copy_name}`) reads and writes {copy_bytes:,} bytes. Its counters read "
+        f"FETCH_SIZE = {f_kib:,.1f} KiB and WRITE_SIZE = {w_kib:,.1f} KiB per dispatch, so "
+        f"bytes = FETCH_SIZE x 1024 x {f_scale:.4f} and WRITE_SIZE x 1024 x {w_scale:.4f}.",
+        "",
+        "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (calibrated) | "
+        "algorithmic bytes | ratio |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    machine = []
+    for k, (ar, aw) in algo.items():
+        if k not in fetch or k not in write:
+            continue
+        fk = sum(fetch[k]) / len(fetch[k])
+        wk = sum(write[k]) / len(write[k])
+        hb = fk * 1024 * f_scale + wk * 1024 * w_scale
+        lines.append(f"| {k} | {len(fetch[k])} | {fk:,.1f} | {wk:,.1f} | {hb:,.0f} | "
+                     f"{ar + aw:,} | {hb / (ar + aw):.4f} |")
+        machine.append(f"traffic_bytes_per_launch[{k}]: {int(round(hb))}")
+    lines += ["", "Algorithmic bytes: compress reads grad and residual and writes residual and "
+              "the block (12 n + 4 (3 + ceil(n/16))); dequantize-sum reads W blocks and writes "
+              "n fp32; max-norm reads W n fp32; quantize reads n fp32 and writes n int8; the "
+              "level sum reads W n int8 and writes n int32 + n fp32.", "",
+              "Machine-readable (bench.py reads these while the kernel sources are unchanged):",
+              "", f"kernel_source_sha256: {kernel_source_hash()}", *machine, ""]
+    PROFILE_TRAFFIC.write_text("\n".join(lines))
+
+    stats = list(csv.DictReader(open(next((d / "prof_bench").glob("*kernel_stats.csv")))))
+    lines = [
+        "# Kernel durations from rocprofv3 (kernel trace)",
+        "",
+        "Command (repo root):",
+        "",
+        f"    {PROFILE_COMMANDS['trace']}",
+        f"    {PROFILE_COMMANDS['summary']}",
+        "",
+        "The 2-bit step (8 x compress_2bit + decompress_2bit_sum W=8) runs 5 warm-up, 20 timed "
+        "and 20 kernel-timing steps; the QSGD-MN step runs 2 warm-up and 5 timed steps.",
+        "",
+        "| kernel | calls | average us | min us | max us | share of GPU time |",
+        "|---|---|---|---|---|---|",
+    ]
+    for r in stats:
+        lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f}% |")
+    comp = next((r for r in stats if r["Name"] == "compress_2bit_vec_kernel"), None)
+    if comp:
+        us = float(comp["AverageNs"]) / 1e3
+        gbs = compress_bytes(n2) / (us * 1e-6) / 1e9
+        lines += ["", f"compress_2bit at {n2:,} values: {compress_bytes(n2):,} algorithmic bytes "
+                  f"in {us:.2f} us = {gbs:,.0f} GB/s = {100 * gbs / HBM_PEAK_GBS:.1f}% of "
+                  f"{HBM_PEAK_GBS:,.0f} GB/s."]
+    lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
+    PROFILE_STATS.write_text("\n".join(lines))
+    print(f"wrote {PROFILE_TRAFFIC} and {PROFILE_STATS}")
 
 
 def cpu_model() -> str:
@@ -127,17 +255,15 @@ def bench_2bit(gcq, torch, np, si, steps: int, warmup: int):
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        for w in range(W):
-            if ev is not None:
-                ev[0][w].record(stream)
-            gcq.compress_2bit(grads[w], res[w], -THR_C2, THR_C2, comprs[w], stream)
-            if ev is not None:
-                ev[1][w].record(stream)
         if ev is not None:
-            ev[2].record(stream)
+            ev[0].record(stream)
+        for w in range(W):
+            gcq.compress_2bit(grads[w], res[w], -THR_C2, THR_C2, comprs[w], stream)
+        if ev is not None:
+            ev[1].record(stream)
         gcq.decompress_2bit_sum(comprs, n, out, stream)
         if ev is not None:
-            ev[3].record(stream)
+            ev[2].record(stream)
 
     log(f"2-bit: warmup {warmup} steps")
     for _ in range(warmup):
@@ -157,14 +283,17 @@ def bench_2bit(gcq, torch, np, si, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / steps
-    # kernel pass: K more steps with an event pair around every launch
-    evs = [([mk() for _ in range(W)], [mk() for _ in range(W)], mk(), mk()) for _ in range(steps)]
-    log(f"2-bit: per-launch events over {steps} more steps")
+    # kernel pass: K more steps with events around the 8 back-to-back compress
+    # launches and around the dequantize-sum; a compress launch's duration is
+    # its group's time over 8 (events around every launch would add their own
+    # packets' latency to each one)
+    evs = [[mk() for _ in range(3)] for _ in range(steps)]
+    log(f"2-bit: kernel timing over {steps} more steps")
     for k in range(steps):
         step(evs[k])
     torch.cuda.synchronize()
-    comp_ms = [evs[k][0][w].elapsed_time(evs[k][1][w]) for k in range(steps) for w in range(W)]
-    deq_ms = [evs[k][2].elapsed_time(evs[k][3]) for k in range(steps)]
+    comp_ms = [evs[k][0].elapsed_time(evs[k][1]) / W for k in range(steps)]
+    deq_ms = [evs[k][1].elapsed_time(evs[k][2]) for k in range(steps)]
     del grads, res, comprs, out
     torch.cuda.empty_cache()
     return {"ms_per_step": ms_step, "wall_s": wall, "compress_ms": comp_ms, "dequant_sum_ms": deq_ms}
@@ -264,6 +393,9 @@ def main() -> int:
         print("bench.py: this library runs on one GPU; multi-GPU runs are not part of it "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         return 2
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return 0
     import numpy as np
     import torch
 
@@ -286,7 +418,7 @@ def main() -> int:
     comp_ms = sum(r2["compress_ms"]) / len(r2["compress_ms"])
     deq_ms = sum(r2["dequant_sum_ms"]) / len(r2["dequant_sum_ms"])
     comp_gbs = compress_bytes(N_C2) / (comp_ms / 1e3) / 1e9
-    traffic = traffic_from_profile()
+    traffic = traffic_from_profile("compress_2bit_vec_kernel")
 
     result = {
         "metric": "2-bit EF quantize+pack GB/s and % HBM peak, 25.6M fp32; QSGD-MN elems/s",
@@ -312,7 +444,7 @@ def main() -> int:
         "kernels": {
             "compress_2bit": {"avg_ms": round(comp_ms, 5), "gbs": round(comp_gbs, 1),
                               "algorithmic_bytes": compress_bytes(N_C2),
-                              "launches": len(r2["compress_ms"])},
+                              "launches": W_C2 * len(r2["compress_ms"])},
             "decompress_2bit_sum": {"avg_ms": round(deq_ms, 5),
                                     "gbs": round(dequant_sum_bytes(N_C2, W_C2) / (deq_ms / 1e3) / 1e9, 1),
                                     "algorithmic_bytes": dequant_sum_bytes(N_C2, W_C2),

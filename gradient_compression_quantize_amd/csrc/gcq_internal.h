@@ -49,6 +49,19 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
 __device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
 
+// CDNA4 dispatches the workgroups of a launch round-robin over its 8 XCDs,
+// each with its own L2: workgroup i runs on XCD i % 8. This bijection of
+// [0, B) gives each XCD one contiguous range of logical workgroup indices,
+// so that neighbouring tiles (which share the cache lines at their edges)
+// meet in the same L2.
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t i, uint32_t B)
+{
+    const uint32_t q = B / kXcds, r = B % kXcds, x = i % kXcds, k = i / kXcds;
+    return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
 // OR of a 32-bit value over the 4 lanes of a DPP quad (lanes 4k..4k+3);
 // every lane of the quad gets the result. Two quad_perm moves, no LDS.
 // quad_perm selectors: [1,0,3,2] = 0xB1 (xor 1), [2,3,0,1] = 0x4E (xor 2).
