@@ -134,16 +134,18 @@ __global__ __launch_bounds__(kFinalThreads) void max_final_kernel(const float* _
 // ---- quantize --------------------------------------------------------------
 
 // floor(x + u) exactly, for x = (|g| / norm) * s (two fp32 roundings) and
-// u = (r >> 8) * 2^-24: with l = floor(x) and p = x - l (exact), the level
-// is l + 1 iff p >= 1 - u, and 1 - u = (2^24 - (r >> 8)) * 2^-24 is exact.
-__device__ __forceinline__ int qsgd_level(float g, uint32_t r, float norm, float s_f)
+// u = k * 2^-24 with k = r >> 8, in integer arithmetic:
+//   x * 2^24 is exact (a power-of-two scaling of a value at most 127), and
+//   floor(x + u) = floor((x * 2^24 + k) / 2^24) = (floor(x * 2^24) + k) >> 24,
+// where floor(x * 2^24) < 2^31 and k < 2^24, so the sum fits in 32 bits.
+// s24 = s * 2^24 is exact, and fl(q * s24) = fl(q * s) * 2^24 whenever
+// fl(q * s) is a normal number; below that x < 2^-126 and both sides give
+// level 0. The conversion truncates, which is the floor for X >= 0.
+__device__ __forceinline__ int qsgd_level(float g, uint32_t r, float norm, float s24)
 {
-    const float a = fabsf(g);
-    const float x = (a / norm) * s_f;
-    const float l = floorf(x);
-    const float p = x - l;
-    const float one_minus_u = float(16777216u - (r >> 8)) * 0x1p-24f;
-    const int m = int(l) + (p >= one_minus_u ? 1 : 0);
+    const float q = fabsf(g) / norm;
+    const uint32_t X = static_cast<uint32_t>(q * s24);
+    const int m = static_cast<int>((X + (r >> 8)) >> 24);
     return g < 0.0f ? -m : m;
 }
 
@@ -156,7 +158,7 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d)
 // One float4 slot q per lane per pass: Philox counter (q lo, q hi, worker, 0)
 // gives the four words of elements 4q .. 4q+3.
 __global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
-    const float* __restrict__ grad, size_t n, const float* __restrict__ norm_ptr, float s_f,
+    const float* __restrict__ grad, size_t n, const float* __restrict__ norm_ptr, float s24,
     uint32_t k0, uint32_t k1, uint32_t worker, int8_t* __restrict__ levels, int vec)
 {
     const float norm = *norm_ptr;
@@ -176,10 +178,10 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
         int lv0 = 0, lv1 = 0, lv2 = 0, lv3 = 0;
         if (norm != 0.0f) {
             const U4 r = philox4x32_10(U4{uint32_t(q), uint32_t(q >> 32), worker, 0u}, k0, k1);
-            lv0 = qsgd_level(g.x, r.x, norm, s_f);
-            lv1 = qsgd_level(g.y, r.y, norm, s_f);
-            lv2 = qsgd_level(g.z, r.z, norm, s_f);
-            lv3 = qsgd_level(g.w, r.w, norm, s_f);
+            lv0 = qsgd_level(g.x, r.x, norm, s24);
+            lv1 = qsgd_level(g.y, r.y, norm, s24);
+            lv2 = qsgd_level(g.z, r.z, norm, s24);
+            lv3 = qsgd_level(g.w, r.w, norm, s24);
         }
         if (full) {
             __builtin_nontemporal_store(pack4(lv0, lv1, lv2, lv3),
@@ -208,39 +210,83 @@ __device__ __forceinline__ int sbyte(uint32_t w, int k)
 }
 
 // Dense form. vec: every level pointer 4-byte aligned, out 16-byte aligned,
-// sums NULL or 16-byte aligned.
+// sums NULL or 16-byte aligned. Each wave takes tiles of kDqTile float4 slots
+// (kDqUnroll per lane); WC > 0: W == WC at compile time, so every worker's
+// level words are in flight together (WC == 0: W read at run time, in groups
+// of four).
+constexpr int kDqUnroll = 2;
+constexpr size_t kDqTile = size_t(kWave) * kDqUnroll;
+
+__device__ __forceinline__ void dequant_store(float norm, float s_f, i32x4 S, int32_t* sums,
+                                              float* out, size_t q)
+{
+    if (sums)
+        __builtin_nontemporal_store(S, reinterpret_cast<i32x4*>(sums) + q);
+    const f32x4 o = {dequant(norm, S.x, s_f), dequant(norm, S.y, s_f), dequant(norm, S.z, s_f),
+                     dequant(norm, S.w, s_f)};
+    __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(out) + q);
+}
+
+template <int WC>
 __global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_kernel(
-    PtrTable<int8_t> tab, int W, size_t n, const float* __restrict__ norm_ptr, float s_f,
+    PtrTable<int8_t> tab, int W_rt, size_t n, const float* __restrict__ norm_ptr, float s_f,
     int32_t* __restrict__ sums, float* __restrict__ out, int vec)
 {
+    const int W = WC > 0 ? WC : W_rt;
     const float norm = *norm_ptr;
     const size_t nslots = (n + 3) >> 2;
     const size_t nfull = n >> 2;
-    const size_t stride = size_t(gridDim.x) * kThreads;
-    for (size_t q = size_t(blockIdx.x) * kThreads + threadIdx.x; q < nslots; q += stride) {
-        if (vec && q < nfull) {
-            i32x4 S = {0, 0, 0, 0};
-            for (int w = 0; w < W; ++w) {
-                const uint32_t word =
-                    __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tab.p[w]) + q);
-                S.x += sbyte(word, 0);
-                S.y += sbyte(word, 1);
-                S.z += sbyte(word, 2);
-                S.w += sbyte(word, 3);
+    const size_t ntiles = (nslots + kDqTile - 1) / kDqTile;
+    const int lane = threadIdx.x & (kWave - 1);
+    const size_t stride = size_t(gridDim.x) * (kThreads / kWave);
+    for (size_t t = size_t(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave; t < ntiles;
+         t += stride) {
+        const size_t q0 = t * kDqTile + lane;
+        if (vec && (t + 1) * kDqTile <= nfull) {
+            i32x4 S[kDqUnroll];
+#pragma unroll
+            for (int u = 0; u < kDqUnroll; ++u)
+                S[u] = i32x4{0, 0, 0, 0};
+            constexpr int kGroup = WC > 0 ? WC : 4;
+            for (int w0 = 0; w0 < W; w0 += kGroup) {
+                uint32_t words[kGroup][kDqUnroll];
+#pragma unroll
+                for (int dw = 0; dw < kGroup; ++dw)
+#pragma unroll
+                    for (int u = 0; u < kDqUnroll; ++u)
+                        words[dw][u] = (WC == 0 && w0 + dw >= W)
+                                           ? 0u
+                                           : __builtin_nontemporal_load(
+                                                 reinterpret_cast<const uint32_t*>(tab.p[w0 + dw]) +
+                                                 q0 + size_t(u) * kWave);
+#pragma unroll
+                for (int dw = 0; dw < kGroup; ++dw)
+#pragma unroll
+                    for (int u = 0; u < kDqUnroll; ++u) {
+                        S[u].x += sbyte(words[dw][u], 0);
+                        S[u].y += sbyte(words[dw][u], 1);
+                        S[u].z += sbyte(words[dw][u], 2);
+                        S[u].w += sbyte(words[dw][u], 3);
+                    }
             }
-            if (sums)
-                __builtin_nontemporal_store(S, reinterpret_cast<i32x4*>(sums) + q);
-            const f32x4 o = {dequant(norm, S.x, s_f), dequant(norm, S.y, s_f),
-                             dequant(norm, S.z, s_f), dequant(norm, S.w, s_f)};
-            __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(out) + q);
+#pragma unroll
+            for (int u = 0; u < kDqUnroll; ++u)
+                dequant_store(norm, s_f, S[u], sums, out, q0 + size_t(u) * kWave);
         } else {
-            for (size_t i = q * 4; i < q * 4 + 4 && i < n; ++i) {
-                int S = 0;
-                for (int w = 0; w < W; ++w)
-                    S += int(tab.p[w][i]);
-                if (sums)
-                    sums[i] = S;
-                out[i] = dequant(norm, S, s_f);
+            // the partial tile, or buffers without the vector alignment
+#pragma unroll 1
+            for (int u = 0; u < kDqUnroll; ++u) {
+                const size_t q = q0 + size_t(u) * kWave;
+#pragma unroll 1
+                for (size_t i = q * 4; i < q * 4 + 4 && i < n; ++i) {
+                    int S = 0;
+#pragma unroll 1
+                    for (int w = 0; w < W; ++w)
+                        S += int(tab.p[w][i]);
+                    if (sums)
+                        sums[i] = S;
+                    out[i] = dequant(norm, S, s_f);
+                }
             }
         }
     }
@@ -425,8 +471,8 @@ GCQ_API int qsgd_maxnorm_quantize(const float* grad, size_t n, const float* norm
         return GC_OK;
     const int vec = (aligned16(grad) && aligned4(levels)) ? 1 : 0;
     hipLaunchKernelGGL(qsgd_quantize_kernel, dim3(grid_for(ceil_div(n, 4))), dim3(kThreads), 0,
-                       stream, grad, n, norm, float(s), uint32_t(seed), uint32_t(seed >> 32),
-                       worker, levels, vec);
+                       stream, grad, n, norm, float(s) * 16777216.0f, uint32_t(seed),
+                       uint32_t(seed >> 32), worker, levels, vec);
     return check_launch("qsgd_maxnorm_quantize");
 }
 
@@ -461,8 +507,29 @@ GCQ_API int qsgd_dequant_sum(const int8_t* const* levels, int W, size_t n, const
         if (n == 0)
             return GC_OK;
         const int vec = (lv_aligned && aligned16(out) && (!sums || aligned16(sums))) ? 1 : 0;
-        hipLaunchKernelGGL(qsgd_dequant_sum_kernel, dim3(grid_for(ceil_div(n, 4))),
-                           dim3(kThreads), 0, stream, tab, W, n, norm, s_f, sums, out, vec);
+        const size_t ntiles = ceil_div(ceil_div(n, 4), kDqTile);
+        const dim3 grid(std::max<size_t>(1, std::min(ceil_div(ntiles, kThreads / kWave),
+                                                     max_grid_blocks()))),
+            block(kThreads);
+        switch (W) {
+#define GCQ_DQ_CASE(k)                                                                      \
+    case k:                                                                                 \
+        hipLaunchKernelGGL((qsgd_dequant_sum_kernel<k>), grid, block, 0, stream, tab, W, n, \
+                           norm, s_f, sums, out, vec);                                      \
+        break;
+            GCQ_DQ_CASE(1)
+            GCQ_DQ_CASE(2)
+            GCQ_DQ_CASE(3)
+            GCQ_DQ_CASE(4)
+            GCQ_DQ_CASE(5)
+            GCQ_DQ_CASE(6)
+            GCQ_DQ_CASE(7)
+            GCQ_DQ_CASE(8)
+#undef GCQ_DQ_CASE
+        default:
+            hipLaunchKernelGGL((qsgd_dequant_sum_kernel<0>), grid, block, 0, stream, tab, W, n,
+                               norm, s_f, sums, out, vec);
+        }
         return check_launch("qsgd_dequant_sum");
     }
     if (dense_n > 0) {

@@ -206,3 +206,26 @@ def test_grandk_step(gcq, full):
     np.testing.assert_array_equal(gu.host(sums), s_or)
     dense_or = oracle.scatter_dense(oracle.qsgd_dequantize(s_or, norm_or, s), idx_or, n)
     check_deq(gu.host(dense), dense_or)
+
+
+@pytest.mark.parametrize("s", [1, 4, 7, 127])
+def test_qsgd_level_edges(gcq, s):
+    """Values whose scaled magnitude x is integral, one ulp either side of an
+    integer, tiny or subnormal, over many rounding seeds: the level must be
+    floor(x + u) exactly, as the oracle computes it."""
+    announce(f"qsgd level edges s={s}")
+    base = [1.0, -1.0, 0.0, -0.0, 1e-45, -1e-40, 1e-30, 2.0 ** -31, 0.5, 0.25, 1.0 / 3.0]
+    for j in range(0, s + 1):
+        v = np.float32(j / s)
+        base += [float(v), float(np.nextafter(v, np.float32(2))), float(np.nextafter(v, np.float32(0)))]
+    g = np.array(base * 4, np.float32)
+    g[len(base):2 * len(base)] *= -1
+    g = np.clip(g, -1.0, 1.0).astype(np.float32)  # norm = 1 exactly
+    g_dev = gu.dev(g)
+    norm = torch.ones(1, dtype=torch.float32, device=gu.DEV)
+    lv = gu.empty(g.size, torch.int8)
+    for seed in range(64):
+        gcq.qsgd_maxnorm_quantize(g_dev, norm, s, seed, seed % 5, lv)
+        gu.sync()
+        np.testing.assert_array_equal(gu.host(lv), oracle.qsgd_quantize(g, 1.0, s, seed, seed % 5),
+                                      err_msg=f"seed {seed}")
