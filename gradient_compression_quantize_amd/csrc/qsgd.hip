@@ -139,14 +139,54 @@ __global__ __launch_bounds__(kFinalThreads) void max_final_kernel(const float* _
 //   floor(x + u) = floor((x * 2^24 + k) / 2^24) = (floor(x * 2^24) + k) >> 24,
 // where floor(x * 2^24) < 2^31 and k < 2^24, so the sum fits in 32 bits.
 // s24 = s * 2^24 is exact, and fl(q * s24) = fl(q * s) * 2^24 whenever
-// fl(q * s) is a normal number; below that x < 2^-126 and both sides give
+// fl(q * s) is a normal number; below that x < 2^-126 and every path gives
 // level 0. The conversion truncates, which is the floor for X >= 0.
-__device__ __forceinline__ int qsgd_level(float g, uint32_t r, float norm, float s24)
+//
+// The quotient: the exact path divides (IEEE, correctly rounded). The fast
+// path multiplies by inv = fl(1 / norm) instead. Every rounding involved
+// (fl(1/norm), fl(a * inv), fl(a / norm), and the product with s24 on each
+// path) is within 2^-24 relative of its real value, so for |g| <= norm the
+// two values of X differ by at most 5 * 2^-24 * X < 5 * 127 = 635. With
+// t = floor(X) + k, the exact t therefore lies within kSlack = 2048 of the
+// fast one; when t - kSlack and t + kSlack fall in the same 2^24 bucket the
+// fast level is the exact level. Otherwise (about one value in 4000) the
+// lane recomputes its slot through the division. `fast` is false when norm
+// is so small that 1 / norm could overflow: then every value divides.
+constexpr uint32_t kSlack = 2048;
+
+__device__ __forceinline__ uint32_t level_from_quotient(float q, uint32_t r, float s24)
 {
-    const float q = fabsf(g) / norm;
-    const uint32_t X = static_cast<uint32_t>(q * s24);
-    const int m = static_cast<int>((X + (r >> 8)) >> 24);
-    return g < 0.0f ? -m : m;
+    return (static_cast<uint32_t>(q * s24) + (r >> 8)) >> 24;
+}
+
+// Levels of four values (one float4 slot and its four Philox words), with the
+// sign of g applied. One branch per slot: the exact path runs for the slot
+// when any of its values is near a bucket edge, or when `fast` is off.
+__device__ __forceinline__ void qsgd_levels4(f32x4 g, U4 r, float norm, float inv, float s24,
+                                             bool fast, int lv[4])
+{
+    const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
+    uint32_t m[4];
+    // t is within kSlack of a multiple of 2^24 iff (t + kSlack) mod 2^24 <
+    // 2 kSlack (t < 2^31 + 2^24, so t + kSlack does not wrap); the test also
+    // flags t < kSlack, which only sends those values to the exact path
+    uint32_t closest = fast ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t t = static_cast<uint32_t>((fabsf(g[k]) * inv) * s24) + (rr[k] >> 8);
+        m[k] = t >> 24;
+        closest = min(closest, (t + kSlack) & 0x00FFFFFFu);
+    }
+    if (closest < 2 * kSlack) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            m[k] = level_from_quotient(fabsf(g[k]) / norm, rr[k], s24);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int mi = static_cast<int>(m[k]);
+        lv[k] = g[k] < 0.0f ? -mi : mi;
+    }
 }
 
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d)
@@ -155,44 +195,81 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d)
            (uint32_t(d) << 24);
 }
 
-// One float4 slot q per lane per pass: Philox counter (q lo, q hi, worker, 0)
-// gives the four words of elements 4q .. 4q+3.
+// Each wave takes tiles of kQTile float4 slots, kQUnroll per lane: the
+// Philox counter (q lo, q hi, worker, 0) of slot q gives the four words of
+// elements 4q .. 4q+3, and a lane's kQUnroll independent Philox chains
+// interleave to fill the VALU pipeline (the kernel is bound by that ALU
+// work, not by HBM). Full tiles take a branch-free vector path; the one
+// partial tile, and buffers without the vector alignment, take a checked
+// scalar path. kLoop = false: one tile per wave (the usual case).
+constexpr int kQUnroll = 2;
+constexpr size_t kQTile = size_t(kWave) * kQUnroll;
+
+template <bool kLoop>
 __global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
     const float* __restrict__ grad, size_t n, const float* __restrict__ norm_ptr, float s24,
     uint32_t k0, uint32_t k1, uint32_t worker, int8_t* __restrict__ levels, int vec)
 {
     const float norm = *norm_ptr;
+    const bool fast = norm >= 0x1p-120f;
+    const float inv = fast ? 1.0f / norm : 0.0f;
     const size_t nslots = (n + 3) >> 2;
     const size_t nfull = n >> 2;
-    const size_t stride = size_t(gridDim.x) * kThreads;
-    for (size_t q = size_t(blockIdx.x) * kThreads + threadIdx.x; q < nslots; q += stride) {
-        const bool full = vec && q < nfull;
-        f32x4 g;
-        if (full) {
-            g = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(grad) + q);
-        } else {
+    const size_t ntiles = (nslots + kQTile - 1) / kQTile;
+    const int lane = threadIdx.x & (kWave - 1);
+    const size_t stride = size_t(gridDim.x) * (kThreads / kWave);
+    for (size_t t = size_t(blockIdx.x) * (kThreads / kWave) + threadIdx.x / kWave; t < ntiles;
+         t += stride) {
+        const size_t q0 = t * kQTile + lane;
+        if (vec && (t + 1) * kQTile <= nfull) {
+            f32x4 g[kQUnroll];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                g[k] = (q * 4 + k < n) ? grad[q * 4 + k] : 0.0f;
-        }
-        int lv0 = 0, lv1 = 0, lv2 = 0, lv3 = 0;
-        if (norm != 0.0f) {
-            const U4 r = philox4x32_10(U4{uint32_t(q), uint32_t(q >> 32), worker, 0u}, k0, k1);
-            lv0 = qsgd_level(g.x, r.x, norm, s24);
-            lv1 = qsgd_level(g.y, r.y, norm, s24);
-            lv2 = qsgd_level(g.z, r.z, norm, s24);
-            lv3 = qsgd_level(g.w, r.w, norm, s24);
-        }
-        if (full) {
-            __builtin_nontemporal_store(pack4(lv0, lv1, lv2, lv3),
-                                        reinterpret_cast<uint32_t*>(levels) + q);
-        } else {
-            const int lv[4] = {lv0, lv1, lv2, lv3};
+            for (int u = 0; u < kQUnroll; ++u)
+                g[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(grad) + q0 +
+                                                  size_t(u) * kWave);
+            uint32_t packed[kQUnroll] = {};
+            if (norm != 0.0f) {
+                U4 r[kQUnroll];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (q * 4 + k < n)
-                    levels[q * 4 + k] = int8_t(lv[k]);
+                for (int u = 0; u < kQUnroll; ++u) {
+                    const size_t q = q0 + size_t(u) * kWave;
+                    r[u] = philox4x32_10(U4{uint32_t(q), uint32_t(q >> 32), worker, 0u}, k0, k1);
+                }
+#pragma unroll
+                for (int u = 0; u < kQUnroll; ++u) {
+                    int lv[4];
+                    qsgd_levels4(g[u], r[u], norm, inv, s24, fast, lv);
+                    packed[u] = pack4(lv[0], lv[1], lv[2], lv[3]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kQUnroll; ++u)
+                __builtin_nontemporal_store(packed[u], reinterpret_cast<uint32_t*>(levels) + q0 +
+                                                           size_t(u) * kWave);
+        } else {
+#pragma unroll 1
+            for (int u = 0; u < kQUnroll; ++u) {
+                const size_t q = q0 + size_t(u) * kWave;
+                if (q >= nslots)
+                    break;
+                f32x4 g;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    g[k] = (q * 4 + k < n) ? grad[q * 4 + k] : 0.0f;
+                int lv[4] = {0, 0, 0, 0};
+                if (norm != 0.0f) {
+                    const U4 r =
+                        philox4x32_10(U4{uint32_t(q), uint32_t(q >> 32), worker, 0u}, k0, k1);
+                    qsgd_levels4(g, r, norm, inv, s24, fast, lv);
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (q * 4 + k < n)
+                        levels[q * 4 + k] = int8_t(lv[k]);
+            }
         }
+        if (!kLoop)
+            break;
     }
 }
 
@@ -470,9 +547,16 @@ GCQ_API int qsgd_maxnorm_quantize(const float* grad, size_t n, const float* norm
     if (n == 0)
         return GC_OK;
     const int vec = (aligned16(grad) && aligned4(levels)) ? 1 : 0;
-    hipLaunchKernelGGL(qsgd_quantize_kernel, dim3(grid_for(ceil_div(n, 4))), dim3(kThreads), 0,
-                       stream, grad, n, norm, float(s) * 16777216.0f, uint32_t(seed),
-                       uint32_t(seed >> 32), worker, levels, vec);
+    const size_t ntiles = ceil_div(ceil_div(n, 4), kQTile);
+    const size_t want = ceil_div(ntiles, kThreads / kWave);
+    const dim3 grid(std::min(want, max_grid_blocks())), block(kThreads);
+    const float s24 = float(s) * 16777216.0f;  // exact: s <= 127
+    if (want > max_grid_blocks())
+        hipLaunchKernelGGL(qsgd_quantize_kernel<true>, grid, block, 0, stream, grad, n, norm, s24,
+                           uint32_t(seed), uint32_t(seed >> 32), worker, levels, vec);
+    else
+        hipLaunchKernelGGL(qsgd_quantize_kernel<false>, grid, block, 0, stream, grad, n, norm,
+                           s24, uint32_t(seed), uint32_t(seed >> 32), worker, levels, vec);
     return check_launch("qsgd_maxnorm_quantize");
 }
 

@@ -229,3 +229,16 @@ def test_qsgd_level_edges(gcq, s):
         gu.sync()
         np.testing.assert_array_equal(gu.host(lv), oracle.qsgd_quantize(g, 1.0, s, seed, seed % 5),
                                       err_msg=f"seed {seed}")
+
+
+@pytest.mark.parametrize("norm_scale", [1e-38, 2.0 ** -121, 1e-30, 1e30])
+def test_qsgd_extreme_norms(gcq, norm_scale):
+    """Tiny norms (where 1/norm would overflow, so every value takes the
+    exact division) and huge ones, through the whole QSGD step."""
+    announce(f"qsgd extreme norm scale {norm_scale}")
+    g = (si.normal_f32(77, 10_007, 1.0) * np.float32(norm_scale)).astype(np.float32)
+    g[5] = np.float32(-3.0 * norm_scale)
+    norm, levels, sums, out = run_qsgd(gcq, [g], 127, 3)
+    norm_or = oracle.maxnorm([g])
+    assert norm.view(np.uint32) == norm_or.view(np.uint32)
+    np.testing.assert_array_equal(levels[0], oracle.qsgd_quantize(g, norm_or, 127, 3, 0))
