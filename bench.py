@@ -90,6 +90,8 @@ def parse_args():
     ap.add_argument("--qsgd-steps", type=int, default=10)
     ap.add_argument("--skip-qsgd", action="store_true", help="time only the 2-bit step")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-extra", action="store_true",
+                    help="skip the many-tensor and GlobalRandK measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -252,18 +254,17 @@ def bench_2bit(gcq, torch, np, si, steps: int, warmup: int):
     words = gcq.gc_compressed_2bit_words(n)
     comprs = [torch.empty(words, dtype=torch.int32, device=dev) for _ in range(W)]
     out = torch.empty(n, dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
 
     def step(ev=None):
         if ev is not None:
-            ev[0].record(stream)
+            ev[0].record()
         for w in range(W):
-            gcq.compress_2bit(grads[w], res[w], -THR_C2, THR_C2, comprs[w], stream)
+            gcq.compress_2bit(grads[w], res[w], -THR_C2, THR_C2, comprs[w])
         if ev is not None:
-            ev[1].record(stream)
-        gcq.decompress_2bit_sum(comprs, n, out, stream)
+            ev[1].record()
+        gcq.decompress_2bit_sum(comprs, n, out)
         if ev is not None:
-            ev[2].record(stream)
+            ev[2].record()
 
     log(f"2-bit: warmup {warmup} steps")
     for _ in range(warmup):
@@ -276,10 +277,10 @@ def bench_2bit(gcq, torch, np, si, steps: int, warmup: int):
     log(f"2-bit: timing {steps} steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t0.record(stream)
+    t0.record()
     for _ in range(steps):
         step()
-    t1.record(stream)
+    t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / steps
@@ -294,9 +295,20 @@ def bench_2bit(gcq, torch, np, si, steps: int, warmup: int):
     torch.cuda.synchronize()
     comp_ms = [evs[k][0].elapsed_time(evs[k][1]) / W for k in range(steps)]
     deq_ms = [evs[k][1].elapsed_time(evs[k][2]) for k in range(steps)]
+    # the same step replayed from a HIP graph (no host launch cost)
+    graph = graph_of(torch, step)
+    g0, g1 = mk(), mk()
+    g0.record()
+    for _ in range(steps):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / steps
+    del graph
     del grads, res, comprs, out
     torch.cuda.empty_cache()
-    return {"ms_per_step": ms_step, "wall_s": wall, "compress_ms": comp_ms, "dequant_sum_ms": deq_ms}
+    return {"ms_per_step": ms_step, "wall_s": wall, "compress_ms": comp_ms, "dequant_sum_ms": deq_ms,
+            "graph_ms_per_step": graph_ms}
 
 
 def bench_qsgd(gcq, torch, np, si, steps: int):
@@ -311,22 +323,21 @@ def bench_qsgd(gcq, torch, np, si, steps: int):
     levels = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(W)]
     sums = torch.empty(n, dtype=torch.int32, device=dev)
     out = torch.empty(n, dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
     mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     def step(seed, ev=None):
         if ev is not None:
-            ev[0].record(stream)
-        gcq.qsgd_global_maxnorm(grads, norm, ws, stream)
+            ev[0].record()
+        gcq.qsgd_global_maxnorm(grads, norm, ws)
         if ev is not None:
-            ev[1].record(stream)
+            ev[1].record()
         for w in range(W):
-            gcq.qsgd_maxnorm_quantize(grads[w], norm, s, seed, w, levels[w], stream)
+            gcq.qsgd_maxnorm_quantize(grads[w], norm, s, seed, w, levels[w])
         if ev is not None:
-            ev[2].record(stream)
-        gcq.qsgd_dequant_sum(levels, norm, s, out, sums=sums, stream=stream)
+            ev[2].record()
+        gcq.qsgd_dequant_sum(levels, norm, s, out, sums=sums)
         if ev is not None:
-            ev[3].record(stream)
+            ev[3].record()
 
     for _ in range(2):
         step(0)
@@ -356,6 +367,149 @@ def bench_qsgd(gcq, torch, np, si, steps: int):
         "algorithmic_bytes": (4 * W + 5 * W + W + 8) * n,
         "steps": steps,
     }
+
+
+def graph_of(torch, fn):
+    """Capture fn's launches (on torch's current stream) as a HIP graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # warm-up on a side stream, as capture requires
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    torch.cuda.synchronize()
+    return graph
+
+
+def multi_bytes(sizes) -> int:
+    return sum(12 * n + 4 * (3 + (n + 15) // 16) for n in sizes)
+
+
+def bench_multi(gcq, torch, np, si, steps: int):
+    """Many-tensor 2-bit compress over the BERT-Base parameter list (198
+    tensors, 109,482,240 values, thresholds +-0.005): one launch per step."""
+    import oracle
+    sizes = si.bert_base_sizes()
+    dev = "cuda"
+    log(f"multi-tensor: generating {len(sizes)} tensors ({sum(sizes)} values)")
+    host = [si.normal_f32(7919 * t, n, 0.005) for t, n in enumerate(sizes)]
+    grads = [torch.from_numpy(h).to(dev) for h in host]
+    res = [torch.zeros(n, dtype=torch.float32, device=dev) for n in sizes]
+    plan = gcq.Plan2bitMulti(grads, res)
+    compr = torch.empty(plan.compressed_words, dtype=torch.int32, device=dev)
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    for _ in range(3):
+        plan.compress(-0.005, 0.005, compr)
+    torch.cuda.synchronize()
+    t0, t1 = mk(), mk()
+    t0.record()
+    for _ in range(steps):
+        plan.compress(-0.005, 0.005, compr)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    plan.destroy()
+    del grads, res, compr
+    torch.cuda.empty_cache()
+    byts = multi_bytes(sizes)
+    gbs = byts / (ms / 1e3) / 1e9
+    # the oracle beside it: one full pass over the same tensors
+    res_h = [np.zeros(n, np.float32) for n in sizes]
+    c0 = time.perf_counter()
+    for t in range(len(sizes)):
+        oracle.quantize_2bit(host[t], res_h[t], -0.005, 0.005)
+    oracle_ms = (time.perf_counter() - c0) * 1e3
+    return {"workload": "compress_2bit_multi over the BERT-Base parameter list: 198 tensors, "
+                        f"{sum(sizes):,} fp32 values, thresholds +-0.005, one launch",
+            "ms_per_call": ms, "algorithmic_bytes": byts, "gbs": gbs,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "oracle_ms_per_call": oracle_ms, "oracle_cores": 1, "steps": steps}
+
+
+def bench_grandk(gcq, torch, np, si, steps: int):
+    """GlobalRandK-MN at the ResNet-50 size: shared K = 10000 indices, gather
+    for 8 workers, max-norm, quantize at s = 7, level sum and scatter into a
+    dense fp32 buffer (the dense zero fill dominates the bytes)."""
+    import oracle
+    n, K, W, s = N_C2, 10_000, W_C2, 7
+    dev = "cuda"
+    log("grandk: generating inputs")
+    host = [si.normal_f32(si.grad_seed(w, 0), n, SIGMA_C2) for w in range(W)]
+    grads = [torch.from_numpy(h).to(dev) for h in host]
+    idx = torch.empty(K, dtype=torch.int32, device=dev)
+    ws = torch.empty(gcq.grandk_ws_bytes(n, K), dtype=torch.uint8, device=dev)
+    gathered = [torch.empty(K, dtype=torch.float32, device=dev) for _ in range(W)]
+    norm = torch.empty(1, dtype=torch.float32, device=dev)
+    mws = torch.empty(gcq.qsgd_maxnorm_ws_bytes(W, K), dtype=torch.uint8, device=dev)
+    levels = [torch.empty(K, dtype=torch.int8, device=dev) for _ in range(W)]
+    sums = torch.empty(K, dtype=torch.int32, device=dev)
+    dense = torch.empty(n, dtype=torch.float32, device=dev)
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(seed, ev=None):
+        if ev is not None:
+            ev[0].record()
+        gcq.grandk_indices(n, K, seed, idx, ws)
+        if ev is not None:
+            ev[1].record()
+        for w in range(W):
+            gcq.gather_f32(grads[w], idx, gathered[w])
+        gcq.qsgd_global_maxnorm(gathered, norm, mws)
+        for w in range(W):
+            gcq.qsgd_maxnorm_quantize(gathered[w], norm, s, seed, w, levels[w])
+        if ev is not None:
+            ev[2].record()
+        gcq.qsgd_dequant_sum(levels, norm, s, dense, sums=sums, scatter_idx=idx, dense_n=n)
+        if ev is not None:
+            ev[3].record()
+
+    for k in range(3):
+        step(k)
+    torch.cuda.synchronize()
+    # eager pass with events between the stages
+    evs = [[mk() for _ in range(4)] for _ in range(steps)]
+    for k in range(steps):
+        step(k, evs[k])
+    torch.cuda.synchronize()
+    mean = lambda v: sum(v) / len(v)  # noqa: E731
+    eager = mean([e[0].elapsed_time(e[3]) for e in evs])
+    draw = mean([e[0].elapsed_time(e[1]) for e in evs])
+    mid = mean([e[1].elapsed_time(e[2]) for e in evs])
+    fill = mean([e[2].elapsed_time(e[3]) for e in evs])
+    # the step's 20 small launches captured once as a HIP graph and replayed
+    graph = graph_of(torch, lambda: step(0))
+    t0, t1 = mk(), mk()
+    t0.record()
+    for _ in range(steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    tot = t0.elapsed_time(t1) / steps
+    del graph, grads, dense
+    torch.cuda.empty_cache()
+    c0 = time.perf_counter()
+    idx_h = oracle.randk_indices(n, K, 0)
+    gk = [oracle.gather(h, idx_h) for h in host]
+    nrm = oracle.maxnorm(gk)
+    lv = [oracle.qsgd_quantize(gk[w], nrm, s, 0, w) for w in range(W)]
+    oracle.scatter_dense(oracle.qsgd_dequantize(oracle.level_sum(lv), nrm, s), idx_h, n)
+    oracle_ms = (time.perf_counter() - c0) * 1e3
+    dense_gbs = 4 * n / (fill / 1e3) / 1e9
+    return {"workload": f"GRandK-MN: n={n:,}, K={K}, W={W}, s={s}: shared index draw, gather, "
+                        "max-norm, quantize, level sum, scatter into a dense fp32 buffer",
+            "ms_per_step": tot, "values_per_s": K * W / (tot / 1e3),
+            "timing": "HIP graph replay of the whole step; stages from an eager pass",
+            "ms_per_step_eager": eager,
+            "stages_ms": {"index_draw": draw, "gather_norm_quantize": mid,
+                          "sum_fill_scatter": fill},
+            "roofline": {"bound": "hbm", "kernel": "fill_zero + scatter (dense output)",
+                         "achieved": round(dense_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(dense_gbs / HBM_PEAK_GBS, 4)},
+            "oracle_ms_per_step": oracle_ms, "oracle_cores": 1, "steps": steps}
 
 
 def cpu_baseline(np, si, budget_s: float):
@@ -434,6 +588,7 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "graph_ms_per_step": round(r2["graph_ms_per_step"], 5),
         "config": {
             "workload": "2-bit EF step: compress_2bit x 8 workers (25,557,032 fp32 each, "
                         "ResNet-50-sized flat gradient, thresholds +-0.01, residual carried) "
@@ -460,6 +615,9 @@ def main() -> int:
         q = bench_qsgd(gcq, torch, np, si, args.qsgd_steps)
         result["qsgd_mn_elems_per_s"] = q["elems_per_s"]
         result["qsgd_mn"] = q
+    if not args.skip_extra:
+        result["multi_tensor"] = bench_multi(gcq, torch, np, si, 20)
+        result["grandk_mn"] = bench_grandk(gcq, torch, np, si, 20)
 
     if not args.skip_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(np, si, args.cpu_seconds)

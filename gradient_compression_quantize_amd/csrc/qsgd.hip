@@ -369,6 +369,8 @@ __global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_kernel(
     }
 }
 
+constexpr int kFillUnroll = 4;
+
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__ out, size_t n,
                                                              int vec)
 {
@@ -378,8 +380,16 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
         const size_t nfull = n >> 2;
         f32x4* o4 = reinterpret_cast<f32x4*>(out);
         const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (size_t q = tid; q < nfull; q += stride)
-            __builtin_nontemporal_store(z, o4 + q);
+        // blocks of kFillUnroll * kThreads float4, lane-contiguous
+        const size_t per = size_t(kFillUnroll) * kThreads;
+        for (size_t b = size_t(blockIdx.x) * per; b < nfull; b += size_t(gridDim.x) * per) {
+#pragma unroll
+            for (int u = 0; u < kFillUnroll; ++u) {
+                const size_t q = b + size_t(u) * kThreads + threadIdx.x;
+                if (q < nfull)
+                    __builtin_nontemporal_store(z, o4 + q);
+            }
+        }
         for (size_t i = nfull * 4 + tid; i < n; i += stride)
             out[i] = 0.0f;
     } else {
@@ -416,6 +426,8 @@ __global__ __launch_bounds__(kThreads) void qsgd_dequant_scatter_kernel(
 // Following that rule from (p, T) = (j[t], t) down to a position nobody
 // targeted gives the index of step t, for every t in parallel. Draws are
 // hashed by target position (chained buckets) to find "the last t' < T".
+// One workgroup does it all: in LDS for K <= kRandKLdsMax (each chain step
+// is an LDS access, not a round trip to L2), in the caller's workspace above.
 constexpr int kRandKThreads = 1024;
 
 __device__ __forceinline__ uint32_t slot_of(uint32_t p, int hbits)
@@ -463,6 +475,54 @@ __global__ __launch_bounds__(kRandKThreads) void grandk_indices_kernel(
         }
         idx[t] = p;
     }
+}
+
+// K up to kRandKLdsMax: the whole structure lives in LDS (128 KB): targets,
+// 16-bit chain links, and at most 2^13 bucket heads (load factor <= 2).
+constexpr uint32_t kRandKLdsMax = 16384;
+constexpr int kRandKLdsHeadBits = 13;
+
+__global__ __launch_bounds__(kRandKThreads) void grandk_indices_lds_kernel(
+    size_t n, uint32_t K, uint32_t k0, uint32_t k1, uint32_t* __restrict__ idx, int hbits)
+{
+    __shared__ uint32_t target[kRandKLdsMax];
+    __shared__ int16_t next[kRandKLdsMax];
+    __shared__ int32_t heads[1 << kRandKLdsHeadBits];
+    const uint32_t nheads = 1u << hbits;
+    for (uint32_t t = threadIdx.x; t < K; t += kRandKThreads) {
+        const U4 r = philox4x32_10(U4{t, 0u, 0u, 1u}, k0, k1);
+        const uint64_t R = (uint64_t(r.y) << 32) | r.x;
+        target[t] = t + uint32_t(__umul64hi(R, uint64_t(n) - t));
+    }
+    for (uint32_t h = threadIdx.x; h < nheads; h += kRandKThreads)
+        heads[h] = -1;
+    __syncthreads();
+    for (uint32_t t = threadIdx.x; t < K; t += kRandKThreads)
+        next[t] = int16_t(atomicExch(&heads[slot_of(target[t], hbits)], int32_t(t)));
+    __syncthreads();
+    for (uint32_t t = threadIdx.x; t < K; t += kRandKThreads) {
+        uint32_t p = target[t];
+        int32_t T = int32_t(t);
+        for (;;) {
+            int32_t best = -1;
+            for (int32_t e = heads[slot_of(p, hbits)]; e >= 0; e = next[e])
+                if (target[e] == p && e < T && e > best)
+                    best = e;
+            if (best < 0)
+                break;
+            p = uint32_t(best);
+            T = best;
+        }
+        idx[t] = p;
+    }
+}
+
+int randk_lds_hash_bits(uint32_t K)
+{
+    int b = 6;
+    while (b < kRandKLdsHeadBits && (uint64_t(1) << b) < uint64_t(K))
+        ++b;
+    return b;
 }
 
 int randk_hash_bits(uint32_t K)
@@ -617,8 +677,8 @@ GCQ_API int qsgd_dequant_sum(const int8_t* const* levels, int W, size_t n, const
         return check_launch("qsgd_dequant_sum");
     }
     if (dense_n > 0) {
-        hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(ceil_div(dense_n, 4))), dim3(kThreads),
-                           0, stream, out, dense_n, aligned16(out) ? 1 : 0);
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(ceil_div(dense_n, 4 * kFillUnroll))),
+                           dim3(kThreads), 0, stream, out, dense_n, aligned16(out) ? 1 : 0);
         if (int rc = check_launch("qsgd_dequant_sum (fill)"))
             return rc;
     }
@@ -650,6 +710,11 @@ GCQ_API int grandk_indices(size_t n, uint32_t K, uint64_t seed, uint32_t* idx, v
         return fail(GC_EINVAL, "grandk_indices: idx is NULL or misaligned");
     if (K == 0)
         return GC_OK;
+    if (K <= kRandKLdsMax) {
+        hipLaunchKernelGGL(grandk_indices_lds_kernel, dim3(1), dim3(kRandKThreads), 0, stream, n,
+                           K, uint32_t(seed), uint32_t(seed >> 32), idx, randk_lds_hash_bits(K));
+        return check_launch("grandk_indices");
+    }
     const int hbits = randk_hash_bits(K);
     int32_t* heads = static_cast<int32_t*>(ws);
     uint32_t* target = reinterpret_cast<uint32_t*>(heads + (size_t(1) << hbits));

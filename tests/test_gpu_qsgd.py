@@ -132,7 +132,8 @@ def test_qsgd_vgg16_full_size_sampled(gcq):
 
 
 @pytest.mark.parametrize("n,K", [(1, 1), (1, 0), (7, 7), (1000, 1000), (100_000, 10_000),
-                                 (1 << 20, 1), (3, 2)])
+                                 (1 << 20, 1), (3, 2), (16384, 16384), (40_000, 16_385),
+                                 (1 << 20, 20_000), (1 << 20, 100_000)])
 def test_grandk_indices(gcq, n, K):
     for seed in (0, 1, 0xDEADBEEFCAFE):
         announce(f"grandk_indices n={n} K={K} seed={seed}")
@@ -242,3 +243,55 @@ def test_qsgd_extreme_norms(gcq, norm_scale):
     norm_or = oracle.maxnorm([g])
     assert norm.view(np.uint32) == norm_or.view(np.uint32)
     np.testing.assert_array_equal(levels[0], oracle.qsgd_quantize(g, norm_or, 127, 3, 0))
+
+
+def test_grandk_step_in_hip_graph(gcq):
+    """The whole GRandK-MN step captured once as a HIP graph and replayed
+    several times, with eager work and synchronisation between replays:
+    every replay must reproduce the eager result bit for bit."""
+    n, K, W, s, seed = 300_007, 2_000, 4, 7, 5
+    announce("grandk step captured in a HIP graph")
+    grads = [gu.dev(si.normal_f32(si.grad_seed(w, 2), n, 0.01)) for w in range(W)]
+    idx = gu.empty(K, torch.int32)
+    ws = torch.empty(gcq.grandk_ws_bytes(n, K), dtype=torch.uint8, device=gu.DEV)
+    gathered = [gu.empty(K, torch.float32) for _ in range(W)]
+    norm = torch.empty(1, dtype=torch.float32, device=gu.DEV)
+    mws = torch.empty(gcq.qsgd_maxnorm_ws_bytes(W, K), dtype=torch.uint8, device=gu.DEV)
+    levels = [gu.empty(K, torch.int8) for _ in range(W)]
+    sums = gu.empty(K, torch.int32)
+    dense = gu.empty(n, torch.float32)
+
+    def step():
+        gcq.grandk_indices(n, K, seed, idx, ws)
+        for w in range(W):
+            gcq.gather_f32(grads[w], idx, gathered[w])
+        gcq.qsgd_global_maxnorm(gathered, norm, mws)
+        for w in range(W):
+            gcq.qsgd_maxnorm_quantize(gathered[w], norm, s, seed, w, levels[w])
+        gcq.qsgd_dequant_sum(levels, norm, s, dense, sums=sums, scatter_idx=idx, dense_n=n)
+
+    step()
+    gu.sync()
+    eager = (gu.host(idx).copy(), gu.host(sums).copy(), gu.host(dense).copy())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    gu.sync()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        dense.fill_(float("nan"))
+        sums.fill_(-1)
+        idx.fill_(-1)
+        gu.sync()
+        graph.replay()
+        gu.sync()
+        got = (gu.host(idx), gu.host(sums), gu.host(dense))
+        for a, b in zip(got, eager):
+            np.testing.assert_array_equal(a, b, err_msg=f"replay {rep}")
+        # eager work in between
+        step()
+        gu.sync()
