@@ -231,3 +231,28 @@ def test_sum_order_is_worker_order():
     exact = np.sum([d.astype(np.float64) for d in deqs], axis=0)
     mag = np.sum([np.abs(d.astype(np.float64)) for d in deqs], axis=0)
     assert np.all(np.abs(got - exact) <= (W - 1) * 2.0 ** -24 * mag)
+
+
+# ------------------------------------------------------ randomised ----
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=60, deadline=None, derandomize=True, database=None)
+@given(n=st.integers(0, 3000), neg=st.floats(1e-6, 100.0), pos=st.floats(1e-6, 100.0),
+       sigma=st.floats(1e-6, 100.0), seed=st.integers(0, 2 ** 32 - 1))
+def test_residual_invariants_random_asymmetric(n, neg, pos, sigma, seed):
+    g = si.normal_f32(seed, n, sigma)
+    r0 = si.normal_f32(seed ^ 0x5A5A, n, sigma)
+    r = r0.copy()
+    v = (g + r0).astype(np.float32)
+    neg32, pos32 = np.float32(-neg), np.float32(pos)
+    compr = oracle.quantize_2bit(g, r, neg32, pos32)
+    assert compr.size == 3 + (n + 15) // 16
+    d = oracle.dequantize_2bit(compr, n)
+    up, dn = v >= pos32, v <= neg32
+    np.testing.assert_array_equal(d, np.where(up, pos32, np.where(dn, neg32, np.float32(0))))
+    np.testing.assert_array_equal(r[~up & ~dn].view(np.uint32), v[~up & ~dn].view(np.uint32))
+    assert np.all(r[up] >= 0) and np.all(r[dn] <= 0)
+    err = np.abs(d.astype(np.float64) + r.astype(np.float64) - v.astype(np.float64))
+    assert np.all(err <= 0.5 * ulp32(r))

@@ -265,3 +265,39 @@ def test_gather_scatter_match_numpy():
     expect = np.zeros(1000, np.float32)
     expect[idx] = x[:100]
     np.testing.assert_array_equal(dense, expect)
+
+
+# ------------------------------------------------------ randomised ----
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=60, deadline=None, derandomize=True, database=None)
+@given(n=st.integers(1, 50_000), frac=st.floats(0.0, 1.0), seed=st.integers(0, 2 ** 64 - 1))
+def test_randk_random_shapes(n, frac, seed):
+    K = int(frac * n)
+    idx = oracle.randk_indices(n, K, seed)
+    assert idx.size == K and len(np.unique(idx)) == K
+    assert K == 0 or int(idx.max()) < n
+    if K > 1:
+        np.testing.assert_array_equal(oracle.randk_indices(n, K // 2, seed), idx[:K // 2])
+
+
+@settings(max_examples=60, deadline=None, derandomize=True, database=None)
+@given(n=st.integers(1, 5000), s=st.integers(1, 127), scale=st.floats(1e-30, 1e30),
+       seed=st.integers(0, 2 ** 64 - 1), worker=st.integers(0, 2 ** 32 - 1))
+def test_levels_bracket_random(n, s, scale, seed, worker):
+    g = (si.normal_f32(seed % (2 ** 32), n, 1.0) * np.float32(scale)).astype(np.float32)
+    g = g[np.isfinite(g)]
+    if g.size == 0:
+        return
+    norm = oracle.maxnorm([g])
+    q = oracle.qsgd_quantize(g, norm, s, seed, worker).astype(np.int64)
+    if norm == 0:
+        assert np.all(q == 0)
+        return
+    x = (np.abs(g) / norm).astype(np.float32) * np.float32(s)
+    lo = np.floor(x.astype(np.float64))
+    m = np.abs(q)
+    assert np.all((m == lo) | (m == lo + 1)) and np.all(m <= s)
+    assert np.all(np.sign(q)[m > 0] == np.sign(g)[m > 0])
