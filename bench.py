@@ -46,6 +46,7 @@ SIGMA_C3 = 0.02
 
 PROFILE_TRAFFIC = ROOT / "profiles" / "hbm_traffic_resnet50_vgg16.md"
 PROFILE_STATS = ROOT / "profiles" / "kernel_stats_resnet50_vgg16.md"
+PROFILE_STATS_EXTRA = ROOT / "profiles" / "kernel_stats_bert_multitensor_grandk.md"
 KERNEL_SOURCES = [ROOT / "gradient_compression_quantize_amd" / "csrc" / f
                   for f in ("gcq_internal.h", "twobit.hip", "qsgd.hip")]
 
@@ -54,11 +55,19 @@ KERNEL_SOURCES = [ROOT / "gradient_compression_quantize_amd" / "csrc" / f
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats -T -d gpurun_out/prof_bench -o bench "
              "--output-format csv -- python3 -u bench.py --steps 20 --warmup 5 --qsgd-steps 5 "
-             "--skip-cpu-baseline",
+             "--skip-cpu-baseline --skip-extra",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_fetch -o fetch --output-format csv "
-             "-- python3 -u bench.py --steps 3 --warmup 1 --qsgd-steps 1 --skip-cpu-baseline",
+             "-- python3 -u bench.py --steps 3 --warmup 1 --qsgd-steps 1 --skip-cpu-baseline "
+             "--skip-extra",
     "write": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_write -o write --output-format csv "
-             "-- python3 -u bench.py --steps 3 --warmup 1 --qsgd-steps 1 --skip-cpu-baseline",
+             "-- python3 -u bench.py --steps 3 --warmup 1 --qsgd-steps 1 --skip-cpu-baseline "
+             "--skip-extra",
+    "trace_extra": "rocprofv3 --kernel-trace --stats -T -d gpurun_out/prof_extra -o extra "
+                   "--output-format csv -- python3 -u bench.py --extras-only",
+    "fetch_extra": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_fetch_extra -o fetch "
+                   "--output-format csv -- python3 -u bench.py --extras-only --extra-steps 3",
+    "write_extra": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_write_extra -o write "
+                   "--output-format csv -- python3 -u bench.py --extras-only --extra-steps 3",
     "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_cal_fetch -o cal "
                  "--output-format csv -- python3 -u bench.py --calibrate-copy",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_cal_write -o cal "
@@ -92,6 +101,9 @@ def parse_args():
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-extra", action="store_true",
                     help="skip the many-tensor and GlobalRandK measurements")
+    ap.add_argument("--extras-only", action="store_true",
+                    help="only the many-tensor and GlobalRandK measurements (profiling)")
+    ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -152,17 +164,26 @@ def summarize_profiles(out_dir: str) -> None:
     w_scale = copy_bytes / (w_kib * 1024)
     fetch = _read_counters(next((d / "pmc_fetch").glob("*counter_collection.csv")))
     write = _read_counters(next((d / "pmc_write").glob("*counter_collection.csv")))
+    sizes = [int(v) for v in __import__("synthetic_inputs").bert_base_sizes()]
+    if (d / "pmc_fetch_extra").exists() and (d / "pmc_write_extra").exists():
+        fx = _read_counters(next((d / "pmc_fetch_extra").glob("*counter_collection.csv")))
+        wx = _read_counters(next((d / "pmc_write_extra").glob("*counter_collection.csv")))
+        for k in ("compress_2bit_multi_kernel",):
+            if k in fx and k in wx:
+                fetch[k], write[k] = fx[k], wx[k]
+                algo[k] = (8 * sum(sizes), multi_bytes(sizes) - 8 * sum(sizes))
     lines = [
         "# HBM traffic per launch from rocprofv3 counters",
         "",
         "Workloads: the 2-bit step on the ResNet-50-sized flat gradient "
-        f"({n2:,} fp32 values, {W2} workers, thresholds +-0.01) and the QSGD-MN step on the "
-        f"VGG16-sized gradient ({n3:,} fp32 values, {W3} workers, s = 127).",
+        f"({n2:,} fp32 values, {W2} workers, thresholds +-0.01), the QSGD-MN step on the "
+        f"VGG16-sized gradient ({n3:,} fp32 values, {W3} workers, s = 127), and the "
+        f"many-tensor compress over the BERT-Base list (198 tensors, {sum(sizes):,} values).",
         "",
         "Commands (repo root, one counter per run):",
         "",
-        *[f"    {PROFILE_COMMANDS[k]}" for k in ("fetch", "write", "cal_fetch", "cal_write",
-                                                 "summary")],
+        *[f"    {PROFILE_COMMANDS[k]}" for k in ("fetch", "write", "fetch_extra", "write_extra",
+                                                 "cal_fetch", "cal_write", "summary")],
         "",
         "Calibration: a plain device copy of 1 GiB (`bench.py --calibrate-copy`, "
         f"kernel `{copy_name}`) reads and writes {copy_bytes:,} bytes. Its counters read "
@@ -200,8 +221,9 @@ def summarize_profiles(out_dir: str) -> None:
         f"    {PROFILE_COMMANDS['trace']}",
         f"    {PROFILE_COMMANDS['summary']}",
         "",
-        "The 2-bit step (8 x compress_2bit + decompress_2bit_sum W=8) runs 5 warm-up, 20 timed "
-        "and 20 kernel-timing steps; the QSGD-MN step runs 2 warm-up and 5 timed steps.",
+        "The 2-bit step (8 x compress_2bit + decompress_2bit_sum W=8) runs 5 warm-up, 20 timed, "
+        "20 kernel-timing and 20 graph-replayed steps; the QSGD-MN step runs 2 warm-up and 5 "
+        "timed steps.",
         "",
         "| kernel | calls | average us | min us | max us | share of GPU time |",
         "|---|---|---|---|---|---|",
@@ -219,7 +241,40 @@ def summarize_profiles(out_dir: str) -> None:
                   f"{HBM_PEAK_GBS:,.0f} GB/s."]
     lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
     PROFILE_STATS.write_text("\n".join(lines))
-    print(f"wrote {PROFILE_TRAFFIC} and {PROFILE_STATS}")
+    wrote = [PROFILE_TRAFFIC, PROFILE_STATS]
+    extra = list((d / "prof_extra").glob("*kernel_stats.csv")) if (d / "prof_extra").exists() else []
+    if extra:
+        stats = list(csv.DictReader(open(extra[0])))
+        lines = [
+            "# Kernel durations from rocprofv3: many-tensor compress and GlobalRandK",
+            "",
+            "Command (repo root):",
+            "",
+            f"    {PROFILE_COMMANDS['trace_extra']}",
+            f"    {PROFILE_COMMANDS['summary']}",
+            "",
+            f"Many-tensor: compress_2bit_multi over the BERT-Base list (198 tensors, "
+            f"{sum(sizes):,} values, {multi_bytes(sizes):,} algorithmic bytes per call). "
+            "GlobalRandK-MN: n = 25,557,032, K = 10000, W = 8, s = 7; eager steps, then graph "
+            "replays of the whole step.",
+            "",
+            "| kernel | calls | average us | min us | max us | share of GPU time |",
+            "|---|---|---|---|---|---|",
+        ]
+        for r in stats:
+            lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                         f"{float(r['Percentage']):.2f}% |")
+        m = next((r for r in stats if r["Name"] == "compress_2bit_multi_kernel"), None)
+        if m:
+            us = float(m["AverageNs"]) / 1e3
+            gbs = multi_bytes(sizes) / (us * 1e-6) / 1e9
+            lines += ["", f"compress_2bit_multi: {us:.2f} us per call = {gbs:,.0f} GB/s = "
+                      f"{100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:,.0f} GB/s."]
+        lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
+        PROFILE_STATS_EXTRA.write_text("\n".join(lines))
+        wrote.append(PROFILE_STATS_EXTRA)
+    print("wrote " + ", ".join(str(w) for w in wrote))
 
 
 def cpu_model() -> str:
@@ -564,6 +619,11 @@ def main() -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     gcq.load()
+    if args.extras_only:
+        print(json.dumps({"multi_tensor": bench_multi(gcq, torch, np, si, args.extra_steps),
+                          "grandk_mn": bench_grandk(gcq, torch, np, si, args.extra_steps)}),
+              flush=True)
+        return 0
 
     r2 = bench_2bit(gcq, torch, np, si, args.steps, args.warmup)
     step_bytes = W_C2 * compress_bytes(N_C2) + dequant_sum_bytes(N_C2, W_C2)
@@ -616,8 +676,8 @@ def main() -> int:
         result["qsgd_mn_elems_per_s"] = q["elems_per_s"]
         result["qsgd_mn"] = q
     if not args.skip_extra:
-        result["multi_tensor"] = bench_multi(gcq, torch, np, si, 20)
-        result["grandk_mn"] = bench_grandk(gcq, torch, np, si, 20)
+        result["multi_tensor"] = bench_multi(gcq, torch, np, si, args.extra_steps)
+        result["grandk_mn"] = bench_grandk(gcq, torch, np, si, args.extra_steps)
 
     if not args.skip_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(np, si, args.cpu_seconds)
