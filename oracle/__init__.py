@@ -76,6 +76,16 @@ def _declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.oracle_dequantize_2bit_sum.argtypes = [ctypes.POINTER(_u32p), ctypes.c_int,
                                              _sz, _f32p]
     L.oracle_dequantize_2bit_sum.restype = None
+    L.oracle_compressed_ternary_words.argtypes = [_sz]
+    L.oracle_compressed_ternary_words.restype = _sz
+    L.oracle_quantize_ternary.argtypes = [_f32p, _f32p, _sz, ctypes.c_float,
+                                          ctypes.c_float, _u32p]
+    L.oracle_quantize_ternary.restype = None
+    L.oracle_dequantize_ternary.argtypes = [_u32p, _sz, _f32p]
+    L.oracle_dequantize_ternary.restype = None
+    L.oracle_dequantize_ternary_sum.argtypes = [ctypes.POINTER(_u32p), ctypes.c_int,
+                                                _sz, _f32p]
+    L.oracle_dequantize_ternary_sum.restype = None
     L.oracle_philox4x32_10.argtypes = [_u32p, _u32p, _u32p]
     L.oracle_philox4x32_10.restype = None
     L.oracle_uniform24.argtypes = [ctypes.c_uint32]
@@ -157,6 +167,44 @@ def dequantize_2bit_sum(comprs, n: int) -> np.ndarray:
     arr = (_u32p * W)(*[_ptr(c, ctypes.c_uint32) for c in comprs])
     out = np.empty(n, dtype=np.float32)
     lib().oracle_dequantize_2bit_sum(arr, W, n, _ptr(out, ctypes.c_float))
+    return out
+
+
+# -------------------------------------------------------------- ternary ----
+
+def compressed_ternary_words(n: int) -> int:
+    return int(lib().oracle_compressed_ternary_words(n))
+
+
+def quantize_ternary(grad: np.ndarray, residual: np.ndarray, neg_threshold: float,
+                     pos_threshold: float) -> np.ndarray:
+    grad = _as(grad, np.float32)
+    if residual.dtype != np.float32 or not residual.flags["C_CONTIGUOUS"]:
+        raise TypeError("residual must be a contiguous float32 array")
+    n = grad.size
+    assert residual.size == n
+    compr = np.empty(compressed_ternary_words(n), dtype=np.uint32)
+    lib().oracle_quantize_ternary(_ptr(grad, ctypes.c_float), _ptr(residual, ctypes.c_float),
+                                  n, float(neg_threshold), float(pos_threshold),
+                                  _ptr(compr, ctypes.c_uint32))
+    return compr
+
+
+def dequantize_ternary(compr: np.ndarray, n: int) -> np.ndarray:
+    compr = _as(compr, np.uint32)
+    assert compr.size == compressed_ternary_words(n)
+    out = np.empty(n, dtype=np.float32)
+    lib().oracle_dequantize_ternary(_ptr(compr, ctypes.c_uint32), n, _ptr(out, ctypes.c_float))
+    return out
+
+
+def dequantize_ternary_sum(comprs, n: int) -> np.ndarray:
+    comprs = [_as(c, np.uint32) for c in comprs]
+    for c in comprs:
+        assert c.size == compressed_ternary_words(n)
+    arr = (_u32p * len(comprs))(*[_ptr(c, ctypes.c_uint32) for c in comprs])
+    out = np.empty(n, dtype=np.float32)
+    lib().oracle_dequantize_ternary_sum(arr, len(comprs), n, _ptr(out, ctypes.c_float))
     return out
 
 

@@ -131,6 +131,83 @@ void oracle_dequantize_2bit_sum(const uint32_t* const* compr, int W, size_t n,
 }
 
 /* ======================================================================
+ * Dense ternary packing: the optimization [MX] "Two bit quantization"
+ * defers. Three codes need log2(3) ~ 1.58 bits, and five codes fit one byte
+ * (3^5 = 243 <= 256), so the block shrinks from 2 to 1.6 bits per value.
+ * READING: the header is the 2-bit block's; then a byte array in memory
+ * order, byte j holding values 5j .. 5j+4 as base-3 digits, the first value
+ * most significant (byte = c0*81 + c1*27 + c2*9 + c3*3 + c4); digits are the
+ * 2-bit codes (0 zero, 1 pos, 2 neg); tail digits 0; the byte array is
+ * padded with zero bytes to whole 32-bit elements. A byte above 242 (never
+ * written) decodes digit by digit like any other, and a leading digit of 3
+ * is an unused code, so it dequantizes to 0.
+ * ==================================================================== */
+
+static const unsigned pow3[5] = {1u, 3u, 9u, 27u, 81u};
+
+size_t oracle_compressed_ternary_words(size_t n)
+{
+    size_t nbytes = (n + 4) / 5;
+    return 3 + (nbytes + 3) / 4;
+}
+
+/* The same error-feedback arithmetic as oracle_quantize_2bit; only the
+ * packing of the codes differs. */
+void oracle_quantize_ternary(const float* grad, float* residual, size_t n,
+                             float neg_threshold, float pos_threshold,
+                             uint32_t* compr)
+{
+    size_t words = oracle_compressed_ternary_words(n);
+    compr[0] = bits_of(neg_threshold);
+    compr[1] = bits_of(pos_threshold);
+    compr[2] = bits_of((float)n);
+    for (size_t j = 3; j < words; ++j)
+        compr[j] = 0u;
+    unsigned char* bytes = (unsigned char*)(compr + 3);
+    for (size_t i = 0; i < n; ++i) {
+        float v = grad[i] + residual[i];
+        uint32_t c = code_of(v, neg_threshold, pos_threshold);
+        float d = value_of(c, neg_threshold, pos_threshold);
+        residual[i] = v - d;
+        bytes[i / 5] = (unsigned char)(bytes[i / 5] + c * pow3[4 - i % 5]);
+    }
+}
+
+static uint32_t ternary_digit_at(const uint32_t* compr, size_t i)
+{
+    const unsigned char* bytes = (const unsigned char*)(compr + 3);
+    unsigned b = bytes[i / 5];
+    unsigned k = 4u - (unsigned)(i % 5);
+    unsigned d = b / pow3[k];
+    return k == 4u ? d : d % 3u; /* the leading digit is not reduced */
+}
+
+void oracle_dequantize_ternary(const uint32_t* compr, size_t n, float* out)
+{
+    float neg = float_of(compr[0]);
+    float pos = float_of(compr[1]);
+    for (size_t i = 0; i < n; ++i)
+        out[i] = value_of(ternary_digit_at(compr, i), neg, pos);
+}
+
+void oracle_dequantize_ternary_sum(const uint32_t* const* compr, int W,
+                                   size_t n, float* out)
+{
+    for (size_t i = 0; i < n; ++i) {
+        const uint32_t* b0 = compr[0];
+        float acc = value_of(ternary_digit_at(b0, i), float_of(b0[0]),
+                             float_of(b0[1]));
+        for (int w = 1; w < W; ++w) {
+            const uint32_t* b = compr[w];
+            float d = value_of(ternary_digit_at(b, i), float_of(b[0]),
+                               float_of(b[1]));
+            acc = acc + d;
+        }
+        out[i] = acc;
+    }
+}
+
+/* ======================================================================
  * Philox-4x32-10 [PHX]: a 4x32-bit counter and a 2x32-bit key.
  * One round: two 32x32->64 products of counter words 0 and 2 with the two
  * Philox-4x32 multipliers; the new words are (hi of the second product XOR

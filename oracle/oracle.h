@@ -39,6 +39,15 @@ void oracle_dequantize_2bit(const uint32_t* compr, size_t n, float* out);
 void oracle_dequantize_2bit_sum(const uint32_t* const* compr, int W, size_t n,
                                 float* out);
 
+/* ---- dense ternary packing of the same codes (5 per byte) [MX] ---- */
+size_t oracle_compressed_ternary_words(size_t n);
+void oracle_quantize_ternary(const float* grad, float* residual, size_t n,
+                             float neg_threshold, float pos_threshold,
+                             uint32_t* compr);
+void oracle_dequantize_ternary(const uint32_t* compr, size_t n, float* out);
+void oracle_dequantize_ternary_sum(const uint32_t* const* compr, int W,
+                                   size_t n, float* out);
+
 /* ---- Philox-4x32-10 [PHX] ---- */
 void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2],
                           uint32_t out[4]);

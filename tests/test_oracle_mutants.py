@@ -21,6 +21,7 @@ from oracle import CFLAGS  # noqa: E402
 T2 = "tests/test_oracle_2bit.py"
 TP = "tests/test_oracle_philox.py"
 TQ = "tests/test_oracle_qsgd.py"
+TT = "tests/test_oracle_ternary.py"
 
 MUTANTS = [
     # 2-bit quantizer
@@ -28,16 +29,28 @@ MUTANTS = [
     ("strict_neg", "if (v <= neg_threshold)", "if (v < neg_threshold)", T2),
     ("lsb_first", "unsigned shift = 30u - 2u * (unsigned)(i % 16);\n        compr",
      "unsigned shift = 2u * (unsigned)(i % 16);\n        compr", T2),
-    ("drop_residual_in", "float v = grad[i] + residual[i];", "float v = grad[i];", T2),
-    ("residual_sign", "residual[i] = v - d;", "residual[i] = v + d;", T2),
-    ("residual_not_reduced", "residual[i] = v - d;", "residual[i] = v;", T2),
-    ("header_swapped", "compr[0] = bits_of(neg_threshold);\n    compr[1] = bits_of(pos_threshold);",
-     "compr[0] = bits_of(pos_threshold);\n    compr[1] = bits_of(neg_threshold);", T2),
+    ("drop_residual_in", "float v = grad[i] + residual[i];\n        uint32_t c = code_of(v, neg_threshold, pos_threshold);\n        float d = value_of(c, neg_threshold, pos_threshold);\n        residual[i] = v - d;\n        unsigned shift",
+     "float v = grad[i];\n        uint32_t c = code_of(v, neg_threshold, pos_threshold);\n        float d = value_of(c, neg_threshold, pos_threshold);\n        residual[i] = v - d;\n        unsigned shift", T2),
+    ("residual_sign", "residual[i] = v - d;\n        unsigned shift", "residual[i] = v + d;\n        unsigned shift", T2),
+    ("residual_not_reduced", "residual[i] = v - d;\n        unsigned shift", "residual[i] = v;\n        unsigned shift", T2),
+    ("header_swapped", "compr[0] = bits_of(neg_threshold);\n    compr[1] = bits_of(pos_threshold);\n    compr[2] = bits_of((float)n);\n    for (size_t j = 0;",
+     "compr[0] = bits_of(pos_threshold);\n    compr[1] = bits_of(neg_threshold);\n    compr[2] = bits_of((float)n);\n    for (size_t j = 0;", T2),
     ("deq_wrong_sign", "    if (code == 2u)\n        return neg_threshold;",
      "    if (code == 2u)\n        return -neg_threshold;", T2),
-    ("sum_drops_worker0", "for (int w = 1; w < W; ++w) {\n            const uint32_t* b = compr[w];",
-     "acc = 0.0f;\n        for (int w = 1; w < W; ++w) {\n            const uint32_t* b = compr[w];", T2),
+    ("sum_drops_worker0", "for (int w = 1; w < W; ++w) {\n            const uint32_t* b = compr[w];\n            float d = value_of(code_at(",
+     "acc = 0.0f;\n        for (int w = 1; w < W; ++w) {\n            const uint32_t* b = compr[w];\n            float d = value_of(code_at(", T2),
     ("word_index", "compr[3 + i / 16] |= c << shift;", "compr[2 + i / 16] |= c << shift;", T2),
+    # ternary packing
+    ("ternary_lsb_first", "bytes[i / 5] = (unsigned char)(bytes[i / 5] + c * pow3[4 - i % 5]);",
+     "bytes[i / 5] = (unsigned char)(bytes[i / 5] + c * pow3[i % 5]);", TT),
+    ("ternary_decode_order", "unsigned k = 4u - (unsigned)(i % 5);", "unsigned k = (unsigned)(i % 5);", TT),
+    ("ternary_digits_unreduced", "return k == 4u ? d : d % 3u;", "return d;", TT),
+    ("ternary_no_residual", "        residual[i] = v - d;\n        bytes[i / 5]",
+     "        residual[i] = v;\n        bytes[i / 5]", TT),
+    ("ternary_header_swapped", "compr[0] = bits_of(neg_threshold);\n    compr[1] = bits_of(pos_threshold);\n    compr[2] = bits_of((float)n);\n    for (size_t j = 3;",
+     "compr[0] = bits_of(pos_threshold);\n    compr[1] = bits_of(neg_threshold);\n    compr[2] = bits_of((float)n);\n    for (size_t j = 3;", TT),
+    ("ternary_sum_drops_worker0", "for (int w = 1; w < W; ++w) {\n            const uint32_t* b = compr[w];\n            float d = value_of(ternary_digit_at(",
+     "acc = 0.0f;\n        for (int w = 1; w < W; ++w) {\n            const uint32_t* b = compr[w];\n            float d = value_of(ternary_digit_at(", TT),
     # Philox
     ("philox_mult_swap", "uint64_t prod_a = (uint64_t)mult_a * (uint64_t)x0;",
      "uint64_t prod_a = (uint64_t)mult_b * (uint64_t)x0;", TP),
