@@ -46,9 +46,10 @@ SIGMA_C3 = 0.02
 
 PROFILE_TRAFFIC = ROOT / "profiles" / "hbm_traffic_resnet50_vgg16.md"
 PROFILE_STATS = ROOT / "profiles" / "kernel_stats_resnet50_vgg16.md"
-PROFILE_STATS_EXTRA = ROOT / "profiles" / "kernel_stats_bert_multitensor_grandk.md"
+PROFILE_STATS_EXTRA = ROOT / "profiles" / "kernel_stats_bert_multitensor_grandk_ternary.md"
 KERNEL_SOURCES = [ROOT / "gradient_compression_quantize_amd" / "csrc" / f
-                  for f in ("gcq_internal.h", "twobit.hip", "qsgd.hip")]
+                  for f in ("gcq_internal.h", "threshold_codes.h", "twobit.hip", "ternary.hip",
+                            "qsgd.hip")]
 
 # The rocprofv3 runs the committed summaries come from (run from the repo
 # root; the output directories are scratch).
@@ -100,9 +101,9 @@ def parse_args():
     ap.add_argument("--skip-qsgd", action="store_true", help="time only the 2-bit step")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-extra", action="store_true",
-                    help="skip the many-tensor and GlobalRandK measurements")
+                    help="skip the many-tensor, GlobalRandK and ternary measurements")
     ap.add_argument("--extras-only", action="store_true",
-                    help="only the many-tensor and GlobalRandK measurements (profiling)")
+                    help="only the many-tensor, GlobalRandK and ternary measurements (profiling)")
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline sample")
@@ -168,17 +169,24 @@ def summarize_profiles(out_dir: str) -> None:
     if (d / "pmc_fetch_extra").exists() and (d / "pmc_write_extra").exists():
         fx = _read_counters(next((d / "pmc_fetch_extra").glob("*counter_collection.csv")))
         wx = _read_counters(next((d / "pmc_write_extra").glob("*counter_collection.csv")))
-        for k in ("compress_2bit_multi_kernel",):
+        tw = ternary_words(n2)
+        extra_algo = {
+            "compress_2bit_multi_kernel": (8 * sum(sizes), multi_bytes(sizes) - 8 * sum(sizes)),
+            "compress_ternary_vec_kernel": (8 * n2, 4 * n2 + 4 * tw),
+            "decompress_ternary_vec_kernel": (4 * W2 * tw, 4 * n2),
+        }
+        for k, ab in extra_algo.items():
             if k in fx and k in wx:
                 fetch[k], write[k] = fx[k], wx[k]
-                algo[k] = (8 * sum(sizes), multi_bytes(sizes) - 8 * sum(sizes))
+                algo[k] = ab
     lines = [
         "# HBM traffic per launch from rocprofv3 counters",
         "",
         "Workloads: the 2-bit step on the ResNet-50-sized flat gradient "
         f"({n2:,} fp32 values, {W2} workers, thresholds +-0.01), the QSGD-MN step on the "
-        f"VGG16-sized gradient ({n3:,} fp32 values, {W3} workers, s = 127), and the "
-        f"many-tensor compress over the BERT-Base list (198 tensors, {sum(sizes):,} values).",
+        f"VGG16-sized gradient ({n3:,} fp32 values, {W3} workers, s = 127), the "
+        f"many-tensor compress over the BERT-Base list (198 tensors, {sum(sizes):,} values), "
+        "and the 2-bit step's workload with the codes packed five per byte (ternary).",
         "",
         "Commands (repo root, one counter per run):",
         "",
@@ -205,7 +213,8 @@ def summarize_profiles(out_dir: str) -> None:
                      f"{ar + aw:,} | {hb / (ar + aw):.4f} |")
         machine.append(f"traffic_bytes_per_launch[{k}]: {int(round(hb))}")
     lines += ["", "Algorithmic bytes: compress reads grad and residual and writes residual and "
-              "the block (12 n + 4 (3 + ceil(n/16))); dequantize-sum reads W blocks and writes "
+              "the block (12 n + 4 (3 + ceil(n/16)), or 4 (3 + ceil(n/20)) for the ternary "
+              "block); dequantize-sum reads W blocks and writes "
               "n fp32; max-norm reads W n fp32; quantize reads n fp32 and writes n int8; the "
               "level sum reads W n int8 and writes n int32 + n fp32.", "",
               "Machine-readable (bench.py reads these while the kernel sources are unchanged):",
@@ -246,7 +255,7 @@ def summarize_profiles(out_dir: str) -> None:
     if extra:
         stats = list(csv.DictReader(open(extra[0])))
         lines = [
-            "# Kernel durations from rocprofv3: many-tensor compress and GlobalRandK",
+            "# Kernel durations from rocprofv3: many-tensor compress, GlobalRandK, ternary",
             "",
             "Command (repo root):",
             "",
@@ -256,7 +265,9 @@ def summarize_profiles(out_dir: str) -> None:
             f"Many-tensor: compress_2bit_multi over the BERT-Base list (198 tensors, "
             f"{sum(sizes):,} values, {multi_bytes(sizes):,} algorithmic bytes per call). "
             "GlobalRandK-MN: n = 25,557,032, K = 10000, W = 8, s = 7; eager steps, then graph "
-            "replays of the whole step.",
+            "replays of the whole step. Ternary: the 2-bit step's workload (n = 25,557,032, "
+            "W = 8, thresholds +-0.01) with compress_ternary + decompress_ternary_sum; 3 "
+            "warm-up, then timed, kernel-timing and graph-replayed steps.",
             "",
             "| kernel | calls | average us | min us | max us | share of GPU time |",
             "|---|---|---|---|---|---|",
@@ -271,6 +282,14 @@ def summarize_profiles(out_dir: str) -> None:
             gbs = multi_bytes(sizes) / (us * 1e-6) / 1e9
             lines += ["", f"compress_2bit_multi: {us:.2f} us per call = {gbs:,.0f} GB/s = "
                       f"{100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:,.0f} GB/s."]
+        t = next((r for r in stats if r["Name"] == "compress_ternary_vec_kernel"), None)
+        if t:
+            us = float(t["AverageNs"]) / 1e3
+            tb = 12 * n2 + 4 * ternary_words(n2)
+            gbs = tb / (us * 1e-6) / 1e9
+            lines += ["", f"compress_ternary at {n2:,} values: {tb:,} algorithmic bytes in "
+                      f"{us:.2f} us = {gbs:,.0f} GB/s = {100 * gbs / HBM_PEAK_GBS:.1f}% of "
+                      f"{HBM_PEAK_GBS:,.0f} GB/s."]
         lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
         PROFILE_STATS_EXTRA.write_text("\n".join(lines))
         wrote.append(PROFILE_STATS_EXTRA)
@@ -300,13 +319,22 @@ def calibrate_copy() -> None:
 
 
 def bench_2bit(gcq, torch, np, si, steps: int, warmup: int):
+    return bench_threshold_step(gcq, torch, si, steps, warmup, "2-bit",
+                                gcq.gc_compressed_2bit_words, gcq.compress_2bit,
+                                gcq.decompress_2bit_sum)
+
+
+def bench_threshold_step(gcq, torch, si, steps: int, warmup: int, tag: str, words_of,
+                         compress, dequant_sum):
+    """W = 8 compresses (residual carried) + the W-block dequantize-sum at the
+    ResNet-50 size, with one of the two packings of the threshold codes."""
     n, W = N_C2, W_C2
     dev = "cuda"
-    log(f"2-bit: generating {W} x {n} fp32 gradients")
+    log(f"{tag}: generating {W} x {n} fp32 gradients")
     grads = [torch.from_numpy(si.normal_f32(si.grad_seed(w, 0), n, SIGMA_C2)).to(dev)
              for w in range(W)]
     res = [torch.zeros(n, dtype=torch.float32, device=dev) for _ in range(W)]
-    words = gcq.gc_compressed_2bit_words(n)
+    words = words_of(n)
     comprs = [torch.empty(words, dtype=torch.int32, device=dev) for _ in range(W)]
     out = torch.empty(n, dtype=torch.float32, device=dev)
 
@@ -314,14 +342,14 @@ def bench_2bit(gcq, torch, np, si, steps: int, warmup: int):
         if ev is not None:
             ev[0].record()
         for w in range(W):
-            gcq.compress_2bit(grads[w], res[w], -THR_C2, THR_C2, comprs[w])
+            compress(grads[w], res[w], -THR_C2, THR_C2, comprs[w])
         if ev is not None:
             ev[1].record()
-        gcq.decompress_2bit_sum(comprs, n, out)
+        dequant_sum(comprs, n, out)
         if ev is not None:
             ev[2].record()
 
-    log(f"2-bit: warmup {warmup} steps")
+    log(f"{tag}: warmup {warmup} steps")
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -329,7 +357,7 @@ def bench_2bit(gcq, torch, np, si, steps: int, warmup: int):
     mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     # timed pass: K plain steps between two events
     t0, t1 = mk(), mk()
-    log(f"2-bit: timing {steps} steps")
+    log(f"{tag}: timing {steps} steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
@@ -344,7 +372,7 @@ def bench_2bit(gcq, torch, np, si, steps: int, warmup: int):
     # its group's time over 8 (events around every launch would add their own
     # packets' latency to each one)
     evs = [[mk() for _ in range(3)] for _ in range(steps)]
-    log(f"2-bit: kernel timing over {steps} more steps")
+    log(f"{tag}: kernel timing over {steps} more steps")
     for k in range(steps):
         step(evs[k])
     torch.cuda.synchronize()
@@ -437,6 +465,51 @@ def graph_of(torch, fn):
         fn()
     torch.cuda.synchronize()
     return graph
+
+
+def ternary_words(n: int) -> int:
+    return 3 + (n + 19) // 20
+
+
+def bench_ternary(gcq, torch, np, si, steps: int):
+    """The 2-bit step's workload with the codes packed five per byte:
+    compress_ternary x 8 workers + decompress_ternary_sum W = 8."""
+    import oracle
+    n, W = N_C2, W_C2
+    r = bench_threshold_step(gcq, torch, si, steps, 3, "ternary", gcq.gc_compressed_ternary_words,
+                             gcq.compress_ternary, gcq.decompress_ternary_sum)
+    comp_b = 12 * n + 4 * ternary_words(n)
+    deq_b = 4 * W * ternary_words(n) + 4 * n
+    comp_ms = sum(r["compress_ms"]) / len(r["compress_ms"])
+    deq_ms = sum(r["dequant_sum_ms"]) / len(r["dequant_sum_ms"])
+    step_b = W * comp_b + deq_b
+    comp_gbs = comp_b / (comp_ms / 1e3) / 1e9
+    # the oracle beside it: one worker's compress and the W-block sum
+    g = si.normal_f32(si.grad_seed(0, 0), n, SIGMA_C2)
+    c0 = time.perf_counter()
+    blk = oracle.quantize_ternary(g, np.zeros(n, np.float32), -THR_C2, THR_C2)
+    oracle_comp_ms = (time.perf_counter() - c0) * 1e3
+    c0 = time.perf_counter()
+    oracle.dequantize_ternary_sum([blk] * W, n)
+    oracle_deq_ms = (time.perf_counter() - c0) * 1e3
+    return {"workload": "dense ternary packing (5 codes per byte): compress_ternary x 8 workers "
+                        f"({n:,} fp32 each, thresholds +-{THR_C2}, residual carried) + "
+                        "decompress_ternary_sum W=8",
+            "ms_per_step": r["ms_per_step"], "graph_ms_per_step": r["graph_ms_per_step"],
+            "step_algorithmic_bytes": step_b,
+            "gbs": step_b / (r["ms_per_step"] / 1e3) / 1e9,
+            "compress_ternary": {"avg_ms": comp_ms, "algorithmic_bytes": comp_b,
+                                 "gbs": comp_gbs},
+            "decompress_ternary_sum": {"avg_ms": deq_ms, "algorithmic_bytes": deq_b,
+                                       "gbs": deq_b / (deq_ms / 1e3) / 1e9},
+            "roofline": {"bound": "hbm", "kernel": "compress_ternary",
+                         "achieved": round(comp_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(comp_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_from_profile("compress_ternary_vec_kernel")},
+            "wire_bytes_per_worker": 4 * ternary_words(n),
+            "wire_bytes_per_worker_2bit": 4 * (3 + (n + 15) // 16),
+            "oracle_ms": {"compress_one_worker": oracle_comp_ms, "dequant_sum_w8": oracle_deq_ms},
+            "oracle_cores": 1, "steps": steps}
 
 
 def multi_bytes(sizes) -> int:
@@ -621,7 +694,8 @@ def main() -> int:
     gcq.load()
     if args.extras_only:
         print(json.dumps({"multi_tensor": bench_multi(gcq, torch, np, si, args.extra_steps),
-                          "grandk_mn": bench_grandk(gcq, torch, np, si, args.extra_steps)}),
+                          "grandk_mn": bench_grandk(gcq, torch, np, si, args.extra_steps),
+                          "ternary": bench_ternary(gcq, torch, np, si, args.extra_steps)}),
               flush=True)
         return 0
 
@@ -678,6 +752,7 @@ def main() -> int:
     if not args.skip_extra:
         result["multi_tensor"] = bench_multi(gcq, torch, np, si, args.extra_steps)
         result["grandk_mn"] = bench_grandk(gcq, torch, np, si, args.extra_steps)
+        result["ternary"] = bench_ternary(gcq, torch, np, si, args.extra_steps)
 
     if not args.skip_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(np, si, args.cpu_seconds)

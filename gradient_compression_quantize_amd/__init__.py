@@ -9,7 +9,8 @@ There is no fallback: if ``libgcq.so`` is missing, ``load()`` raises.
 Two method families (see include/gcq.h for exact semantics):
   * 2-bit threshold quantization with residual error feedback (apache MXNet
     pull request #8342): compress_2bit, decompress_2bit, decompress_2bit_sum,
-    Plan2bitMulti / compress_2bit_multi;
+    Plan2bitMulti / compress_2bit_multi, and the same codes packed five per
+    byte: compress_ternary, decompress_ternary, decompress_ternary_sum;
   * QSGDMaxNorm stochastic quantization and GlobalRandK (vineeths96
     "Gradient-Compression"): qsgd_global_maxnorm, qsgd_maxnorm_quantize,
     qsgd_dequant_sum, grandk_indices, gather_f32.
@@ -63,6 +64,11 @@ def _declare(L):
     L.compress_2bit.argtypes = [_vp, _vp, _sz, _f, _f, _vp, _vp]
     L.decompress_2bit.argtypes = [_vp, _sz, _vp, _i, _vp]
     L.decompress_2bit_sum.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _vp]
+    L.gc_compressed_ternary_words.argtypes = [_sz]
+    L.gc_compressed_ternary_words.restype = _sz
+    L.compress_ternary.argtypes = [_vp, _vp, _sz, _f, _f, _vp, _vp]
+    L.decompress_ternary.argtypes = [_vp, _sz, _vp, _i, _vp]
+    L.decompress_ternary_sum.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _vp]
     L.gc_plan_2bit_multi_create.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                             ctypes.POINTER(_sz), _i, ctypes.POINTER(_vp)]
     L.gc_plan_compressed_words.argtypes = [_vp]
@@ -81,6 +87,7 @@ def _declare(L):
                                  ctypes.POINTER(_sz), _vp]
     L.gather_f32.argtypes = [_vp, _vp, _sz, _vp, _vp]
     for name in ("compress_2bit", "decompress_2bit", "decompress_2bit_sum",
+                 "compress_ternary", "decompress_ternary", "decompress_ternary_sum",
                  "gc_plan_2bit_multi_create", "gc_plan_block_offsets", "compress_2bit_multi",
                  "qsgd_global_maxnorm", "qsgd_maxnorm_quantize", "qsgd_dequant_sum",
                  "grandk_indices", "gather_f32"):
@@ -172,6 +179,50 @@ def decompress_2bit_sum(comprs: Sequence, n: int, out, stream=None) -> None:
     arr = _ptr_array(comprs, torch.int32, "compr")
     _check(load().decompress_2bit_sum(arr, len(comprs), n, _dev(out, torch.float32, "out"),
                                       _stream(stream)))
+
+
+# ---- the same codes, five per byte ------------------------------------------
+
+def gc_compressed_ternary_words(n: int) -> int:
+    return int(load().gc_compressed_ternary_words(n))
+
+
+compressed_ternary_words = gc_compressed_ternary_words
+
+
+def compress_ternary(grad, residual, neg_threshold: float, pos_threshold: float, compr,
+                     stream=None) -> None:
+    torch = _torch()
+    n = grad.numel()
+    if residual.numel() != n:
+        raise ValueError("compress_ternary: grad and residual differ in size")
+    if compr.numel() < gc_compressed_ternary_words(n):
+        raise ValueError("compress_ternary: compr too small")
+    _check(load().compress_ternary(_dev(grad, torch.float32, "grad"),
+                                   _dev(residual, torch.float32, "residual"), n,
+                                   float(neg_threshold), float(pos_threshold),
+                                   _dev(compr, torch.int32, "compr"), _stream(stream)))
+
+
+def decompress_ternary(compr, n: int, out, accumulate: bool = False, stream=None) -> None:
+    torch = _torch()
+    if compr.numel() < gc_compressed_ternary_words(n) or out.numel() < n:
+        raise ValueError("decompress_ternary: buffer too small")
+    _check(load().decompress_ternary(_dev(compr, torch.int32, "compr"), n,
+                                     _dev(out, torch.float32, "out"), int(bool(accumulate)),
+                                     _stream(stream)))
+
+
+def decompress_ternary_sum(comprs: Sequence, n: int, out, stream=None) -> None:
+    torch = _torch()
+    for c in comprs:
+        if c.numel() < gc_compressed_ternary_words(n):
+            raise ValueError("decompress_ternary_sum: compr too small")
+    if out.numel() < n:
+        raise ValueError("decompress_ternary_sum: out too small")
+    arr = _ptr_array(comprs, torch.int32, "compr")
+    _check(load().decompress_ternary_sum(arr, len(comprs), n, _dev(out, torch.float32, "out"),
+                                         _stream(stream)))
 
 
 class Plan2bitMulti:

@@ -11,7 +11,7 @@ CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB_PATH = PKG / "libgcq.so"
 
-SOURCES = ["status.hip", "twobit.hip", "qsgd.hip"]
+SOURCES = ["status.hip", "twobit.hip", "ternary.hip", "qsgd.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -1,0 +1,503 @@
+// ternary.hip -- dense packing of the threshold quantizer's codes: five
+// codes per byte as base-3 digits, 1.6 bits per value instead of 2.
+//
+// Method: apache/incubator-mxnet PR #8342 "[WIP] 2bit gradient compression".
+// "Two bit quantization" notes that three codes leave one of the four 2-bit
+// patterns unused and puts a denser packing off for later; this is that
+// packing, with the same thresholds, codes and error feedback ("Approach")
+// and the same 3-element header ("Format of compressed gradient"). Byte j of
+// the payload (from element 3 on, bytes in memory order) holds values
+// 5j .. 5j+4 as c0*81 + c1*27 + c2*9 + c3*3 + c4, the first value most
+// significant; zero bytes pad the payload to whole 32-bit elements, so a
+// block of n values takes 3 + ceil(n / 20) elements. Bytes 243..255 are
+// never written; decoded, their leading digit 3 reads as zero.
+//
+// Layout and mapping (HBM-bound: ~12.2 bytes moved per value to compress,
+// 4 + 0.2 W to dequantize-and-sum W blocks):
+//  - one 32-bit element holds 20 values = 5 float4 slots, so a wave tile is
+//    5 float4 slots per lane (1280 values, 64 elements): grad / residual /
+//    out move lane-contiguous, 1 KiB per instruction;
+//  - compress: each lane writes its slots' codes, one per byte, to a
+//    wave-private LDS buffer; lane L reads back the 20 codes of element L
+//    (5 consecutive dwords: distinct banks) and folds them into 4 base-3
+//    bytes with byte dot products; one coalesced 256-byte store per tile;
+//  - dequantize: lane L loads element L of each block (one 256-byte load per
+//    worker), decodes its 20 values through two LDS tables and sums them in
+//    worker order; a wave-private LDS transpose turns each lane's 20
+//    consecutive values into lane-contiguous float4 stores.
+#include "gcq_internal.h"
+#include "threshold_codes.h"
+
+#include <algorithm>
+
+namespace gcq {
+namespace {
+
+constexpr int kThreads = 256;                          // 4 waves
+constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kSlots = 5;                              // float4 slots per lane per tile
+constexpr int kWordValues = 20;                        // values per 32-bit element
+constexpr size_t kTileF4 = size_t(kWave) * kSlots;     // 320 float4 slots
+constexpr size_t kTileElems = kTileF4 * 4;             // 1280 values
+static_assert(kTileElems == size_t(kWave) * kWordValues, "one tile = one element per lane");
+
+__host__ __device__ inline size_t payload_words(size_t n)
+{
+    return n / kWordValues + (n % kWordValues != 0 ? 1 : 0);
+}
+
+// Orders this wave's LDS accesses across its lanes: LDS operations of one
+// wave complete in issue order, so it suffices that the compiler moves no
+// LDS access across this point.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Code of one value (0 zero, 1 pos, 2 neg) and its new residual.
+__device__ __forceinline__ uint32_t code_and_residual(float v, float neg, float pos, float& rn)
+{
+    const bool up = v >= pos;
+    const bool dn = v <= neg;
+    const float d = up ? pos : (dn ? neg : 0.0f);
+    rn = v - d;
+    return up ? 1u : (dn ? 2u : 0u);
+}
+
+// Codes of a float4 slot, value k in byte k, and the slot's new residual.
+__device__ __forceinline__ uint32_t classify4_bytes(f32x4 g, f32x4 r, float neg, float pos,
+                                                    f32x4& rn)
+{
+    uint32_t codes = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float rk;
+        codes |= code_and_residual(g[k] + r[k], neg, pos, rk) << (8 * k);
+        rn[k] = rk;
+    }
+    return codes;
+}
+
+constexpr uint32_t bytes4(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    return a | b << 8 | c << 16 | d << 24;
+}
+
+__device__ __forceinline__ uint32_t dot4(uint32_t a, uint32_t b, uint32_t acc)
+{
+    return __builtin_amdgcn_udot4(a, b, acc, false);
+}
+
+// The element of 20 codes held one per byte (value 4k + i in byte i of
+// c[k]): payload byte b is the base-3 number of values 5b .. 5b+4, first
+// value most significant, each a sum of byte products.
+__device__ __forceinline__ uint32_t fold_base3(const uint32_t (&c)[kSlots])
+{
+    const uint32_t b0 = dot4(c[0], bytes4(81, 27, 9, 3), dot4(c[1], bytes4(1, 0, 0, 0), 0u));
+    const uint32_t b1 = dot4(c[1], bytes4(0, 81, 27, 9), dot4(c[2], bytes4(3, 1, 0, 0), 0u));
+    const uint32_t b2 = dot4(c[2], bytes4(0, 0, 81, 27), dot4(c[3], bytes4(9, 3, 1, 0), 0u));
+    const uint32_t b3 = dot4(c[3], bytes4(0, 0, 0, 81), dot4(c[4], bytes4(27, 9, 3, 1), 0u));
+    return b0 | b1 << 8 | b2 << 16 | b3 << 24;
+}
+
+// Element j (values 20j .. 20j+19) by one thread, scalar accesses; values at
+// or past n are digit 0 and are neither read nor written.
+__device__ __forceinline__ uint32_t compress_word_scalar(const float* __restrict__ grad,
+                                                         float* __restrict__ residual, size_t n,
+                                                         float neg, float pos, size_t j)
+{
+    uint32_t word = 0;
+    // rolled: this path serves misaligned buffers and the one partial tile
+#pragma unroll 1
+    for (int b = 0; b < 4; ++b) {
+        uint32_t byte = 0;
+#pragma unroll 1
+        for (int k = 0; k < 5; ++k) {
+            const size_t i = j * kWordValues + size_t(5 * b + k);
+            uint32_t c = 0;
+            if (i < n) {
+                float rn;
+                c = code_and_residual(grad[i] + residual[i], neg, pos, rn);
+                residual[i] = rn;
+            }
+            byte = byte * 3u + c;
+        }
+        word |= byte << (8 * b);
+    }
+    return word;
+}
+
+// One full wave tile: float4 slots q0 .. q0 + kTileF4 - 1, all below n / 4.
+// `codes` is this wave's kTileF4-dword LDS buffer.
+__device__ __forceinline__ void compress_full_tile(const float* __restrict__ grad,
+                                                   float* __restrict__ residual, float neg,
+                                                   float pos, uint32_t* __restrict__ payload,
+                                                   size_t q0, int lane, uint32_t* codes)
+{
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(grad);
+    f32x4* r4 = reinterpret_cast<f32x4*>(residual);
+    f32x4 g[kSlots], r[kSlots];
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+        const size_t q = q0 + size_t(u) * kWave + lane;
+        g[u] = __builtin_nontemporal_load(g4 + q);
+        r[u] = __builtin_nontemporal_load(r4 + q);
+    }
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+        const size_t q = q0 + size_t(u) * kWave + lane;
+        f32x4 rn;
+        codes[u * kWave + lane] = classify4_bytes(g[u], r[u], neg, pos, rn);
+        __builtin_nontemporal_store(rn, r4 + q);
+    }
+    wave_lds_sync();
+    uint32_t c[kSlots];
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k)
+        c[k] = codes[kSlots * lane + k];
+    wave_lds_sync();  // these reads precede the next tile's writes
+    __builtin_nontemporal_store(fold_base3(c), payload + q0 / kSlots + lane);
+}
+
+__device__ __forceinline__ void compress_tile(const float* __restrict__ grad,
+                                              float* __restrict__ residual, size_t n, float neg,
+                                              float pos, uint32_t* __restrict__ payload,
+                                              size_t q0, int lane, uint32_t* codes)
+{
+    if (q0 + kTileF4 <= (n >> 2)) {
+        compress_full_tile(grad, residual, neg, pos, payload, q0, lane, codes);
+    } else {
+        const size_t j = q0 / kSlots + lane;
+        if (j < payload_words(n))
+            payload[j] = compress_word_scalar(grad, residual, n, neg, pos, j);
+    }
+}
+
+// 16-byte-aligned grad and residual. kLoop: a capped grid strides over tiles.
+template <bool kLoop>
+__global__ __launch_bounds__(kThreads) void compress_ternary_vec_kernel(
+    const float* __restrict__ grad, float* __restrict__ residual, size_t n, float neg,
+    float pos, float n_f, uint32_t* __restrict__ compr, size_t ntiles)
+{
+    __shared__ uint32_t codes[kWavesPerBlock][kTileF4];
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        write_header(compr, neg, pos, n_f);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const size_t stride = size_t(gridDim.x) * kWavesPerBlock;
+    for (size_t t = size_t(blockIdx.x) * kWavesPerBlock + wave; t < ntiles; t += stride) {
+        compress_tile(grad, residual, n, neg, pos, compr + 3, t * kTileF4, lane, codes[wave]);
+        if (!kLoop)
+            break;
+    }
+}
+
+// Any 4-byte alignment: one thread per element.
+__global__ __launch_bounds__(kThreads) void compress_ternary_scalar_kernel(
+    const float* __restrict__ grad, float* __restrict__ residual, size_t n, float neg,
+    float pos, float n_f, uint32_t* __restrict__ compr)
+{
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        write_header(compr, neg, pos, n_f);
+    const size_t nwords = payload_words(n);
+    const size_t stride = size_t(gridDim.x) * blockDim.x;
+    for (size_t j = size_t(blockIdx.x) * blockDim.x + threadIdx.x; j < nwords; j += stride)
+        compr[3 + j] = compress_word_scalar(grad, residual, n, neg, pos, j);
+}
+
+// Digit table in LDS: for a payload byte with digits c0..c4 (c0 = 3 for the
+// unused bytes 243..255), the byte offsets into one worker's nibble table of
+// the code pairs (c0, c1) in bits 0..7, (c2, c3) in bits 8..15 and (c4, 0)
+// in bits 16..23. No barrier: build_nibble_table, called next, ends in one.
+__device__ __forceinline__ void build_digit_table(uint32_t* dtab)
+{
+    for (uint32_t b = threadIdx.x; b < 256u; b += blockDim.x) {
+        const uint32_t c0 = b / 81u, c1 = b / 27u % 3u, c2 = b / 9u % 3u, c3 = b / 3u % 3u,
+                       c4 = b % 3u;
+        dtab[b] = (8u * (4u * c0 + c1)) | (8u * (4u * c2 + c3)) << 8 | (8u * (4u * c4)) << 16;
+    }
+}
+
+// Adds (or, for the first worker, sets) the 20 values of one element into
+// acc, through worker table t (16 float2) and the digit table.
+__device__ __forceinline__ void decode_element(uint32_t word, const float2* t,
+                                               const uint32_t* dtab, float (&acc)[kWordValues],
+                                               bool first)
+{
+    const char* tb = reinterpret_cast<const char*>(t);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t d = dtab[(word >> (8 * b)) & 0xFFu];
+        const float2 p0 = *reinterpret_cast<const float2*>(tb + (d & 0xFFu));
+        const float2 p1 = *reinterpret_cast<const float2*>(tb + ((d >> 8) & 0xFFu));
+        const float s = *reinterpret_cast<const float*>(tb + (d >> 16));
+        const float v[5] = {p0.x, p0.y, p1.x, p1.y, s};
+#pragma unroll
+        for (int k = 0; k < 5; ++k)
+            acc[5 * b + k] = first ? v[k] : acc[5 * b + k] + v[k];
+    }
+}
+
+// One full wave tile of the W-block dequantize-and-sum. WC > 0: W == WC at
+// compile time, every worker's element in flight at once; WC == 0: W read at
+// run time, in groups of four. `stage` is this wave's kTileF4-float4 buffer.
+template <int WC, bool kAcc>
+__device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& tab, int W_rt,
+                                                     const float2* lut, const uint32_t* dtab,
+                                                     float* __restrict__ out, size_t q0,
+                                                     int lane, f32x4* stage)
+{
+    const int W = WC > 0 ? WC : W_rt;
+    const size_t j = q0 / kSlots + lane;
+    float acc[kWordValues];
+    constexpr int kGroup = WC > 0 ? WC : 4;
+    for (int w0 = 0; w0 < W; w0 += kGroup) {
+        uint32_t mine[kGroup];
+#pragma unroll
+        for (int dw = 0; dw < kGroup; ++dw) {
+            mine[dw] = (WC == 0 && w0 + dw >= W)
+                           ? 0u
+                           : __builtin_nontemporal_load(tab.p[w0 + dw] + 3 + j);
+        }
+#pragma unroll
+        for (int dw = 0; dw < kGroup; ++dw) {
+            const int w = w0 + dw;
+            if (WC == 0 && w >= W)
+                break;
+            decode_element(mine[dw], lut + 16 * w, dtab, acc, w == 0);
+        }
+    }
+    // lane L holds values 20L .. 20L+19 of the tile = float4 slots 5L .. 5L+4
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k)
+        stage[kSlots * lane + k] =
+            f32x4{acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]};
+    wave_lds_sync();
+    f32x4* o4 = reinterpret_cast<f32x4*>(out);
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u) {
+        const size_t q = q0 + size_t(u) * kWave + lane;
+        f32x4 v = stage[u * kWave + lane];
+        if (kAcc)
+            v = o4[q] + v;
+        __builtin_nontemporal_store(v, o4 + q);
+    }
+    wave_lds_sync();  // these reads precede the next tile's writes
+}
+
+// The last, partial tile: lane L decodes element q0/5 + L for every worker
+// and writes the values below n.
+__device__ __forceinline__ void decompress_tail_tile(const PtrTable<uint32_t>& tab, int W,
+                                                     const float2* lut, const uint32_t* dtab,
+                                                     size_t n, float* __restrict__ out,
+                                                     int accumulate, size_t q0, int lane)
+{
+    const size_t j = q0 / kSlots + lane;
+    if (j >= payload_words(n))
+        return;
+    float acc[kWordValues];
+#pragma unroll 1
+    for (int w = 0; w < W; ++w)
+        decode_element(tab.p[w][3 + j], lut + 16 * w, dtab, acc, w == 0);
+#pragma unroll
+    for (int k = 0; k < kWordValues; ++k) {
+        const size_t i = j * kWordValues + k;
+        if (i < n)
+            out[i] = accumulate ? out[i] + acc[k] : acc[k];
+    }
+}
+
+// Dequantize-and-sum of W blocks into a 16-byte-aligned out (kAcc: added to
+// what out holds). Last tile first, XCD-contiguous, as in the 2-bit kernel:
+// the partial tile's scalar path starts with the first wave, and tiles whose
+// 256-byte element runs share edge cache lines meet in one L2.
+template <int WC, bool kAcc, bool kLoop>
+__global__ __launch_bounds__(kThreads) void decompress_ternary_vec_kernel(
+    PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, size_t ntiles)
+{
+    __shared__ float2 lut[16 * GC_MAX_WORKERS];
+    __shared__ uint32_t dtab[256];
+    __shared__ f32x4 stage[kWavesPerBlock][kTileF4];
+    build_digit_table(dtab);
+    build_nibble_table(lut, tab, WC > 0 ? WC : W);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const size_t stride = size_t(gridDim.x) * kWavesPerBlock;
+    const size_t blk = kLoop ? blockIdx.x : xcd_contiguous(blockIdx.x, gridDim.x);
+    for (size_t t = blk * kWavesPerBlock + wave; t < ntiles; t += stride) {
+        const size_t q0 = (ntiles - 1 - t) * kTileF4;
+        if (q0 + kTileF4 <= (n >> 2))
+            decompress_full_tile<WC, kAcc>(tab, W, lut, dtab, out, q0, lane, stage[wave]);
+        else
+            decompress_tail_tile(tab, WC > 0 ? WC : W, lut, dtab, n, out, kAcc ? 1 : 0, q0,
+                                 lane);
+        if (!kLoop)
+            break;
+    }
+}
+
+// Any 4-byte-aligned out: one thread per value.
+__global__ __launch_bounds__(kThreads) void decompress_ternary_scalar_kernel(
+    PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, int accumulate)
+{
+    __shared__ float2 lut[16 * GC_MAX_WORKERS];
+    __shared__ uint32_t dtab[256];
+    build_digit_table(dtab);
+    build_nibble_table(lut, tab, W);
+    const size_t stride = size_t(gridDim.x) * blockDim.x;
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const size_t byte_i = i / 5;
+        const uint32_t k = uint32_t(i % 5);
+        const uint32_t shift = k < 2u ? 0u : (k < 4u ? 8u : 16u);
+        float acc = 0.0f;
+        for (int w = 0; w < W; ++w) {
+            const uint8_t* bytes = reinterpret_cast<const uint8_t*>(tab.p[w] + 3);
+            const uint32_t off = (dtab[bytes[byte_i]] >> shift) & 0xFFu;
+            const float2 p = lut[16 * w + off / 8u];
+            const float d = (k & 1u) ? p.y : p.x;
+            acc = (w == 0) ? d : acc + d;
+        }
+        out[i] = accumulate ? out[i] + acc : acc;
+    }
+}
+
+size_t grid_for_tiles(size_t ntiles)
+{
+    return std::max<size_t>(1, std::min(ceil_div(ntiles, kWavesPerBlock), max_grid_blocks()));
+}
+
+bool tiles_need_loop(size_t ntiles)
+{
+    return ceil_div(ntiles, kWavesPerBlock) > max_grid_blocks();
+}
+
+template <bool kLoop>
+void launch_decompress_vec(const PtrTable<uint32_t>& tab, int W, size_t n, float* out,
+                           int accumulate, size_t ntiles, dim3 grid, dim3 block,
+                           hipStream_t stream)
+{
+    if (accumulate) {
+        // only decompress_ternary accumulates (W == 1)
+        hipLaunchKernelGGL((decompress_ternary_vec_kernel<1, true, kLoop>), grid, block, 0,
+                           stream, tab, W, n, out, ntiles);
+        return;
+    }
+    switch (W) {
+#define GCQ_TDEC_CASE(k)                                                                    \
+    case k:                                                                                 \
+        hipLaunchKernelGGL((decompress_ternary_vec_kernel<k, false, kLoop>), grid, block, 0, \
+                           stream, tab, W, n, out, ntiles);                                 \
+        break;
+        GCQ_TDEC_CASE(1)
+        GCQ_TDEC_CASE(2)
+        GCQ_TDEC_CASE(3)
+        GCQ_TDEC_CASE(4)
+        GCQ_TDEC_CASE(5)
+        GCQ_TDEC_CASE(6)
+        GCQ_TDEC_CASE(7)
+        GCQ_TDEC_CASE(8)
+#undef GCQ_TDEC_CASE
+    default:
+        hipLaunchKernelGGL((decompress_ternary_vec_kernel<0, false, kLoop>), grid, block, 0,
+                           stream, tab, W, n, out, ntiles);
+    }
+}
+
+int launch_decompress(const PtrTable<uint32_t>& tab, int W, size_t n, float* out,
+                      int accumulate, hipStream_t stream, const char* what)
+{
+    if (n == 0)
+        return GC_OK;
+    if (aligned16(out)) {
+        const size_t ntiles = ceil_div(n, kTileElems);
+        const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
+        if (tiles_need_loop(ntiles))
+            launch_decompress_vec<true>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
+        else
+            launch_decompress_vec<false>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
+    } else {
+        const size_t blocks = std::min(ceil_div(n, kThreads), max_grid_blocks());
+        hipLaunchKernelGGL(decompress_ternary_scalar_kernel, dim3(blocks), dim3(kThreads), 0,
+                           stream, tab, W, n, out, accumulate);
+    }
+    return check_launch(what);
+}
+
+}  // namespace
+}  // namespace gcq
+
+using namespace gcq;
+
+GCQ_API size_t gc_compressed_ternary_words(size_t n) { return 3 + payload_words(n); }
+
+GCQ_API int compress_ternary(const float* grad, float* residual, size_t n, float neg_threshold,
+                             float pos_threshold, uint32_t* compr, hipStream_t stream)
+{
+    clear_error();
+    if (!compr)
+        return fail(GC_EINVAL, "compress_ternary: compr is NULL");
+    if (n > 0 && (!grad || !residual))
+        return fail(GC_EINVAL, "compress_ternary: grad or residual is NULL with n > 0");
+    if (int rc = check_thresholds(neg_threshold, pos_threshold))
+        return rc;
+    if (!aligned4(compr) || !aligned4(grad) || !aligned4(residual))
+        return fail(GC_EINVAL, "compress_ternary: buffers must be 4-byte aligned");
+    const float n_f = static_cast<float>(n);
+    if (n == 0 || (aligned16(grad) && aligned16(residual))) {
+        const size_t ntiles = ceil_div(n, kTileElems);
+        const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
+        if (tiles_need_loop(ntiles))
+            hipLaunchKernelGGL(compress_ternary_vec_kernel<true>, grid, block, 0, stream, grad,
+                               residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles);
+        else
+            hipLaunchKernelGGL(compress_ternary_vec_kernel<false>, grid, block, 0, stream, grad,
+                               residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles);
+    } else {
+        const size_t blocks =
+            std::min(ceil_div(payload_words(n), kThreads), max_grid_blocks());
+        hipLaunchKernelGGL(compress_ternary_scalar_kernel, dim3(blocks), dim3(kThreads), 0,
+                           stream, grad, residual, n, neg_threshold, pos_threshold, n_f, compr);
+    }
+    return check_launch("compress_ternary");
+}
+
+GCQ_API int decompress_ternary(const uint32_t* compr, size_t n, float* out, int accumulate,
+                               hipStream_t stream)
+{
+    clear_error();
+    if (!compr)
+        return fail(GC_EINVAL, "decompress_ternary: compr is NULL");
+    if (n > 0 && !out)
+        return fail(GC_EINVAL, "decompress_ternary: out is NULL with n > 0");
+    if (accumulate != 0 && accumulate != 1)
+        return fail(GC_EINVAL, "decompress_ternary: accumulate must be 0 or 1");
+    if (!aligned4(compr) || !aligned4(out))
+        return fail(GC_EINVAL, "decompress_ternary: buffers must be 4-byte aligned");
+    PtrTable<uint32_t> tab{};
+    tab.p[0] = compr;
+    return launch_decompress(tab, 1, n, out, accumulate, stream, "decompress_ternary");
+}
+
+GCQ_API int decompress_ternary_sum(const uint32_t* const* compr, int W, size_t n, float* out,
+                                   hipStream_t stream)
+{
+    clear_error();
+    if (!compr)
+        return fail(GC_EINVAL, "decompress_ternary_sum: compr is NULL");
+    if (W < 1 || W > GC_MAX_WORKERS)
+        return fail(GC_EINVAL, "decompress_ternary_sum: W must be in [1, 64]");
+    if (n > 0 && !out)
+        return fail(GC_EINVAL, "decompress_ternary_sum: out is NULL with n > 0");
+    if (!aligned4(out))
+        return fail(GC_EINVAL, "decompress_ternary_sum: out must be 4-byte aligned");
+    PtrTable<uint32_t> tab{};
+    for (int w = 0; w < W; ++w) {
+        if (!compr[w] || !aligned4(compr[w]))
+            return fail(GC_EINVAL,
+                        "decompress_ternary_sum: a block pointer is NULL or misaligned");
+        tab.p[w] = compr[w];
+    }
+    return launch_decompress(tab, W, n, out, 0, stream, "decompress_ternary_sum");
+}

@@ -20,6 +20,7 @@
 //  - a float4 slot that straddles n is handled by scalar loads in the same
 //    lane; values past n take code 00 and are never read or written.
 #include "gcq_internal.h"
+#include "threshold_codes.h"
 
 #include <algorithm>
 #include <cmath>
@@ -37,11 +38,6 @@ constexpr size_t kBlockElems = kTileElems * kWavesPerBlock;  // 4096 values
 // A tile is 64 words of codes, one per lane: the cross-lane moves that
 // gather and scatter words rely on it.
 static_assert(kUnroll == 4 && kTileF4 == 256, "one tile = 64 words of codes");
-
-__device__ __forceinline__ float code_value(uint32_t c, float neg, float pos)
-{
-    return c == 1u ? pos : (c == 2u ? neg : 0.0f);
-}
 
 // Code and residual of four values. Thresholds satisfy neg < 0 < pos, so at
 // most one of the two comparisons holds and value 0 is always code 00.
@@ -142,13 +138,6 @@ __device__ __forceinline__ void compress_tile(const float* __restrict__ grad,
     }
 }
 
-__device__ __forceinline__ void write_header(uint32_t* blk, float neg, float pos, float n_f)
-{
-    blk[0] = f2u(neg);
-    blk[1] = f2u(pos);
-    blk[2] = f2u(n_f);
-}
-
 // 16-byte-aligned grad and residual. kLoop = false: the grid has one wave
 // per tile (the usual case); true: a capped grid strides over the tiles.
 template <bool kLoop>
@@ -184,25 +173,6 @@ __global__ __launch_bounds__(kThreads) void compress_2bit_scalar_kernel(
     const size_t stride = size_t(gridDim.x) * blockDim.x;
     for (size_t j = size_t(blockIdx.x) * blockDim.x + threadIdx.x; j < nwords; j += stride)
         compr[3 + j] = compress_word_scalar(grad, residual, n, neg, pos, j);
-}
-
-// Dequantization table in LDS: for worker w and a 4-bit nibble v (two codes,
-// the earlier value in the high pair), entry 16w + v holds the two values.
-// One worker's 16 entries span 128 bytes -- every LDS bank once -- so a
-// wave's lookups into it never conflict.
-__device__ __forceinline__ void build_nibble_table(float2* lut, const PtrTable<uint32_t>& tab,
-                                                   int W)
-{
-    for (int w = 0; w < W; ++w) {
-        if (threadIdx.x < 16) {
-            const uint32_t* b = tab.p[w];
-            const float neg = u2f(b[0]);
-            const float pos = u2f(b[1]);
-            const uint32_t v = threadIdx.x;
-            lut[16 * w + v] = make_float2(code_value(v >> 2, neg, pos), code_value(v & 3u, neg, pos));
-        }
-    }
-    __syncthreads();
 }
 
 // One wave tile of the W-block dequantize-and-sum (see compress_wave_tile).
@@ -379,13 +349,6 @@ __global__ __launch_bounds__(kThreads) void compress_2bit_multi_kernel(
 }
 
 static_assert(kBlockElems / 16 == kThreads, "scalar multi path: one word per thread");
-
-int check_thresholds(float neg, float pos)
-{
-    if (!(std::isfinite(neg) && std::isfinite(pos) && neg < 0.0f && pos > 0.0f))
-        return fail(GC_EINVAL, "thresholds must be finite with neg_threshold < 0 < pos_threshold");
-    return GC_OK;
-}
 
 size_t grid_for_tiles(size_t ntiles)
 {

@@ -135,6 +135,39 @@ int compress_2bit_multi(gc_plan* plan, float neg_threshold,
 /* Frees the plan's device memory. Waits for the device first. */
 void gc_plan_destroy(gc_plan* plan);
 
+/* ---- dense ternary packing of the same codes ------------------------- */
+
+/* PR #8342 "Two bit quantization" notes that its three codes leave one
+ * 2-bit pattern unused and defers a denser packing. These entry points are
+ * that packing: the same thresholds, codes, residual update and header as
+ * compress_2bit, with five codes per byte as base-3 digits (1.6 bits per
+ * value). Payload byte j (bytes in memory order from element 3 on) holds
+ * values 5j .. 5j+4 as c0*81 + c1*27 + c2*9 + c3*3 + c4, the first value
+ * most significant, digit = code (0 zero, 1 positive, 2 negative); zero
+ * bytes pad the payload to whole elements.
+ *
+ * Size in 32-bit elements of the block for n values: 3 + ceil(n / 20).
+ * Host-only; enqueues nothing. */
+size_t gc_compressed_ternary_words(size_t n);
+
+/* As compress_2bit (same arguments, same residual update, same
+ * validation), writing the ternary block: every element of `compr`
+ * (gc_compressed_ternary_words(n) of them, 4-byte aligned) is written. */
+int compress_ternary(const float* grad, float* residual, size_t n,
+                     float neg_threshold, float pos_threshold,
+                     uint32_t* compr, hipStream_t stream);
+
+/* As decompress_2bit, for a ternary block. Digit 1 -> compr[1], 2 ->
+ * compr[0], 0 -> 0; a byte above 242 (never written) has leading digit 3,
+ * which also reads as 0. */
+int decompress_ternary(const uint32_t* compr, size_t n, float* out,
+                       int accumulate, hipStream_t stream);
+
+/* As decompress_2bit_sum, for W ternary blocks: fp32 sum in worker order,
+ * starting from worker 0's value. */
+int decompress_ternary_sum(const uint32_t* const* compr, int W, size_t n,
+                           float* out, hipStream_t stream);
+
 /* ====================================================================
  * QSGDMaxNorm (vineeths96 page, "About The Project": one max-norm shared by
  * all workers keeps the integer levels summable by an all-reduce)

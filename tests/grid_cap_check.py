@@ -57,6 +57,34 @@ def main():
             gu.sync()
             check(np.array_equal(gu.host(out), oracle.dequantize_2bit_sum(comprs, n)),
                   f"decompress sum W={W} n={n}")
+    # ternary packing: same shapes
+    for n in (40_000 + 7, 123_457):
+        print(f"[case] capped ternary n={n}", flush=True)
+        g = si.normal_f32(n + 3, n, 0.5)
+        r0 = si.normal_f32(n + 4, n, 0.2)
+        r_dev = gu.dev(r0)
+        compr = gu.empty(gcq.gc_compressed_ternary_words(n), torch.int32, fill=-1)
+        gcq.compress_ternary(gu.dev(g), r_dev, -0.5, 0.5, compr)
+        r_or = r0.copy()
+        c_or = oracle.quantize_ternary(g, r_or, -0.5, 0.5)
+        gu.sync()
+        check(np.array_equal(gu.host(compr, np.uint32), c_or), f"ternary words n={n}")
+        check(np.array_equal(gu.host(r_dev).view(np.uint32), r_or.view(np.uint32)),
+              f"ternary residual n={n}")
+        base = si.normal_f32(n + 5, n, 1.0)
+        out = gu.dev(base)
+        gcq.decompress_ternary(gu.dev(c_or), n, out, accumulate=True)
+        gu.sync()
+        check(np.array_equal(gu.host(out), (base + oracle.dequantize_ternary(c_or, n)).astype(np.float32)),
+              f"ternary decompress accumulate n={n}")
+        for W in (8, 9):
+            comprs = [oracle.quantize_ternary(si.normal_f32(11 * w + n, n, 0.5), np.zeros(n, np.float32),
+                                              -0.3 - 0.01 * w, 0.3 + 0.02 * w) for w in range(W)]
+            out = gu.empty(n, torch.float32, fill=float("nan"))
+            gcq.decompress_ternary_sum([gu.dev(c) for c in comprs], n, out)
+            gu.sync()
+            check(np.array_equal(gu.host(out), oracle.dequantize_ternary_sum(comprs, n)),
+                  f"ternary decompress sum W={W} n={n}")
     # many tensors, more chunks than workgroups
     print("[case] capped multi-tensor", flush=True)
     sizes = [5000, 0, 17, 70_001, 4096 * 3, 33]

@@ -44,7 +44,9 @@ def test_header_declares_the_expected_entry_points():
                  "qsgd_maxnorm_quantize", "qsgd_dequant_sum", "qsgd_global_maxnorm",
                  "grandk_indices", "gather_f32", "compress_2bit_multi",
                  "gc_plan_2bit_multi_create", "gc_plan_destroy", "gc_compressed_2bit_words",
-                 "gc_plan_compressed_words", "gc_plan_block_offsets", "gc_last_error"):
+                 "gc_plan_compressed_words", "gc_plan_block_offsets", "gc_last_error",
+                 "gc_compressed_ternary_words", "compress_ternary", "decompress_ternary",
+                 "decompress_ternary_sum"):
         assert must in names, must
 
 
@@ -65,6 +67,13 @@ def test_compressed_words_matches_oracle(lib, n):
         assert lib.gc_compressed_2bit_words(n) == oracle.compressed_2bit_words(n)
 
 
+@pytest.mark.parametrize("n", [0, 1, 19, 20, 21, 1280, 25_557_032, 2 ** 33 + 5, 2 ** 64 - 1])
+def test_compressed_ternary_words_matches_oracle(lib, n):
+    assert lib.gc_compressed_ternary_words(n) == 3 + (n + 19) // 20
+    if n < 10 ** 8:
+        assert lib.gc_compressed_ternary_words(n) == oracle.compressed_ternary_words(n)
+
+
 def _rc_compress(lib, grad, res, n, neg, pos, compr):
     return lib.compress_2bit(grad, res, n, neg, pos, compr, None)
 
@@ -76,6 +85,7 @@ def test_compress_rejects_bad_thresholds(lib, neg, pos):
     assert _rc_compress(lib, FAKE, FAKE, 16, neg, pos, FAKE) == gcq.GC_EINVAL
     assert b"threshold" in lib.gc_last_error()
     assert lib.compress_2bit_multi(FAKE, neg, pos, FAKE, None) == gcq.GC_EINVAL
+    assert lib.compress_ternary(FAKE, FAKE, 16, neg, pos, FAKE, None) == gcq.GC_EINVAL
 
 
 def test_compress_rejects_null_and_misaligned(lib):
@@ -95,6 +105,22 @@ def test_decompress_rejects_bad_arguments(lib):
     assert lib.decompress_2bit_sum(arr, 65, 16, FAKE, None) == gcq.GC_EINVAL
     arr[1] = None
     assert lib.decompress_2bit_sum(arr, 2, 16, FAKE, None) == gcq.GC_EINVAL
+
+
+def test_ternary_rejects_null_and_misaligned(lib):
+    for args in ((FAKE, FAKE, 16, -1.0, 1.0, NULL), (NULL, FAKE, 16, -1.0, 1.0, FAKE),
+                 (FAKE, NULL, 16, -1.0, 1.0, FAKE), (FAKE + 2, FAKE, 16, -1.0, 1.0, FAKE),
+                 (FAKE, FAKE, 16, -1.0, 1.0, FAKE + 1)):
+        assert lib.compress_ternary(*args, None) == gcq.GC_EINVAL
+    assert lib.decompress_ternary(NULL, 16, FAKE, 0, None) == gcq.GC_EINVAL
+    assert lib.decompress_ternary(FAKE, 16, NULL, 0, None) == gcq.GC_EINVAL
+    assert lib.decompress_ternary(FAKE, 16, FAKE, 2, None) == gcq.GC_EINVAL
+    arr = (ctypes.c_void_p * 65)(*([FAKE] * 65))
+    assert lib.decompress_ternary_sum(arr, 0, 16, FAKE, None) == gcq.GC_EINVAL
+    assert lib.decompress_ternary_sum(arr, 65, 16, FAKE, None) == gcq.GC_EINVAL
+    arr[1] = None
+    assert lib.decompress_ternary_sum(arr, 2, 16, FAKE, None) == gcq.GC_EINVAL
+    assert b"decompress_ternary_sum" in lib.gc_last_error()
 
 
 def test_qsgd_rejects_bad_arguments(lib):

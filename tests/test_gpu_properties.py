@@ -40,6 +40,33 @@ def test_compress_decompress_random(gcq, n, neg, pos, sigma, misalign, seed):
 
 
 @SETTINGS
+@given(n=st.integers(0, 70_000), neg=st.floats(1e-4, 4.0), pos=st.floats(1e-4, 4.0),
+       sigma=st.floats(1e-3, 8.0), misalign=st.booleans(), W=st.integers(1, 10),
+       seed=st.integers(0, 2 ** 31 - 1))
+def test_ternary_random(gcq, n, neg, pos, sigma, misalign, W, seed):
+    announce(f"prop ternary n={n} neg=-{neg} pos={pos} sigma={sigma} mis={misalign} W={W} seed={seed}")
+    neg32, pos32 = np.float32(-neg), np.float32(pos)
+    comprs_or, comprs_dev = [], []
+    for w in range(W):
+        g = si.normal_f32(seed + 31 * w, n, sigma)
+        r0 = si.normal_f32(seed + 31 * w + 1, n, sigma / 2)
+        r_dev = gu.dev(r0, misalign)
+        compr = gu.empty(gcq.gc_compressed_ternary_words(n), torch.int32, misalign=misalign, fill=-1)
+        gcq.compress_ternary(gu.dev(g, misalign), r_dev, float(neg32), float(pos32), compr)
+        r_or = r0.copy()
+        c_or = oracle.quantize_ternary(g, r_or, neg32, pos32)
+        gu.sync()
+        np.testing.assert_array_equal(gu.host(compr, np.uint32), c_or)
+        np.testing.assert_array_equal(gu.host(r_dev).view(np.uint32), r_or.view(np.uint32))
+        comprs_or.append(c_or)
+        comprs_dev.append(compr)
+    out = gu.empty(n, torch.float32, misalign=not misalign, fill=float("nan"))
+    gcq.decompress_ternary_sum(comprs_dev, n, out)
+    gu.sync()
+    np.testing.assert_array_equal(gu.host(out), oracle.dequantize_ternary_sum(comprs_or, n))
+
+
+@SETTINGS
 @given(W=st.integers(1, 12), n=st.integers(1, 40_000), seed=st.integers(0, 2 ** 31 - 1))
 def test_dequantize_sum_random(gcq, W, n, seed):
     announce(f"prop dequantize-sum W={W} n={n} seed={seed}")
