@@ -22,9 +22,11 @@
 //    (5 consecutive dwords: distinct banks) and folds them into 4 base-3
 //    bytes with byte dot products; one coalesced 256-byte store per tile;
 //  - dequantize: lane L loads element L of each block (one 256-byte load per
-//    worker), decodes its 20 values through two LDS tables and sums them in
+//    worker), splits each byte into digits with multiply-shifts, reads the
+//    values from a per-worker LDS table of digit pairs and sums them in
 //    worker order; a wave-private LDS transpose turns each lane's 20
-//    consecutive values into lane-contiguous float4 stores.
+//    consecutive values into lane-contiguous float4 stores (storing them
+//    directly, 80 bytes apart per lane, measured three times slower).
 #include "gcq_internal.h"
 #include "threshold_codes.h"
 
@@ -207,33 +209,67 @@ __global__ __launch_bounds__(kThreads) void compress_ternary_scalar_kernel(
         compr[3 + j] = compress_word_scalar(grad, residual, n, neg, pos, j);
 }
 
-// Digit table in LDS: for a payload byte with digits c0..c4 (c0 = 3 for the
-// unused bytes 243..255), the byte offsets into one worker's nibble table of
-// the code pairs (c0, c1) in bits 0..7, (c2, c3) in bits 8..15 and (c4, 0)
-// in bits 16..23. No barrier: build_nibble_table, called next, ends in one.
-__device__ __forceinline__ void build_digit_table(uint32_t* dtab)
+// Pair table in LDS: for worker w, entry 16w + p (p = 3a + b < 16) holds
+// the values of the digit pair (a, b); a >= 3 -- only the leading digit of
+// the never-written bytes 243..255 -- reads as zero. One worker's entries
+// span 128 bytes, so a wave's lookups into it never conflict. Ends with a
+// block barrier.
+__device__ __forceinline__ void build_pair_table(float2* lut, const PtrTable<uint32_t>& tab,
+                                                 int W)
 {
-    for (uint32_t b = threadIdx.x; b < 256u; b += blockDim.x) {
-        const uint32_t c0 = b / 81u, c1 = b / 27u % 3u, c2 = b / 9u % 3u, c3 = b / 3u % 3u,
-                       c4 = b % 3u;
-        dtab[b] = (8u * (4u * c0 + c1)) | (8u * (4u * c2 + c3)) << 8 | (8u * (4u * c4)) << 16;
+    for (int w = 0; w < W; ++w) {
+        if (threadIdx.x < 16) {
+            const uint32_t* b = tab.p[w];
+            const float neg = u2f(b[0]);
+            const float pos = u2f(b[1]);
+            const uint32_t p = threadIdx.x;
+            lut[16 * w + p] = make_float2(code_value(p / 3u, neg, pos), code_value(p % 3u, neg, pos));
+        }
     }
+    __syncthreads();
 }
 
+// Digits of a payload byte x without a division: x = 27 p0 + 3 p1 + c4 with
+// p0 = 3 c0 + c1 (the leading pair; 9 for x >= 243) and p1 = 3 c2 + c3.
+// (2428 x) >> 16 is floor(x / 27) for every x < 256 and (11 r) >> 5 is
+// floor(r / 3) for every r < 27 (checked at compile time below).
+struct Digits {
+    uint32_t p0, p1, c4;
+};
+
+__host__ __device__ constexpr Digits split_byte(uint32_t x)
+{
+    const uint32_t p0 = (x * 2428u) >> 16;
+    const uint32_t r = x - 27u * p0;
+    const uint32_t p1 = (r * 11u) >> 5;
+    return Digits{p0, p1, r - 3u * p1};
+}
+
+constexpr bool split_byte_exact()
+{
+    for (uint32_t x = 0; x < 256u; ++x) {
+        const Digits d = split_byte(x);
+        if (d.p0 != x / 27u || d.p1 != x % 27u / 3u || d.c4 != x % 3u)
+            return false;
+    }
+    return true;
+}
+static_assert(split_byte_exact(), "multiply-shift digit split must be exact for every byte");
+
 // Adds (or, for the first worker, sets) the 20 values of one element into
-// acc, through worker table t (16 float2) and the digit table.
+// acc through worker pair table t: per byte two pairs and one single digit
+// (entry 3 c4 holds (c4, 0)).
 __device__ __forceinline__ void decode_element(uint32_t word, const float2* t,
-                                               const uint32_t* dtab, float (&acc)[kWordValues],
-                                               bool first)
+                                               float (&acc)[kWordValues], bool first)
 {
     const char* tb = reinterpret_cast<const char*>(t);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        const uint32_t d = dtab[(word >> (8 * b)) & 0xFFu];
-        const float2 p0 = *reinterpret_cast<const float2*>(tb + (d & 0xFFu));
-        const float2 p1 = *reinterpret_cast<const float2*>(tb + ((d >> 8) & 0xFFu));
-        const float s = *reinterpret_cast<const float*>(tb + (d >> 16));
-        const float v[5] = {p0.x, p0.y, p1.x, p1.y, s};
+        const Digits d = split_byte((word >> (8 * b)) & 0xFFu);
+        const float2 q0 = *reinterpret_cast<const float2*>(tb + 8u * d.p0);
+        const float2 q1 = *reinterpret_cast<const float2*>(tb + 8u * d.p1);
+        const float s = *reinterpret_cast<const float*>(tb + 24u * d.c4);
+        const float v[5] = {q0.x, q0.y, q1.x, q1.y, s};
 #pragma unroll
         for (int k = 0; k < 5; ++k)
             acc[5 * b + k] = first ? v[k] : acc[5 * b + k] + v[k];
@@ -245,9 +281,8 @@ __device__ __forceinline__ void decode_element(uint32_t word, const float2* t,
 // run time, in groups of four. `stage` is this wave's kTileF4-float4 buffer.
 template <int WC, bool kAcc>
 __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& tab, int W_rt,
-                                                     const float2* lut, const uint32_t* dtab,
-                                                     float* __restrict__ out, size_t q0,
-                                                     int lane, f32x4* stage)
+                                                     const float2* lut, float* __restrict__ out,
+                                                     size_t q0, int lane, f32x4* stage)
 {
     const int W = WC > 0 ? WC : W_rt;
     const size_t j = q0 / kSlots + lane;
@@ -266,7 +301,7 @@ __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& t
             const int w = w0 + dw;
             if (WC == 0 && w >= W)
                 break;
-            decode_element(mine[dw], lut + 16 * w, dtab, acc, w == 0);
+            decode_element(mine[dw], lut + 16 * w, acc, w == 0);
         }
     }
     // lane L holds values 20L .. 20L+19 of the tile = float4 slots 5L .. 5L+4
@@ -290,9 +325,9 @@ __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& t
 // The last, partial tile: lane L decodes element q0/5 + L for every worker
 // and writes the values below n.
 __device__ __forceinline__ void decompress_tail_tile(const PtrTable<uint32_t>& tab, int W,
-                                                     const float2* lut, const uint32_t* dtab,
-                                                     size_t n, float* __restrict__ out,
-                                                     int accumulate, size_t q0, int lane)
+                                                     const float2* lut, size_t n,
+                                                     float* __restrict__ out, int accumulate,
+                                                     size_t q0, int lane)
 {
     const size_t j = q0 / kSlots + lane;
     if (j >= payload_words(n))
@@ -300,7 +335,7 @@ __device__ __forceinline__ void decompress_tail_tile(const PtrTable<uint32_t>& t
     float acc[kWordValues];
 #pragma unroll 1
     for (int w = 0; w < W; ++w)
-        decode_element(tab.p[w][3 + j], lut + 16 * w, dtab, acc, w == 0);
+        decode_element(tab.p[w][3 + j], lut + 16 * w, acc, w == 0);
 #pragma unroll
     for (int k = 0; k < kWordValues; ++k) {
         const size_t i = j * kWordValues + k;
@@ -312,16 +347,16 @@ __device__ __forceinline__ void decompress_tail_tile(const PtrTable<uint32_t>& t
 // Dequantize-and-sum of W blocks into a 16-byte-aligned out (kAcc: added to
 // what out holds). Last tile first, XCD-contiguous, as in the 2-bit kernel:
 // the partial tile's scalar path starts with the first wave, and tiles whose
-// 256-byte element runs share edge cache lines meet in one L2.
+// 256-byte element runs share edge cache lines meet in one L2. The pair
+// table holds WC workers when W is known at compile time (less LDS per
+// workgroup, more workgroups per CU).
 template <int WC, bool kAcc, bool kLoop>
 __global__ __launch_bounds__(kThreads) void decompress_ternary_vec_kernel(
     PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, size_t ntiles)
 {
-    __shared__ float2 lut[16 * GC_MAX_WORKERS];
-    __shared__ uint32_t dtab[256];
+    __shared__ float2 lut[16 * (WC > 0 ? WC : GC_MAX_WORKERS)];
     __shared__ f32x4 stage[kWavesPerBlock][kTileF4];
-    build_digit_table(dtab);
-    build_nibble_table(lut, tab, WC > 0 ? WC : W);
+    build_pair_table(lut, tab, WC > 0 ? WC : W);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const size_t stride = size_t(gridDim.x) * kWavesPerBlock;
@@ -329,10 +364,9 @@ __global__ __launch_bounds__(kThreads) void decompress_ternary_vec_kernel(
     for (size_t t = blk * kWavesPerBlock + wave; t < ntiles; t += stride) {
         const size_t q0 = (ntiles - 1 - t) * kTileF4;
         if (q0 + kTileF4 <= (n >> 2))
-            decompress_full_tile<WC, kAcc>(tab, W, lut, dtab, out, q0, lane, stage[wave]);
+            decompress_full_tile<WC, kAcc>(tab, W, lut, out, q0, lane, stage[wave]);
         else
-            decompress_tail_tile(tab, WC > 0 ? WC : W, lut, dtab, n, out, kAcc ? 1 : 0, q0,
-                                 lane);
+            decompress_tail_tile(tab, WC > 0 ? WC : W, lut, n, out, kAcc ? 1 : 0, q0, lane);
         if (!kLoop)
             break;
     }
@@ -343,21 +377,19 @@ __global__ __launch_bounds__(kThreads) void decompress_ternary_scalar_kernel(
     PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, int accumulate)
 {
     __shared__ float2 lut[16 * GC_MAX_WORKERS];
-    __shared__ uint32_t dtab[256];
-    build_digit_table(dtab);
-    build_nibble_table(lut, tab, W);
+    build_pair_table(lut, tab, W);
     const size_t stride = size_t(gridDim.x) * blockDim.x;
     for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
         const size_t byte_i = i / 5;
         const uint32_t k = uint32_t(i % 5);
-        const uint32_t shift = k < 2u ? 0u : (k < 4u ? 8u : 16u);
         float acc = 0.0f;
         for (int w = 0; w < W; ++w) {
             const uint8_t* bytes = reinterpret_cast<const uint8_t*>(tab.p[w] + 3);
-            const uint32_t off = (dtab[bytes[byte_i]] >> shift) & 0xFFu;
-            const float2 p = lut[16 * w + off / 8u];
-            const float d = (k & 1u) ? p.y : p.x;
-            acc = (w == 0) ? d : acc + d;
+            const Digits d = split_byte(bytes[byte_i]);
+            // digits 0, 1 in pair p0; 2, 3 in pair p1; 4 alone (entry 3 c4)
+            const float2 q = lut[16 * w + (k < 2u ? d.p0 : (k < 4u ? d.p1 : 3u * d.c4))];
+            const float v = (k & 1u) ? q.y : q.x;
+            acc = (w == 0) ? v : acc + v;
         }
         out[i] = accumulate ? out[i] + acc : acc;
     }
