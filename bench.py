@@ -154,6 +154,7 @@ def summarize_profiles(out_dir: str) -> None:
         "maxabs_partial_kernel": (4 * W3 * n3, 0),
         "qsgd_quantize_kernel": (4 * n3, n3),
         "qsgd_dequant_sum_kernel": (W3 * n3, 8 * n3),
+        "qsgd_quantize_sum_kernel": (4 * W3 * n3, 8 * n3),
     }
     cal_f = _read_counters(next((d / "pmc_cal_fetch").glob("*counter_collection.csv")))
     cal_w = _read_counters(next((d / "pmc_cal_write").glob("*counter_collection.csv")))
@@ -216,7 +217,8 @@ def summarize_profiles(out_dir: str) -> None:
               "the block (12 n + 4 (3 + ceil(n/16)), or 4 (3 + ceil(n/20)) for the ternary "
               "block); dequantize-sum reads W blocks and writes "
               "n fp32; max-norm reads W n fp32; quantize reads n fp32 and writes n int8; the "
-              "level sum reads W n int8 and writes n int32 + n fp32.", "",
+              "level sum reads W n int8 and writes n int32 + n fp32; the fused quantize-sum "
+              "reads W n fp32 and writes n int32 + n fp32.", "",
               "Machine-readable (bench.py reads these while the kernel sources are unchanged):",
               "", f"kernel_source_sha256: {kernel_source_hash()}", *machine, ""]
     PROFILE_TRAFFIC.write_text("\n".join(lines))
@@ -232,7 +234,7 @@ def summarize_profiles(out_dir: str) -> None:
         "",
         "The 2-bit step (8 x compress_2bit + decompress_2bit_sum W=8) runs 5 warm-up, 20 timed, "
         "20 kernel-timing and 20 graph-replayed steps; the QSGD-MN step runs 2 warm-up and 5 "
-        "timed steps.",
+        "timed steps, then 1 + 5 steps of its fused form (max-norm + qsgd_quantize_sum).",
         "",
         "| kernel | calls | average us | min us | max us | share of GPU time |",
         "|---|---|---|---|---|---|",
@@ -434,10 +436,39 @@ def bench_qsgd(gcq, torch, np, si, steps: int):
     mx = [e[0].elapsed_time(e[1]) for e in evs]
     qz = [e[1].elapsed_time(e[2]) for e in evs]
     ds = [e[2].elapsed_time(e[3]) for e in evs]
-    del grads, levels, sums, out
+    del levels
+
+    # the same step with the W quantizes and the level sum fused (no int8
+    # levels written): max-norm, then qsgd_quantize_sum
+    def fused_step(seed, ev):
+        ev[0].record()
+        gcq.qsgd_global_maxnorm(grads, norm, ws)
+        ev[1].record()
+        gcq.qsgd_quantize_sum(grads, norm, s, seed, out, sums=sums)
+        ev[2].record()
+
+    fused_step(0, [mk() for _ in range(3)])
+    torch.cuda.synchronize()
+    fevs = [[mk() for _ in range(3)] for _ in range(steps)]
+    log(f"qsgd: timing {steps} fused steps")
+    for k in range(steps):
+        fused_step(0, fevs[k])
+    torch.cuda.synchronize()
+    ftot = [e[0].elapsed_time(e[2]) for e in fevs]
+    fqs = [e[1].elapsed_time(e[2]) for e in fevs]
+    del grads, sums, out
     torch.cuda.empty_cache()
     mean = lambda v: sum(v) / len(v)  # noqa: E731
     t = mean(tot) / 1e3
+    fused = {
+        "workload": "the same step with qsgd_quantize_sum (W quantizes + level sum + dequantize "
+                    "in one pass; the int8 levels are not written)",
+        "ms_per_step": mean(ftot),
+        "elems_per_s": W * n / (mean(ftot) / 1e3),
+        "quantize_sum_ms": mean(fqs),
+        "quantize_sum_gbs": (4 * W + 8) * n / (mean(fqs) / 1e3) / 1e9,
+        "algorithmic_bytes": (4 * W + 4 * W + 8) * n,
+    }
     return {
         "elems_per_s": W * n / t,
         "ms_per_step": mean(tot),
@@ -449,6 +480,7 @@ def bench_qsgd(gcq, torch, np, si, steps: int):
                        "dequant_sum": (W + 8) * n / (mean(ds) / 1e3) / 1e9},
         "algorithmic_bytes": (4 * W + 5 * W + W + 8) * n,
         "steps": steps,
+        "fused": fused,
     }
 
 

@@ -13,7 +13,8 @@ Two method families (see include/gcq.h for exact semantics):
     byte: compress_ternary, decompress_ternary, decompress_ternary_sum;
   * QSGDMaxNorm stochastic quantization and GlobalRandK (vineeths96
     "Gradient-Compression"): qsgd_global_maxnorm, qsgd_maxnorm_quantize,
-    qsgd_dequant_sum, grandk_indices, gather_f32.
+    qsgd_dequant_sum, qsgd_quantize_sum (the W quantizes and the level sum fused),
+    grandk_indices, gather_f32.
 """
 from __future__ import annotations
 
@@ -83,6 +84,8 @@ def _declare(L):
                                         _vp, _vp]
     L.qsgd_dequant_sum.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _i, _vp, _vp, _vp, _sz,
                                    _vp]
+    L.qsgd_quantize_sum.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _i, ctypes.c_uint64,
+                                    _vp, _vp, _vp]
     L.grandk_indices.argtypes = [_sz, ctypes.c_uint32, ctypes.c_uint64, _vp, _vp,
                                  ctypes.POINTER(_sz), _vp]
     L.gather_f32.argtypes = [_vp, _vp, _sz, _vp, _vp]
@@ -90,6 +93,7 @@ def _declare(L):
                  "compress_ternary", "decompress_ternary", "decompress_ternary_sum",
                  "gc_plan_2bit_multi_create", "gc_plan_block_offsets", "compress_2bit_multi",
                  "qsgd_global_maxnorm", "qsgd_maxnorm_quantize", "qsgd_dequant_sum",
+                 "qsgd_quantize_sum",
                  "grandk_indices", "gather_f32"):
         getattr(L, name).restype = _i
     return L
@@ -340,6 +344,21 @@ def qsgd_dequant_sum(levels: Sequence, norm, s: int, out, sums=None, scatter_idx
 
 
 # ---- GlobalRandK ------------------------------------------------------------
+
+def qsgd_quantize_sum(grads: Sequence, norm, s: int, seed: int, out, sums=None,
+                      stream=None) -> None:
+    torch = _torch()
+    n = grads[0].numel()
+    if any(g.numel() != n for g in grads):
+        raise ValueError("qsgd_quantize_sum: gradients differ in size")
+    if out.numel() < n or (sums is not None and sums.numel() < n):
+        raise ValueError("qsgd_quantize_sum: out or sums too small")
+    arr = _ptr_array(grads, torch.float32, "grads")
+    _check(load().qsgd_quantize_sum(arr, len(grads), n, _dev(norm, torch.float32, "norm"),
+                                    int(s), int(seed) & (2 ** 64 - 1),
+                                    _dev(sums, torch.int32, "sums"),
+                                    _dev(out, torch.float32, "out"), _stream(stream)))
+
 
 def grandk_ws_bytes(n: int, K: int) -> int:
     size = _sz(0)

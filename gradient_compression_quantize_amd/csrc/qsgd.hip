@@ -369,6 +369,89 @@ __global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_kernel(
     }
 }
 
+// ---- fused quantize + level sum + dequantize --------------------------------
+//
+// The W quantizes and the dense level sum of one simulated step in a single
+// pass: a thread takes one float4 slot of every worker's gradient, draws that
+// worker's four Philox words (counter (q lo, q hi, w, 0), as in the quantize
+// kernel), forms the four levels with the same arithmetic and adds them into
+// int32 sums, then dequantizes. The int8 levels -- what each worker would put
+// on the wire -- are never written: a step reads 4 W n bytes and writes 8 n
+// (4 n without the sums) instead of 5 W n + W n + 8 n. WC > 0: W known at
+// compile time, all W loads in flight together and the W Philox chains
+// interleaved; WC == 0: groups of kFGroup workers.
+constexpr int kFGroup = 4;
+
+template <int WC>
+__global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_kernel(
+    PtrTable<float> tab, int W_rt, size_t n, const float* __restrict__ norm_ptr, float s24,
+    float s_f, uint32_t k0, uint32_t k1, int32_t* __restrict__ sums, float* __restrict__ out,
+    int vec)
+{
+    const int W = WC > 0 ? WC : W_rt;
+    const float norm = *norm_ptr;
+    const bool fast = norm >= 0x1p-120f;
+    const float inv = fast ? 1.0f / norm : 0.0f;
+    const size_t nslots = (n + 3) >> 2;
+    const size_t nfull = n >> 2;
+    const size_t stride = size_t(gridDim.x) * kThreads;
+    for (size_t q = size_t(blockIdx.x) * kThreads + threadIdx.x; q < nslots; q += stride) {
+        const U4 ctr0 = {uint32_t(q), uint32_t(q >> 32), 0u, 0u};
+        i32x4 S = {0, 0, 0, 0};
+        if (vec && q < nfull) {
+            constexpr int kG = WC > 0 ? WC : kFGroup;
+            for (int w0 = 0; w0 < W; w0 += kG) {
+                f32x4 g[kG];
+#pragma unroll
+                for (int dw = 0; dw < kG; ++dw)
+                    g[dw] = (WC == 0 && w0 + dw >= W)
+                                ? f32x4{0.0f, 0.0f, 0.0f, 0.0f}
+                                : __builtin_nontemporal_load(
+                                      reinterpret_cast<const f32x4*>(tab.p[w0 + dw]) + q);
+                if (norm != 0.0f) {
+                    U4 r[kG];
+#pragma unroll
+                    for (int dw = 0; dw < kG; ++dw)
+                        r[dw] = philox4x32_10(U4{ctr0.x, ctr0.y, uint32_t(w0 + dw), 0u}, k0, k1);
+#pragma unroll
+                    for (int dw = 0; dw < kG; ++dw) {
+                        if (WC == 0 && w0 + dw >= W)
+                            break;
+                        int lv[4];
+                        qsgd_levels4(g[dw], r[dw], norm, inv, s24, fast, lv);
+                        S += i32x4{lv[0], lv[1], lv[2], lv[3]};
+                    }
+                }
+            }
+            dequant_store(norm, s_f, S, sums, out, q);
+        } else {
+            // the partial slot, or buffers without the vector alignment
+#pragma unroll 1
+            for (int w = 0; w < W; ++w) {
+                f32x4 g;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    g[k] = (q * 4 + k < n) ? tab.p[w][q * 4 + k] : 0.0f;
+                if (norm != 0.0f) {
+                    int lv[4];
+                    qsgd_levels4(g, philox4x32_10(U4{ctr0.x, ctr0.y, uint32_t(w), 0u}, k0, k1),
+                                 norm, inv, s24, fast, lv);
+                    S += i32x4{lv[0], lv[1], lv[2], lv[3]};
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const size_t i = q * 4 + k;
+                if (i < n) {
+                    if (sums)
+                        sums[i] = S[k];
+                    out[i] = dequant(norm, S[k], s_f);
+                }
+            }
+        }
+    }
+}
+
 constexpr int kFillUnroll = 4;
 
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__ out, size_t n,
@@ -687,6 +770,58 @@ GCQ_API int qsgd_dequant_sum(const int8_t* const* levels, int W, size_t n, const
     hipLaunchKernelGGL(qsgd_dequant_scatter_kernel, dim3(grid_for(n)), dim3(kThreads), 0, stream,
                        tab, W, n, norm, s_f, sums, out, scatter_idx);
     return check_launch("qsgd_dequant_sum (scatter)");
+}
+
+GCQ_API int qsgd_quantize_sum(const float* const* grads, int W, size_t n, const float* norm,
+                              int s, uint64_t seed, int32_t* sums, float* out,
+                              hipStream_t stream)
+{
+    clear_error();
+    if (W < 1 || W > GC_MAX_WORKERS)
+        return fail(GC_EINVAL, "qsgd_quantize_sum: W must be in [1, 64]");
+    if (s < 1 || s > 127)
+        return fail(GC_EINVAL, "qsgd_quantize_sum: s must be in [1, 127]");
+    if (!grads || !norm || !aligned4(norm))
+        return fail(GC_EINVAL, "qsgd_quantize_sum: NULL or misaligned pointer");
+    if (n > 0 && !out)
+        return fail(GC_EINVAL, "qsgd_quantize_sum: out is NULL with n > 0");
+    if (!aligned4(out) || !aligned4(sums))
+        return fail(GC_EINVAL, "qsgd_quantize_sum: out and sums must be 4-byte aligned");
+    PtrTable<float> tab{};
+    bool g_aligned = true;
+    for (int w = 0; w < W; ++w) {
+        if (n > 0 && !grads[w])
+            return fail(GC_EINVAL, "qsgd_quantize_sum: a gradient pointer is NULL");
+        if (!aligned4(grads[w]))
+            return fail(GC_EINVAL, "qsgd_quantize_sum: gradients must be 4-byte aligned");
+        tab.p[w] = grads[w];
+        g_aligned = g_aligned && aligned16(grads[w]);
+    }
+    if (n == 0)
+        return GC_OK;
+    const int vec = (g_aligned && aligned16(out) && (!sums || aligned16(sums))) ? 1 : 0;
+    const dim3 grid(std::max<size_t>(1, std::min(ceil_div(ceil_div(n, 4), kThreads),
+                                                 max_grid_blocks()))),
+        block(kThreads);
+    const float s24 = float(s) * 16777216.0f;  // exact: s <= 127
+    const float s_f = float(s);
+    const uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
+    switch (W) {
+#define GCQ_QS_CASE(k)                                                                        \
+    case k:                                                                                   \
+        hipLaunchKernelGGL((qsgd_quantize_sum_kernel<k>), grid, block, 0, stream, tab, W, n, \
+                           norm, s24, s_f, k0, k1, sums, out, vec);                          \
+        break;
+        GCQ_QS_CASE(1)
+        GCQ_QS_CASE(2)
+        GCQ_QS_CASE(4)
+        GCQ_QS_CASE(8)
+#undef GCQ_QS_CASE
+    default:
+        hipLaunchKernelGGL((qsgd_quantize_sum_kernel<0>), grid, block, 0, stream, tab, W, n, norm,
+                           s24, s_f, k0, k1, sums, out, vec);
+    }
+    return check_launch("qsgd_quantize_sum");
 }
 
 GCQ_API int grandk_indices(size_t n, uint32_t K, uint64_t seed, uint32_t* idx, void* ws,

@@ -214,6 +214,20 @@ int qsgd_dequant_sum(const int8_t* const* levels, int W, size_t n,
                      const uint32_t* scatter_idx, size_t dense_n,
                      hipStream_t stream);
 
+/* The W quantizes and the dense level sum of one step in one pass, for a
+ * single device that simulates all W workers (the pages' all-reduce of
+ * levels, "About The Project"): sums and out are exactly those of
+ * qsgd_maxnorm_quantize on grads[w] with worker = w, for w = 0 .. W-1,
+ * followed by the dense qsgd_dequant_sum. The int8 levels themselves are
+ * not written, which saves their write and read-back (5 W n + W n bytes
+ * become 4 W n).
+ *   grads  HOST array of W device pointers, each [n] fp32
+ *   norm   device fp32 scalar (the shared max-norm);  s 1 .. 127
+ *   sums   [n] int32, or NULL;  out [n] fp32;  W 1 .. GC_MAX_WORKERS */
+int qsgd_quantize_sum(const float* const* grads, int W, size_t n,
+                      const float* norm, int s, uint64_t seed,
+                      int32_t* sums, float* out, hipStream_t stream);
+
 /* ---- GlobalRandK (vineeths96 page, "Results": K shared indices) -------- */
 
 /* The K indices every worker shares: the first K positions of a partial

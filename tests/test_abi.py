@@ -46,7 +46,7 @@ def test_header_declares_the_expected_entry_points():
                  "gc_plan_2bit_multi_create", "gc_plan_destroy", "gc_compressed_2bit_words",
                  "gc_plan_compressed_words", "gc_plan_block_offsets", "gc_last_error",
                  "gc_compressed_ternary_words", "compress_ternary", "decompress_ternary",
-                 "decompress_ternary_sum"):
+                 "decompress_ternary_sum", "qsgd_quantize_sum"):
         assert must in names, must
 
 
@@ -133,6 +133,22 @@ def test_qsgd_rejects_bad_arguments(lib):
     assert lib.qsgd_dequant_sum(arr, 2, 16, FAKE, 0, NULL, FAKE, NULL, 0, None) == gcq.GC_EINVAL
     # more scattered values than the dense output holds
     assert lib.qsgd_dequant_sum(arr, 2, 16, FAKE, 7, NULL, FAKE, FAKE, 8, None) == gcq.GC_EINVAL
+
+
+def test_quantize_sum_rejects_bad_arguments(lib):
+    arr = (ctypes.c_void_p * 65)(*([FAKE] * 65))
+    for W in (0, 65):
+        assert lib.qsgd_quantize_sum(arr, W, 16, FAKE, 7, 0, NULL, FAKE, None) == gcq.GC_EINVAL
+    for s in (0, 128):
+        assert lib.qsgd_quantize_sum(arr, 2, 16, FAKE, s, 0, NULL, FAKE, None) == gcq.GC_EINVAL
+    assert lib.qsgd_quantize_sum(arr, 2, 16, NULL, 7, 0, NULL, FAKE, None) == gcq.GC_EINVAL
+    assert lib.qsgd_quantize_sum(arr, 2, 16, FAKE, 7, 0, NULL, NULL, None) == gcq.GC_EINVAL
+    assert lib.qsgd_quantize_sum(arr, 2, 16, FAKE, 7, 0, FAKE + 2, FAKE, None) == gcq.GC_EINVAL
+    arr[1] = FAKE + 2
+    assert lib.qsgd_quantize_sum(arr, 2, 16, FAKE, 7, 0, NULL, FAKE, None) == gcq.GC_EINVAL
+    arr[1] = None
+    assert lib.qsgd_quantize_sum(arr, 2, 16, FAKE, 7, 0, NULL, FAKE, None) == gcq.GC_EINVAL
+    assert b"qsgd_quantize_sum" in lib.gc_last_error()
 
 
 def test_workspace_queries(lib):

@@ -111,6 +111,28 @@ def test_qsgd_step_random(gcq, W, n, s, scale, misalign, seed):
 
 
 @SETTINGS
+@given(W=st.integers(1, 10), n=st.integers(1, 30_000), s=st.integers(1, 127),
+       scale=st.sampled_from([1e-3, 0.02, 1.0, 50.0]), misalign=st.booleans(),
+       with_sums=st.booleans(), seed=st.integers(0, 2 ** 63 - 1))
+def test_qsgd_fused_random(gcq, W, n, s, scale, misalign, with_sums, seed):
+    announce(f"prop qsgd fused W={W} n={n} s={s} scale={scale} mis={misalign} sums={with_sums} seed={seed}")
+    grads = [si.heavy_tailed_f32((seed + 3 * w) % (2 ** 32), n, scale) for w in range(W)]
+    g_dev = [gu.dev(g, misalign) for g in grads]
+    norm = torch.empty(1, dtype=torch.float32, device=gu.DEV)
+    ws = torch.empty(gcq.qsgd_maxnorm_ws_bytes(W, n), dtype=torch.uint8, device=gu.DEV)
+    gcq.qsgd_global_maxnorm(g_dev, norm, ws)
+    sums = gu.empty(n, torch.int32, misalign=misalign) if with_sums else None
+    out = gu.empty(n, torch.float32, misalign=not misalign)
+    gcq.qsgd_quantize_sum(g_dev, norm, s, seed, out, sums=sums)
+    gu.sync()
+    norm_or = oracle.maxnorm(grads)
+    s_or = oracle.level_sum([oracle.qsgd_quantize(g, norm_or, s, seed, w) for w, g in enumerate(grads)])
+    if with_sums:
+        np.testing.assert_array_equal(gu.host(sums), s_or)
+    np.testing.assert_array_equal(gu.host(out), oracle.qsgd_dequantize(s_or, norm_or, s))
+
+
+@SETTINGS
 @given(n=st.integers(1, 200_000), frac=st.floats(0.0, 1.0), seed=st.integers(0, 2 ** 63 - 1))
 def test_grandk_indices_random(gcq, n, frac, seed):
     K = min(n, int(frac * min(n, 30_000)))
