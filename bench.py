@@ -648,8 +648,34 @@ def bench_grandk(gcq, torch, np, si, steps: int):
         graph.replay()
     t1.record()
     torch.cuda.synchronize()
+    sep_graph = t0.elapsed_time(t1) / steps
+    del graph
+
+    # the same step through grandk_mn_step: three launches
+    sws = torch.empty(gcq.grandk_mn_step_ws_bytes(W, n, K), dtype=torch.uint8, device=dev)
+
+    def one_call(seed):
+        gcq.grandk_mn_step(grads, K, seed, s, idx, dense, sws, sums=sums, norm=norm)
+
+    for k in range(3):
+        one_call(k)
+    torch.cuda.synchronize()
+    t0, t1 = mk(), mk()
+    t0.record()
+    for k in range(steps):
+        one_call(k)
+    t1.record()
+    torch.cuda.synchronize()
+    one_eager = t0.elapsed_time(t1) / steps
+    graph = graph_of(torch, lambda: one_call(0))
+    t0, t1 = mk(), mk()
+    t0.record()
+    for _ in range(steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
     tot = t0.elapsed_time(t1) / steps
-    del graph, grads, dense
+    del graph, grads, dense, sws
     torch.cuda.empty_cache()
     c0 = time.perf_counter()
     idx_h = oracle.randk_indices(n, K, 0)
@@ -661,11 +687,16 @@ def bench_grandk(gcq, torch, np, si, steps: int):
     dense_gbs = 4 * n / (fill / 1e3) / 1e9
     return {"workload": f"GRandK-MN: n={n:,}, K={K}, W={W}, s={s}: shared index draw, gather, "
                         "max-norm, quantize, level sum, scatter into a dense fp32 buffer",
-            "ms_per_step": tot, "values_per_s": K * W / (tot / 1e3),
-            "timing": "HIP graph replay of the whole step; stages from an eager pass",
-            "ms_per_step_eager": eager,
-            "stages_ms": {"index_draw": draw, "gather_norm_quantize": mid,
-                          "sum_fill_scatter": fill},
+            "ms_per_step": one_eager, "values_per_s": K * W / (one_eager / 1e3),
+            "timing": "grandk_mn_step (three launches), K steps back to back between two "
+                      "events; graph_ms_per_step replays it from a HIP graph",
+            "graph_ms_per_step": tot,
+            "separate_calls": {
+                "timing": "the 20 separate calls (draw, W gathers, max-norm, W quantizes, "
+                          "dequantize-scatter): HIP graph replay; stages from an eager pass",
+                "ms_per_step": sep_graph, "ms_per_step_eager": eager,
+                "stages_ms": {"index_draw": draw, "gather_norm_quantize": mid,
+                              "sum_fill_scatter": fill}},
             "roofline": {"bound": "hbm", "kernel": "fill_zero + scatter (dense output)",
                          "achieved": round(dense_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(dense_gbs / HBM_PEAK_GBS, 4)},

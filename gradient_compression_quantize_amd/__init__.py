@@ -14,7 +14,7 @@ Two method families (see include/gcq.h for exact semantics):
   * QSGDMaxNorm stochastic quantization and GlobalRandK (vineeths96
     "Gradient-Compression"): qsgd_global_maxnorm, qsgd_maxnorm_quantize,
     qsgd_dequant_sum, qsgd_quantize_sum (the W quantizes and the level sum fused),
-    grandk_indices, gather_f32.
+    grandk_indices, gather_f32, and grandk_mn_step (the whole GRandK-MN step).
 """
 from __future__ import annotations
 
@@ -89,12 +89,14 @@ def _declare(L):
     L.grandk_indices.argtypes = [_sz, ctypes.c_uint32, ctypes.c_uint64, _vp, _vp,
                                  ctypes.POINTER(_sz), _vp]
     L.gather_f32.argtypes = [_vp, _vp, _sz, _vp, _vp]
+    L.grandk_mn_step.argtypes = [ctypes.POINTER(_vp), _i, _sz, ctypes.c_uint32, ctypes.c_uint64,
+                                 _i, _vp, _vp, _vp, _vp, _vp, ctypes.POINTER(_sz), _vp]
     for name in ("compress_2bit", "decompress_2bit", "decompress_2bit_sum",
                  "compress_ternary", "decompress_ternary", "decompress_ternary_sum",
                  "gc_plan_2bit_multi_create", "gc_plan_block_offsets", "compress_2bit_multi",
                  "qsgd_global_maxnorm", "qsgd_maxnorm_quantize", "qsgd_dequant_sum",
                  "qsgd_quantize_sum",
-                 "grandk_indices", "gather_f32"):
+                 "grandk_indices", "gather_f32", "grandk_mn_step"):
         getattr(L, name).restype = _i
     return L
 
@@ -385,3 +387,28 @@ def gather_f32(x, idx, out, stream=None) -> None:
         raise ValueError("gather_f32: out too small")
     _check(load().gather_f32(_dev(x, torch.float32, "x"), _dev(idx, torch.int32, "idx"), K,
                              _dev(out, torch.float32, "out"), _stream(stream)))
+
+
+def grandk_mn_step_ws_bytes(W: int, n: int, K: int) -> int:
+    size = _sz(0)
+    arr = (_vp * W)()
+    _check(load().grandk_mn_step(arr, W, n, K, 0, 7, None, None, None, None, None,
+                                 ctypes.byref(size), None))
+    return size.value
+
+
+def grandk_mn_step(grads: Sequence, K: int, seed: int, s: int, idx, dense, ws, sums=None,
+                   norm=None, stream=None) -> None:
+    torch = _torch()
+    n = grads[0].numel()
+    if any(g.numel() != n for g in grads):
+        raise ValueError("grandk_mn_step: gradients differ in size")
+    if idx.numel() < K or dense.numel() < n or (sums is not None and sums.numel() < K):
+        raise ValueError("grandk_mn_step: idx, sums or dense too small")
+    arr = _ptr_array(grads, torch.float32, "grads")
+    size = _sz(ws.numel() * ws.element_size())
+    _check(load().grandk_mn_step(arr, len(grads), n, K, int(seed) & (2 ** 64 - 1), int(s),
+                                 _dev(idx, torch.int32, "idx"), _dev(sums, torch.int32, "sums"),
+                                 _dev(dense, torch.float32, "dense"),
+                                 _dev(norm, torch.float32, "norm"), _dev(ws, torch.uint8, "ws"),
+                                 ctypes.byref(size), _stream(stream)))

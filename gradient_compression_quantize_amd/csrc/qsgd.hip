@@ -454,21 +454,25 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_kernel(
 
 constexpr int kFillUnroll = 4;
 
-__global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__ out, size_t n,
-                                                             int vec)
+// Zero out[0, n) with workgroups b = 0 .. nb-1 (of NT threads) of a launch:
+// lane-contiguous non-temporal float4 stores when out is 16-byte aligned
+// (vec), scalar stores otherwise.
+template <int NT = kThreads>
+__device__ __forceinline__ void fill_zero_range(float* __restrict__ out, size_t n, int vec,
+                                                size_t b, size_t nb)
 {
-    const size_t stride = size_t(gridDim.x) * kThreads;
-    const size_t tid = size_t(blockIdx.x) * kThreads + threadIdx.x;
+    const size_t stride = nb * NT;
+    const size_t tid = b * NT + threadIdx.x;
     if (vec) {
         const size_t nfull = n >> 2;
         f32x4* o4 = reinterpret_cast<f32x4*>(out);
         const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-        // blocks of kFillUnroll * kThreads float4, lane-contiguous
-        const size_t per = size_t(kFillUnroll) * kThreads;
-        for (size_t b = size_t(blockIdx.x) * per; b < nfull; b += size_t(gridDim.x) * per) {
+        // blocks of kFillUnroll * NT float4, lane-contiguous
+        const size_t per = size_t(kFillUnroll) * NT;
+        for (size_t c = b * per; c < nfull; c += nb * per) {
 #pragma unroll
             for (int u = 0; u < kFillUnroll; ++u) {
-                const size_t q = b + size_t(u) * kThreads + threadIdx.x;
+                const size_t q = c + size_t(u) * NT + threadIdx.x;
                 if (q < nfull)
                     __builtin_nontemporal_store(z, o4 + q);
             }
@@ -479,6 +483,12 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__
         for (size_t i = tid; i < n; i += stride)
             out[i] = 0.0f;
     }
+}
+
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__ out, size_t n,
+                                                             int vec)
+{
+    fill_zero_range(out, n, vec, blockIdx.x, gridDim.x);
 }
 
 // Sparse form: value k lands at out[idx[k]] (out already zeroed).
@@ -565,8 +575,9 @@ __global__ __launch_bounds__(kRandKThreads) void grandk_indices_kernel(
 constexpr uint32_t kRandKLdsMax = 16384;
 constexpr int kRandKLdsHeadBits = 13;
 
-__global__ __launch_bounds__(kRandKThreads) void grandk_indices_lds_kernel(
-    size_t n, uint32_t K, uint32_t k0, uint32_t k1, uint32_t* __restrict__ idx, int hbits)
+// The LDS draw by one workgroup of kRandKThreads threads.
+__device__ __forceinline__ void grandk_draw_lds(size_t n, uint32_t K, uint32_t k0, uint32_t k1,
+                                                uint32_t* __restrict__ idx, int hbits)
 {
     __shared__ uint32_t target[kRandKLdsMax];
     __shared__ int16_t next[kRandKLdsMax];
@@ -600,6 +611,12 @@ __global__ __launch_bounds__(kRandKThreads) void grandk_indices_lds_kernel(
     }
 }
 
+__global__ __launch_bounds__(kRandKThreads) void grandk_indices_lds_kernel(
+    size_t n, uint32_t K, uint32_t k0, uint32_t k1, uint32_t* __restrict__ idx, int hbits)
+{
+    grandk_draw_lds(n, K, k0, k1, idx, hbits);
+}
+
 int randk_lds_hash_bits(uint32_t K)
 {
     int b = 6;
@@ -628,6 +645,154 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const float* __restric
     const size_t stride = size_t(gridDim.x) * kThreads;
     for (size_t k = size_t(blockIdx.x) * kThreads + threadIdx.x; k < K; k += stride)
         out[k] = x[idx[k]];
+}
+
+// ---- the whole GlobalRandK-MN step ------------------------------------------
+//
+// Three launches instead of one per worker per stage. Launch 1 is the index
+// draw above, with the dense zero fill beside it when the draw runs in LDS.
+// Launch 2: its first workgroups gather g_w[idx[k]] of every worker into the
+// workspace (worker w at offset w * Kp, Kp = K rounded up to a multiple of 4)
+// and write one partial max |g| each; any remaining workgroups zero the
+// dense output (when launch 1 could not). Launch 3: every workgroup reduces the
+// same partials to the shared norm (the max is exact and order-free), then
+// takes float4 slots of the gathered values: for each worker the Philox
+// words of (slot, worker, 0) and the levels, exactly as
+// qsgd_maxnorm_quantize computes them on the gathered array; the int32 sum
+// of the W levels; its dequantized value, scattered to dense[idx[k]].
+constexpr unsigned kGkMaxGatherBlocks = 1024;
+constexpr int kGkQThreads = 64;
+
+// Launch 1 when K <= kRandKLdsMax: workgroup 0 draws the indices in LDS
+// while the others zero the dense output. The draw's 128 KB of LDS holds
+// every workgroup of the launch to one per CU, which at 1024 threads still
+// gives the fill 16 waves per CU.
+__global__ __launch_bounds__(kRandKThreads) void grandk_draw_fill_kernel(
+    size_t n, uint32_t K, uint32_t k0, uint32_t k1, uint32_t* __restrict__ idx, int hbits,
+    float* __restrict__ dense, int dense_vec)
+{
+    if (blockIdx.x == 0) {
+        if (K > 0)
+            grandk_draw_lds(n, K, k0, k1, idx, hbits);
+        return;
+    }
+    fill_zero_range<kRandKThreads>(dense, n, dense_vec, blockIdx.x - 1, gridDim.x - 1);
+}
+
+__global__ __launch_bounds__(kThreads) void grandk_gather_fill_kernel(
+    PtrTable<float> tab, int W, uint32_t K, size_t Kp, const uint32_t* __restrict__ idx,
+    float* __restrict__ gathered, float* __restrict__ partials, unsigned gather_blocks,
+    float* __restrict__ dense, size_t n, int dense_vec)
+{
+    if (blockIdx.x >= gather_blocks) {
+        fill_zero_range(dense, n, dense_vec, blockIdx.x - gather_blocks,
+                        gridDim.x - gather_blocks);
+        return;
+    }
+    const size_t total = size_t(W) * K;
+    float m = 0.0f;
+    for (size_t e = size_t(blockIdx.x) * kThreads + threadIdx.x; e < total;
+         e += size_t(gather_blocks) * kThreads) {
+        const size_t w = e / K, k = e % K;
+        const float v = tab.p[w][idx[k]];
+        gathered[w * Kp + k] = v;
+        m = fmaxf(m, fabsf(v));
+    }
+    m = block_max<kThreads>(m);
+    if (threadIdx.x == 0)
+        partials[blockIdx.x] = m;
+}
+
+template <int WC>
+__global__ __launch_bounds__(kGkQThreads) void grandk_quantize_scatter_kernel(
+    int W_rt, uint32_t K, size_t Kp, const float* __restrict__ gathered,
+    const float* __restrict__ partials, unsigned nparts, float s24, float s_f, uint32_t k0,
+    uint32_t k1, const uint32_t* __restrict__ idx, int32_t* __restrict__ sums,
+    float* __restrict__ dense, float* __restrict__ norm_out)
+{
+    __shared__ float norm_sh;
+    float m = 0.0f;
+    for (unsigned i = threadIdx.x; i < nparts; i += kGkQThreads)
+        m = fmaxf(m, partials[i]);
+    m = block_max<kGkQThreads>(m);
+    if (threadIdx.x == 0) {
+        norm_sh = m;
+        if (blockIdx.x == 0 && norm_out)
+            *norm_out = m;
+    }
+    __syncthreads();
+    const float norm = norm_sh;
+    const int W = WC > 0 ? WC : W_rt;
+    const bool fast = norm >= 0x1p-120f;
+    const float inv = fast ? 1.0f / norm : 0.0f;
+    const size_t nslots = (size_t(K) + 3) >> 2;
+    for (size_t q = size_t(blockIdx.x) * kGkQThreads + threadIdx.x; q < nslots;
+         q += size_t(gridDim.x) * kGkQThreads) {
+        i32x4 S = {0, 0, 0, 0};
+        if (norm != 0.0f) {
+            constexpr int kG = WC > 0 ? WC : kFGroup;
+            for (int w0 = 0; w0 < W; w0 += kG) {
+                f32x4 g[kG];
+                U4 r[kG];
+#pragma unroll
+                for (int dw = 0; dw < kG; ++dw) {
+                    g[dw] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    if (WC > 0 || w0 + dw < W) {
+                        g[dw] = reinterpret_cast<const f32x4*>(gathered +
+                                                               size_t(w0 + dw) * Kp)[q];
+                        // the padding past K holds no value: level 0, as in
+                        // the quantize kernel's partial slot
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            if (q * 4 + k >= K)
+                                g[dw][k] = 0.0f;
+                    }
+                    r[dw] = philox4x32_10(U4{uint32_t(q), uint32_t(q >> 32), uint32_t(w0 + dw), 0u},
+                                          k0, k1);
+                }
+#pragma unroll
+                for (int dw = 0; dw < kG; ++dw) {
+                    if (WC == 0 && w0 + dw >= W)
+                        break;
+                    int lv[4];
+                    qsgd_levels4(g[dw], r[dw], norm, inv, s24, fast, lv);
+                    S += i32x4{lv[0], lv[1], lv[2], lv[3]};
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const size_t i = q * 4 + k;
+            if (i < K) {
+                if (sums)
+                    sums[i] = S[k];
+                dense[idx[i]] = dequant(norm, S[k], s_f);
+            }
+        }
+    }
+}
+
+struct GrandkStepLayout {
+    size_t Kp, gathered_off, partials_off, draw_off, total;
+    unsigned gather_blocks;
+};
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+GrandkStepLayout grandk_step_layout(int W, uint32_t K)
+{
+    GrandkStepLayout L{};
+    L.Kp = (size_t(K) + 3) & ~size_t(3);
+    const size_t total = size_t(W) * K;
+    // at most half of the launch cap, so that the fill keeps workgroups too
+    L.gather_blocks = unsigned(std::max<size_t>(
+        1, std::min<size_t>({ceil_div(total, kThreads), size_t(kGkMaxGatherBlocks),
+                             max_grid_blocks() / 2})));
+    L.gathered_off = 0;
+    L.partials_off = align256(size_t(W) * L.Kp * 4);
+    L.draw_off = L.partials_off + align256(size_t(L.gather_blocks) * 4);
+    L.total = L.draw_off + (K > kRandKLdsMax ? align256(randk_ws_bytes(K)) : 0);
+    return L;
 }
 
 size_t grid_for(size_t items)
@@ -872,4 +1037,96 @@ GCQ_API int gather_f32(const float* x, const uint32_t* idx, size_t K, float* out
     hipLaunchKernelGGL(gather_kernel, dim3(grid_for(K)), dim3(kThreads), 0, stream, x, idx, K,
                        out);
     return check_launch("gather_f32");
+}
+
+GCQ_API int grandk_mn_step(const float* const* grads, int W, size_t n, uint32_t K,
+                           uint64_t seed, int s, uint32_t* idx, int32_t* sums, float* dense,
+                           float* norm, void* ws, size_t* ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (!ws_bytes)
+        return fail(GC_EINVAL, "grandk_mn_step: ws_bytes is NULL");
+    if (W < 1 || W > GC_MAX_WORKERS)
+        return fail(GC_EINVAL, "grandk_mn_step: W must be in [1, 64]");
+    if (s < 1 || s > 127)
+        return fail(GC_EINVAL, "grandk_mn_step: s must be in [1, 127]");
+    if (n < 1 || n > (size_t(1) << 32) || size_t(K) > n)
+        return fail(GC_EINVAL, "grandk_mn_step: need 1 <= n <= 2^32 and K <= n");
+    if (K > (1u << 30))
+        return fail(GC_EUNSUPPORTED, "grandk_mn_step: K above 2^30");
+    const GrandkStepLayout L = grandk_step_layout(W, K);
+    if (!ws) {
+        *ws_bytes = L.total;
+        return GC_OK;
+    }
+    if (*ws_bytes < L.total || !aligned16(ws))
+        return fail(GC_EINVAL, "grandk_mn_step: workspace too small or not 16-byte aligned");
+    if (!grads || !dense || !aligned4(dense) || !aligned4(sums) || !aligned4(norm))
+        return fail(GC_EINVAL, "grandk_mn_step: NULL or misaligned pointer");
+    if (K > 0 && (!idx || !aligned4(idx)))
+        return fail(GC_EINVAL, "grandk_mn_step: idx is NULL or misaligned");
+    PtrTable<float> tab{};
+    for (int w = 0; w < W; ++w) {
+        if (!grads[w] || !aligned4(grads[w]))
+            return fail(GC_EINVAL, "grandk_mn_step: a gradient pointer is NULL or misaligned");
+        tab.p[w] = grads[w];
+    }
+    char* base = static_cast<char*>(ws);
+    float* gathered = reinterpret_cast<float*>(base + L.gathered_off);
+    float* partials = reinterpret_cast<float*>(base + L.partials_off);
+    const uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
+    const size_t cap = max_grid_blocks();
+    const int dense_vec = aligned16(dense) ? 1 : 0;
+    // launch 1: the shared index draw; with the draw in LDS, the dense zero
+    // fill runs beside it in the same launch
+    size_t fill_blocks = 0;  // fill workgroups left for launch 2
+    if (K <= kRandKLdsMax) {
+        const size_t fb = std::max<size_t>(
+            1, std::min(ceil_div(ceil_div(n, 4 * kFillUnroll), kRandKThreads),
+                        cap > 1 ? cap - 1 : 1));
+        hipLaunchKernelGGL(grandk_draw_fill_kernel, dim3(unsigned(1 + fb)), dim3(kRandKThreads),
+                           0, stream, n, K, k0, k1, idx, randk_lds_hash_bits(K), dense,
+                           dense_vec);
+    } else {
+        const int hbits = randk_hash_bits(K);
+        int32_t* heads = reinterpret_cast<int32_t*>(base + L.draw_off);
+        uint32_t* target = reinterpret_cast<uint32_t*>(heads + (size_t(1) << hbits));
+        int32_t* next = reinterpret_cast<int32_t*>(target + K);
+        hipLaunchKernelGGL(grandk_indices_kernel, dim3(1), dim3(kRandKThreads), 0, stream, n, K,
+                           k0, k1, idx, target, next, heads, hbits);
+        fill_blocks = std::max<size_t>(
+            1, std::min(ceil_div(ceil_div(n, 4 * kFillUnroll), kThreads),
+                        cap > L.gather_blocks ? cap - L.gather_blocks : 1));
+    }
+    if (int rc = check_launch("grandk_mn_step (draw)"))
+        return rc;
+    // launch 2: gathers and partial maxima (and the fill, if not done above)
+    hipLaunchKernelGGL(grandk_gather_fill_kernel, dim3(unsigned(L.gather_blocks + fill_blocks)),
+                       dim3(kThreads), 0, stream, tab, W, K, L.Kp, idx, gathered, partials,
+                       L.gather_blocks, dense, n, dense_vec);
+    if (int rc = check_launch("grandk_mn_step (gather, fill)"))
+        return rc;
+    // launch 3: norm, levels, sum, dequantize, scatter
+    const size_t qblocks = std::max<size_t>(
+        1, std::min(ceil_div(ceil_div(size_t(K), 4), kGkQThreads), max_grid_blocks()));
+    const float s24 = float(s) * 16777216.0f;  // exact: s <= 127
+    const float s_f = float(s);
+    switch (W) {
+#define GCQ_GK_CASE(c)                                                                          \
+    case c:                                                                                     \
+        hipLaunchKernelGGL((grandk_quantize_scatter_kernel<c>), dim3(unsigned(qblocks)),        \
+                           dim3(kGkQThreads), 0, stream, W, K, L.Kp, gathered, partials,        \
+                           L.gather_blocks, s24, s_f, k0, k1, idx, sums, dense, norm);          \
+        break;
+        GCQ_GK_CASE(1)
+        GCQ_GK_CASE(2)
+        GCQ_GK_CASE(4)
+        GCQ_GK_CASE(8)
+#undef GCQ_GK_CASE
+    default:
+        hipLaunchKernelGGL((grandk_quantize_scatter_kernel<0>), dim3(unsigned(qblocks)),
+                           dim3(kGkQThreads), 0, stream, W, K, L.Kp, gathered, partials,
+                           L.gather_blocks, s24, s_f, k0, k1, idx, sums, dense, norm);
+    }
+    return check_launch("grandk_mn_step (quantize, scatter)");
 }

@@ -244,6 +244,27 @@ int grandk_indices(size_t n, uint32_t K, uint64_t seed, uint32_t* idx,
 int gather_f32(const float* x, const uint32_t* idx, size_t K, float* out,
                hipStream_t stream);
 
+/* The whole GlobalRandK-MN step of [QMN] "Results" for W simulated workers,
+ * in three launches instead of one per worker per stage. The results are
+ * exactly those of the separate calls:
+ *   grandk_indices(n, K, seed)            -> idx
+ *   gather_f32(grads[w], idx) for each w  -> g_w (length K)
+ *   qsgd_global_maxnorm(g_0 .. g_{W-1})   -> norm
+ *   qsgd_maxnorm_quantize(g_w, norm, s, seed, worker = w) for each w
+ *   qsgd_dequant_sum(levels, norm, s, dense, sums, scatter_idx = idx, n)
+ * (one seed serves the draw and the rounding, as in those calls).
+ *   grads  HOST array of W device pointers, each [n] fp32
+ *   idx    [K] uint32 out;  sums [K] int32 out, or NULL
+ *   dense  [n] fp32 out: 0 outside idx, the dequantized sum at idx[k]
+ *   norm   device fp32 scalar out (the shared max-norm), or NULL
+ *   ws     16-byte-aligned workspace; ws == NULL: *ws_bytes = its size
+ *          (about 4 W K bytes), else *ws_bytes must be at least that
+ *   1 <= n <= 2^32, K <= n, K <= 2^30, s 1 .. 127, W 1 .. GC_MAX_WORKERS */
+int grandk_mn_step(const float* const* grads, int W, size_t n, uint32_t K,
+                   uint64_t seed, int s, uint32_t* idx, int32_t* sums,
+                   float* dense, float* norm, void* ws, size_t* ws_bytes,
+                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

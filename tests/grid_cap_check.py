@@ -135,6 +135,25 @@ def main():
     check(np.array_equal(gu.host(dense),
                          oracle.scatter_dense(oracle.qsgd_dequantize(sk, norm_or, s), idx, n)),
           "scatter-dequantize")
+    # the one-call GRandK step: one gather workgroup striding, a capped fill
+    print("[case] capped grandk_mn_step", flush=True)
+    n, K, W, s, seed = 200_003, 7_001, 8, 7, 9
+    gs = [si.normal_f32(500 + w, n, 0.01) for w in range(W)]
+    g_dev = [gu.dev(g) for g in gs]
+    idx = gu.empty(K, torch.int32)
+    sums = gu.empty(K, torch.int32)
+    dense = gu.empty(n, torch.float32, fill=float("nan"))
+    ws = torch.empty(gcq.grandk_mn_step_ws_bytes(W, n, K), dtype=torch.uint8, device=gu.DEV)
+    gcq.grandk_mn_step(g_dev, K, seed, s, idx, dense, ws, sums=sums)
+    gu.sync()
+    idx_or = oracle.randk_indices(n, K, seed)
+    gk = [oracle.gather(g, idx_or) for g in gs]
+    nrm = oracle.maxnorm(gk)
+    S = oracle.level_sum([oracle.qsgd_quantize(g, nrm, s, seed, w) for w, g in enumerate(gk)])
+    check(np.array_equal(gu.host(idx, np.uint32), idx_or), "grandk_mn_step indices")
+    check(np.array_equal(gu.host(sums), S), "grandk_mn_step sums")
+    check(np.array_equal(gu.host(dense), oracle.scatter_dense(oracle.qsgd_dequantize(S, nrm, s), idx_or, n)),
+          "grandk_mn_step dense")
     print("OK", flush=True)
 
 

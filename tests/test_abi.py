@@ -46,7 +46,7 @@ def test_header_declares_the_expected_entry_points():
                  "gc_plan_2bit_multi_create", "gc_plan_destroy", "gc_compressed_2bit_words",
                  "gc_plan_compressed_words", "gc_plan_block_offsets", "gc_last_error",
                  "gc_compressed_ternary_words", "compress_ternary", "decompress_ternary",
-                 "decompress_ternary_sum", "qsgd_quantize_sum"):
+                 "decompress_ternary_sum", "qsgd_quantize_sum", "grandk_mn_step"):
         assert must in names, must
 
 
@@ -163,6 +163,29 @@ def test_workspace_queries(lib):
     assert size.value == 4 * (32768 + 2 * 10_000)
     assert lib.grandk_indices(10, 11, 0, None, None, ctypes.byref(size), None) == gcq.GC_EINVAL
     assert lib.grandk_indices(2 ** 32 + 1, 1, 0, None, None, ctypes.byref(size), None) == gcq.GC_EINVAL
+
+
+def test_grandk_mn_step_workspace_and_validation(lib):
+    size = ctypes.c_size_t(0)
+    arr = (ctypes.c_void_p * 64)(*([FAKE] * 64))
+    assert lib.grandk_mn_step(arr, 8, 25_557_032, 10_000, 0, 7, None, None, None, None, None,
+                              ctypes.byref(size), None) == 0
+    # gathered values (8 x 10000 fp32) + partial maxima; the draw uses LDS
+    assert 8 * 10_000 * 4 <= size.value <= 8 * 10_000 * 4 + 8192
+    big = ctypes.c_size_t(0)
+    assert lib.grandk_mn_step(arr, 2, 10 ** 6, 20_000, 0, 7, None, None, None, None, None,
+                              ctypes.byref(big), None) == 0
+    assert big.value >= 2 * 20_000 * 4 + 4 * (65536 + 2 * 20_000)
+    bad = [(0, 100, 10, 7), (65, 100, 10, 7), (2, 100, 101, 7), (2, 0, 0, 7), (2, 100, 10, 0),
+           (2, 100, 10, 128), (2, 2 ** 32 + 1, 10, 7)]
+    for W, n, K, s in bad:
+        assert lib.grandk_mn_step(arr, W, n, K, 0, s, None, None, None, None, None,
+                                  ctypes.byref(size), None) == gcq.GC_EINVAL, (W, n, K, s)
+    small = ctypes.c_size_t(16)
+    assert lib.grandk_mn_step(arr, 2, 100, 10, 0, 7, FAKE, NULL, FAKE, NULL, FAKE,
+                              ctypes.byref(small), None) == gcq.GC_EINVAL
+    assert lib.grandk_mn_step(arr, 2, 100, 10, 0, 7, FAKE, NULL, FAKE, NULL, NULL, NULL,
+                              None) == gcq.GC_EINVAL
 
 
 def test_plan_rejects_bad_arguments(lib):
