@@ -47,6 +47,7 @@ SIGMA_C3 = 0.02
 PROFILE_TRAFFIC = ROOT / "profiles" / "hbm_traffic_resnet50_vgg16.md"
 PROFILE_STATS = ROOT / "profiles" / "kernel_stats_resnet50_vgg16.md"
 PROFILE_STATS_EXTRA = ROOT / "profiles" / "kernel_stats_bert_multitensor_grandk_ternary.md"
+PROFILE_VALU = ROOT / "profiles" / "valu_busy_all_workloads.md"
 KERNEL_SOURCES = [ROOT / "gradient_compression_quantize_amd" / "csrc" / f
                   for f in ("gcq_internal.h", "threshold_codes.h", "twobit.hip", "ternary.hip",
                             "qsgd.hip")]
@@ -69,6 +70,11 @@ PROFILE_COMMANDS = {
                    "--output-format csv -- python3 -u bench.py --extras-only --extra-steps 3",
     "write_extra": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_write_extra -o write "
                    "--output-format csv -- python3 -u bench.py --extras-only --extra-steps 3",
+    "valu": "rocprofv3 --pmc VALUBusy SQ_INSTS_VALU SQ_INSTS_LDS -T -d gpurun_out/pmc_valu -o valu "
+            "--output-format csv -- python3 -u bench.py --steps 3 --warmup 1 --qsgd-steps 1 "
+            "--skip-cpu-baseline --skip-extra",
+    "valu_extra": "rocprofv3 --pmc VALUBusy SQ_INSTS_VALU SQ_INSTS_LDS -T -d gpurun_out/pmc_valu_extra "
+                  "-o valu --output-format csv -- python3 -u bench.py --extras-only --extra-steps 3",
     "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_cal_fetch -o cal "
                  "--output-format csv -- python3 -u bench.py --calibrate-copy",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_cal_write -o cal "
@@ -141,6 +147,54 @@ def _read_counters(path: pathlib.Path):
     for r in csv.DictReader(open(path)):
         per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
     return per
+
+
+def _read_counters_by_name(path: pathlib.Path):
+    """{kernel: {counter: [value per dispatch]}} from a rocprofv3 counter CSV."""
+    import csv
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize_valu(d: pathlib.Path) -> pathlib.Path | None:
+    """profiles/ summary of VALUBusy / SQ_INSTS_VALU / SQ_INSTS_LDS per kernel."""
+    files = [f for sub in ("pmc_valu", "pmc_valu_extra") if (d / sub).exists()
+             for f in (d / sub).glob("*counter_collection.csv")]
+    if not files:
+        return None
+    rows = {}
+    for f in files:
+        for k, cs in _read_counters_by_name(f).items():
+            rows.setdefault(k, cs)
+    lines = [
+        "# VALU activity per kernel from rocprofv3 counters",
+        "",
+        "Commands (repo root):",
+        "",
+        f"    {PROFILE_COMMANDS['valu']}",
+        f"    {PROFILE_COMMANDS['valu_extra']}",
+        f"    {PROFILE_COMMANDS['summary']}",
+        "",
+        "VALUBusy is rocprofv3's derived metric 100 * sum(SQ_ACTIVE_INST_VALU) / CU_NUM / "
+        "max(GRBM_GUI_ACTIVE): the share of the kernel's GPU time in which the CUs issue vector "
+        "ALU work. SQ_INSTS_VALU and SQ_INSTS_LDS count wave-level instructions per dispatch. "
+        "A kernel near its HBM roofline shows a low VALUBusy; one bound by its arithmetic "
+        "shows a high one.",
+        "",
+        "| kernel | dispatches | VALUBusy % | SQ_INSTS_VALU per dispatch | SQ_INSTS_LDS per dispatch |",
+        "|---|---|---|---|---|",
+    ]
+    mean = lambda v: sum(v) / len(v) if v else float("nan")  # noqa: E731
+    for k in sorted(rows, key=lambda k: -mean(rows[k].get("VALUBusy", [0]))):
+        cs = rows[k]
+        lines.append(f"| {k} | {len(cs.get('SQ_INSTS_VALU', []))} | {mean(cs.get('VALUBusy', [])):.1f} | "
+                     f"{mean(cs.get('SQ_INSTS_VALU', [])):,.0f} | {mean(cs.get('SQ_INSTS_LDS', [])):,.0f} |")
+    lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
+    PROFILE_VALU.write_text("\n".join(lines))
+    return PROFILE_VALU
 
 
 def summarize_profiles(out_dir: str) -> None:
@@ -295,6 +349,9 @@ def summarize_profiles(out_dir: str) -> None:
         lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
         PROFILE_STATS_EXTRA.write_text("\n".join(lines))
         wrote.append(PROFILE_STATS_EXTRA)
+    v = summarize_valu(d)
+    if v:
+        wrote.append(v)
     print("wrote " + ", ".join(str(w) for w in wrote))
 
 

@@ -661,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const float* __restric
 // qsgd_maxnorm_quantize computes them on the gathered array; the int32 sum
 // of the W levels; its dequantized value, scattered to dense[idx[k]].
 constexpr unsigned kGkMaxGatherBlocks = 1024;
-constexpr int kGkQThreads = 64;
+constexpr int kGkQThreads = 256;
 
 // Launch 1 when K <= kRandKLdsMax: workgroup 0 draws the indices in LDS
 // while the others zero the dense output. The draw's 128 KB of LDS holds
@@ -703,14 +703,18 @@ __global__ __launch_bounds__(kThreads) void grandk_gather_fill_kernel(
         partials[blockIdx.x] = m;
 }
 
-template <int WC>
+// One thread per (slot, worker): a workgroup takes kGkQThreads / W slots,
+// each thread draws one worker's Philox words for its slot and adds the four
+// levels into the slot's int32 sums in LDS (integer adds: exact in any
+// order), then the slots are dequantized and scattered.
 __global__ __launch_bounds__(kGkQThreads) void grandk_quantize_scatter_kernel(
-    int W_rt, uint32_t K, size_t Kp, const float* __restrict__ gathered,
+    int W, uint32_t K, size_t Kp, const float* __restrict__ gathered,
     const float* __restrict__ partials, unsigned nparts, float s24, float s_f, uint32_t k0,
     uint32_t k1, const uint32_t* __restrict__ idx, int32_t* __restrict__ sums,
     float* __restrict__ dense, float* __restrict__ norm_out)
 {
     __shared__ float norm_sh;
+    __shared__ int32_t lsum[kGkQThreads][4];
     float m = 0.0f;
     for (unsigned i = threadIdx.x; i < nparts; i += kGkQThreads)
         m = fmaxf(m, partials[i]);
@@ -720,55 +724,44 @@ __global__ __launch_bounds__(kGkQThreads) void grandk_quantize_scatter_kernel(
         if (blockIdx.x == 0 && norm_out)
             *norm_out = m;
     }
+    for (int e = threadIdx.x; e < kGkQThreads * 4; e += kGkQThreads)
+        lsum[e >> 2][e & 3] = 0;
     __syncthreads();
     const float norm = norm_sh;
-    const int W = WC > 0 ? WC : W_rt;
     const bool fast = norm >= 0x1p-120f;
     const float inv = fast ? 1.0f / norm : 0.0f;
+    const int spb = kGkQThreads / W;  // slots per workgroup pass (W <= 64: at least 4)
+    const int ls = int(threadIdx.x) / W, w = int(threadIdx.x) % W;
     const size_t nslots = (size_t(K) + 3) >> 2;
-    for (size_t q = size_t(blockIdx.x) * kGkQThreads + threadIdx.x; q < nslots;
-         q += size_t(gridDim.x) * kGkQThreads) {
-        i32x4 S = {0, 0, 0, 0};
-        if (norm != 0.0f) {
-            constexpr int kG = WC > 0 ? WC : kFGroup;
-            for (int w0 = 0; w0 < W; w0 += kG) {
-                f32x4 g[kG];
-                U4 r[kG];
+    for (size_t base = size_t(blockIdx.x) * spb; base < nslots; base += size_t(gridDim.x) * spb) {
+        const size_t q = base + size_t(ls);
+        if (ls < spb && q < nslots && norm != 0.0f) {
+            f32x4 g = reinterpret_cast<const f32x4*>(gathered + size_t(w) * Kp)[q];
+            // the padding past K holds no value: level 0, as in the quantize
+            // kernel's partial slot
 #pragma unroll
-                for (int dw = 0; dw < kG; ++dw) {
-                    g[dw] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                    if (WC > 0 || w0 + dw < W) {
-                        g[dw] = reinterpret_cast<const f32x4*>(gathered +
-                                                               size_t(w0 + dw) * Kp)[q];
-                        // the padding past K holds no value: level 0, as in
-                        // the quantize kernel's partial slot
+            for (int k = 0; k < 4; ++k)
+                if (q * 4 + k >= K)
+                    g[k] = 0.0f;
+            int lv[4];
+            qsgd_levels4(g, philox4x32_10(U4{uint32_t(q), uint32_t(q >> 32), uint32_t(w), 0u}, k0, k1),
+                         norm, inv, s24, fast, lv);
 #pragma unroll
-                        for (int k = 0; k < 4; ++k)
-                            if (q * 4 + k >= K)
-                                g[dw][k] = 0.0f;
-                    }
-                    r[dw] = philox4x32_10(U4{uint32_t(q), uint32_t(q >> 32), uint32_t(w0 + dw), 0u},
-                                          k0, k1);
-                }
-#pragma unroll
-                for (int dw = 0; dw < kG; ++dw) {
-                    if (WC == 0 && w0 + dw >= W)
-                        break;
-                    int lv[4];
-                    qsgd_levels4(g[dw], r[dw], norm, inv, s24, fast, lv);
-                    S += i32x4{lv[0], lv[1], lv[2], lv[3]};
-                }
-            }
+            for (int k = 0; k < 4; ++k)
+                atomicAdd(&lsum[ls][k], lv[k]);
         }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const size_t i = q * 4 + k;
+        __syncthreads();
+        for (int e = threadIdx.x; e < spb * 4; e += kGkQThreads) {
+            const size_t i = (base + size_t(e >> 2)) * 4 + (e & 3);
+            const int32_t S = lsum[e >> 2][e & 3];
+            lsum[e >> 2][e & 3] = 0;
             if (i < K) {
                 if (sums)
-                    sums[i] = S[k];
-                dense[idx[i]] = dequant(norm, S[k], s_f);
+                    sums[i] = S;
+                dense[idx[i]] = dequant(norm, S, s_f);
             }
         }
+        __syncthreads();
     }
 }
 
@@ -1107,26 +1100,12 @@ GCQ_API int grandk_mn_step(const float* const* grads, int W, size_t n, uint32_t 
     if (int rc = check_launch("grandk_mn_step (gather, fill)"))
         return rc;
     // launch 3: norm, levels, sum, dequantize, scatter
+    const size_t spb = size_t(kGkQThreads / W);
     const size_t qblocks = std::max<size_t>(
-        1, std::min(ceil_div(ceil_div(size_t(K), 4), kGkQThreads), max_grid_blocks()));
+        1, std::min(ceil_div(ceil_div(size_t(K), 4), spb), max_grid_blocks()));
     const float s24 = float(s) * 16777216.0f;  // exact: s <= 127
-    const float s_f = float(s);
-    switch (W) {
-#define GCQ_GK_CASE(c)                                                                          \
-    case c:                                                                                     \
-        hipLaunchKernelGGL((grandk_quantize_scatter_kernel<c>), dim3(unsigned(qblocks)),        \
-                           dim3(kGkQThreads), 0, stream, W, K, L.Kp, gathered, partials,        \
-                           L.gather_blocks, s24, s_f, k0, k1, idx, sums, dense, norm);          \
-        break;
-        GCQ_GK_CASE(1)
-        GCQ_GK_CASE(2)
-        GCQ_GK_CASE(4)
-        GCQ_GK_CASE(8)
-#undef GCQ_GK_CASE
-    default:
-        hipLaunchKernelGGL((grandk_quantize_scatter_kernel<0>), dim3(unsigned(qblocks)),
-                           dim3(kGkQThreads), 0, stream, W, K, L.Kp, gathered, partials,
-                           L.gather_blocks, s24, s_f, k0, k1, idx, sums, dense, norm);
-    }
+    hipLaunchKernelGGL(grandk_quantize_scatter_kernel, dim3(unsigned(qblocks)), dim3(kGkQThreads),
+                       0, stream, W, K, L.Kp, gathered, partials, L.gather_blocks, s24, float(s),
+                       k0, k1, idx, sums, dense, norm);
     return check_launch("grandk_mn_step (quantize, scatter)");
 }

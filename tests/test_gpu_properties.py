@@ -142,3 +142,26 @@ def test_grandk_indices_random(gcq, n, frac, seed):
     gcq.grandk_indices(n, K, seed, idx[:K], ws)
     gu.sync()
     np.testing.assert_array_equal(gu.host(idx, np.uint32)[:K], oracle.randk_indices(n, K, seed))
+
+
+@SETTINGS
+@given(n=st.integers(1, 150_000), frac=st.floats(0.0, 1.0), W=st.integers(1, 12),
+       s=st.integers(1, 127), misalign=st.booleans(), seed=st.integers(0, 2 ** 63 - 1))
+def test_grandk_mn_step_random(gcq, n, frac, W, s, misalign, seed):
+    K = min(n, int(frac * min(n, 24_000)))
+    announce(f"prop grandk_mn_step n={n} K={K} W={W} s={s} mis={misalign} seed={seed}")
+    grads = [si.normal_f32((seed + 7 * w) % (2 ** 32), n, 0.01) for w in range(W)]
+    idx = gu.empty(max(K, 1), torch.int32, fill=-1)
+    sums = gu.empty(max(K, 1), torch.int32, fill=-1)
+    dense = gu.empty(n, torch.float32, misalign=misalign, fill=float("nan"))
+    ws = torch.empty(gcq.grandk_mn_step_ws_bytes(W, n, K), dtype=torch.uint8, device=gu.DEV)
+    gcq.grandk_mn_step([gu.dev(g) for g in grads], K, seed, s, idx, dense, ws, sums=sums)
+    gu.sync()
+    idx_or = oracle.randk_indices(n, K, seed)
+    gk = [oracle.gather(g, idx_or) for g in grads]
+    nrm = oracle.maxnorm(gk) if K > 0 else np.float32(0.0)
+    S = oracle.level_sum([oracle.qsgd_quantize(g, nrm, s, seed, w) for w, g in enumerate(gk)])
+    np.testing.assert_array_equal(gu.host(idx, np.uint32)[:K], idx_or)
+    np.testing.assert_array_equal(gu.host(sums)[:K], S)
+    np.testing.assert_array_equal(gu.host(dense),
+                                  oracle.scatter_dense(oracle.qsgd_dequantize(S, nrm, s), idx_or, n))
