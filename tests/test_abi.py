@@ -154,7 +154,7 @@ def test_quantize_sum_rejects_bad_arguments(lib):
 def test_workspace_queries(lib):
     size = ctypes.c_size_t(0)
     assert lib.qsgd_global_maxnorm(None, 8, 138_357_544, None, None, ctypes.byref(size), None) == 0
-    assert 0 < size.value <= 8 * 512 * 4
+    assert 0 < size.value <= 8 * 4096 * 4
     small = ctypes.c_size_t(size.value - 4)
     arr = (ctypes.c_void_p * 8)(*([FAKE] * 8))
     assert lib.qsgd_global_maxnorm(arr, 8, 138_357_544, FAKE, FAKE, ctypes.byref(small),
