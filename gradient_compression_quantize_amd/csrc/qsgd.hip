@@ -72,16 +72,28 @@ __device__ __forceinline__ float block_max(float m)
 
 // Each workgroup reduces one contiguous chunk of a worker's float4 slots,
 // two non-temporal loads in flight per lane. Measured over 8 x 138M values:
-// chunks for 4096 workgroups per worker read at ~86% of peak HBM bandwidth,
-// against ~73% for 512 strided workgroups with four loads in flight each.
+// 512-byte-aligned chunks for ~4096 workgroups per worker read at ~88% of
+// peak HBM bandwidth, against ~73% for 512 strided workgroups with four
+// loads in flight each.
 constexpr unsigned kMaxPartialsPerWorker = 4096;
 constexpr int kMaxAbsUnroll = 2;
 constexpr size_t kMaxAbsMinChunk = 2048;  // float4 slots per workgroup, at least
+constexpr size_t kMaxAbsChunkAlign = 32;  // float4 slots: chunks start on 512 B
 
-unsigned maxnorm_grid_x(size_t n)
+struct MaxNormGrid {
+    unsigned gx;    // workgroups per worker = partial maxima per worker
+    size_t chunk4;  // float4 slots per workgroup
+};
+
+MaxNormGrid maxnorm_grid(size_t n)
 {
-    return unsigned(std::max<size_t>(
-        1, std::min<size_t>(ceil_div(n >> 2, kMaxAbsMinChunk), kMaxPartialsPerWorker)));
+    const size_t n4 = n >> 2;
+    const size_t gx0 = std::max<size_t>(
+        1, std::min<size_t>(ceil_div(n4, kMaxAbsMinChunk), kMaxPartialsPerWorker));
+    const size_t chunk4 =
+        ceil_div(ceil_div(n4, gx0), kMaxAbsChunkAlign) * kMaxAbsChunkAlign;
+    const size_t gx = chunk4 ? std::max<size_t>(1, ceil_div(n4, chunk4)) : 1;
+    return MaxNormGrid{unsigned(gx), chunk4};
 }
 
 // blockIdx.y = worker. Workgroup x takes float4 slots [x chunk4, (x+1) chunk4)
@@ -130,13 +142,31 @@ __global__ __launch_bounds__(kThreads) void maxabs_partial_kernel(PtrTable<float
 
 constexpr int kFinalThreads = 1024;
 
+constexpr int kFinalUnroll = 8;
+
+// Eight independent loads in flight per lane: the partials are tens of
+// thousands of floats, and one dependent load at a time made this
+// latency-bound.
 __global__ __launch_bounds__(kFinalThreads) void max_final_kernel(const float* __restrict__ partials,
                                                                   unsigned count,
                                                                   float* __restrict__ norm)
 {
-    float m = 0.0f;
-    for (unsigned i = threadIdx.x; i < count; i += kFinalThreads)
-        m = fmaxf(m, partials[i]);
+    float mu[kFinalUnroll];
+#pragma unroll
+    for (int u = 0; u < kFinalUnroll; ++u)
+        mu[u] = 0.0f;
+    unsigned i = threadIdx.x;
+    for (; i + (kFinalUnroll - 1) * kFinalThreads < count; i += kFinalUnroll * kFinalThreads) {
+#pragma unroll
+        for (int u = 0; u < kFinalUnroll; ++u)
+            mu[u] = fmaxf(mu[u], partials[i + u * kFinalThreads]);
+    }
+    for (; i < count; i += kFinalThreads)
+        mu[0] = fmaxf(mu[0], partials[i]);
+    float m = mu[0];
+#pragma unroll
+    for (int u = 1; u < kFinalUnroll; ++u)
+        m = fmaxf(m, mu[u]);
     m = block_max<kFinalThreads>(m);
     if (threadIdx.x == 0)
         *norm = m;
@@ -817,7 +847,8 @@ GCQ_API int qsgd_global_maxnorm(const float* const* grads, int W, size_t n, floa
         return fail(GC_EINVAL, "qsgd_global_maxnorm: W must be in [1, 64]");
     if (!ws_bytes)
         return fail(GC_EINVAL, "qsgd_global_maxnorm: ws_bytes is NULL");
-    const unsigned gx = maxnorm_grid_x(n);
+    const MaxNormGrid mg = maxnorm_grid(n);
+    const unsigned gx = mg.gx;
     const size_t need = size_t(gx) * size_t(W) * sizeof(float);
     if (!ws) {
         *ws_bytes = need;
@@ -835,7 +866,7 @@ GCQ_API int qsgd_global_maxnorm(const float* const* grads, int W, size_t n, floa
     }
     float* partials = static_cast<float*>(ws);
     hipLaunchKernelGGL(maxabs_partial_kernel, dim3(gx, unsigned(W)), dim3(kThreads), 0, stream,
-                       tab, n, ceil_div(n >> 2, gx), partials);
+                       tab, n, mg.chunk4, partials);
     if (int rc = check_launch("qsgd_global_maxnorm (partials)"))
         return rc;
     hipLaunchKernelGGL(max_final_kernel, dim3(1), dim3(kFinalThreads), 0, stream, partials,
