@@ -183,16 +183,19 @@ __global__ __launch_bounds__(kFinalThreads) void max_final_kernel(const float* _
 // fl(q * s) is a normal number; below that x < 2^-126 and every path gives
 // level 0. The conversion truncates, which is the floor for X >= 0.
 //
-// The quotient: the exact path divides (IEEE, correctly rounded). The fast
-// path multiplies by inv = fl(1 / norm) instead. Every rounding involved
-// (fl(1/norm), fl(a * inv), fl(a / norm), and the product with s24 on each
-// path) is within 2^-24 relative of its real value, so for |g| <= norm the
-// two values of X differ by at most 5 * 2^-24 * X < 5 * 127 = 635. With
+// The quotient: the exact path divides (IEEE, correctly rounded) and then
+// scales by s24. The fast path multiplies once, by c = fl(fl(1 / norm) * s24).
+// Each side takes rounded steps (fl(1/norm), fl(inv * s24), fl(a * c); and
+// fl(a / norm), fl(q * s24)), every one within 2^-24 relative of its real
+// value while its result is a normal number -- which holds wherever the
+// level can be nonzero (X >= 1 needs a / norm >= 2^-31). So for |g| <= norm
+// the two values of X differ by at most 5 * 2^-24 * X < 5 * 127 = 635. With
 // t = floor(X) + k, the exact t therefore lies within kSlack = 2048 of the
 // fast one; when t - kSlack and t + kSlack fall in the same 2^24 bucket the
 // fast level is the exact level. Otherwise (about one value in 4000) the
 // lane recomputes its slot through the division. `fast` is false when norm
-// is so small that 1 / norm could overflow: then every value divides.
+// is so small that c could overflow (norm < 2^-96; c <= 2^96 * 127 * 2^24
+// stays finite): then every value divides.
 constexpr uint32_t kSlack = 2048;
 
 __device__ __forceinline__ uint32_t level_from_quotient(float q, uint32_t r, float s24)
@@ -200,10 +203,14 @@ __device__ __forceinline__ uint32_t level_from_quotient(float q, uint32_t r, flo
     return (static_cast<uint32_t>(q * s24) + (r >> 8)) >> 24;
 }
 
+// Smallest norm for which the fast path's multiplier stays finite.
+constexpr float kFastNormMin = 0x1p-96f;
+
 // Levels of four values (one float4 slot and its four Philox words), with the
 // sign of g applied. One branch per slot: the exact path runs for the slot
 // when any of its values is near a bucket edge, or when `fast` is off.
-__device__ __forceinline__ void qsgd_levels4(f32x4 g, U4 r, float norm, float inv, float s24,
+// c = fl(fl(1 / norm) * s24) when fast.
+__device__ __forceinline__ void qsgd_levels4(f32x4 g, U4 r, float norm, float c, float s24,
                                              bool fast, int lv[4])
 {
     const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
@@ -214,7 +221,7 @@ __device__ __forceinline__ void qsgd_levels4(f32x4 g, U4 r, float norm, float in
     uint32_t closest = fast ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint32_t t = static_cast<uint32_t>((fabsf(g[k]) * inv) * s24) + (rr[k] >> 8);
+        const uint32_t t = static_cast<uint32_t>(fabsf(g[k]) * c) + (rr[k] >> 8);
         m[k] = t >> 24;
         closest = min(closest, (t + kSlack) & 0x00FFFFFFu);
     }
@@ -252,8 +259,8 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
     uint32_t k0, uint32_t k1, uint32_t worker, int8_t* __restrict__ levels, int vec)
 {
     const float norm = *norm_ptr;
-    const bool fast = norm >= 0x1p-120f;
-    const float inv = fast ? 1.0f / norm : 0.0f;
+    const bool fast = norm >= kFastNormMin;
+    const float c = fast ? (1.0f / norm) * s24 : 0.0f;
     const size_t nslots = (n + 3) >> 2;
     const size_t nfull = n >> 2;
     const size_t ntiles = (nslots + kQTile - 1) / kQTile;
@@ -279,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
 #pragma unroll
                 for (int u = 0; u < kQUnroll; ++u) {
                     int lv[4];
-                    qsgd_levels4(g[u], r[u], norm, inv, s24, fast, lv);
+                    qsgd_levels4(g[u], r[u], norm, c, s24, fast, lv);
                     packed[u] = pack4(lv[0], lv[1], lv[2], lv[3]);
                 }
             }
@@ -301,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
                 if (norm != 0.0f) {
                     const U4 r =
                         philox4x32_10(U4{uint32_t(q), uint32_t(q >> 32), worker, 0u}, k0, k1);
-                    qsgd_levels4(g, r, norm, inv, s24, fast, lv);
+                    qsgd_levels4(g, r, norm, c, s24, fast, lv);
                 }
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
@@ -431,8 +438,8 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_kernel(
 {
     const int W = WC > 0 ? WC : W_rt;
     const float norm = *norm_ptr;
-    const bool fast = norm >= 0x1p-120f;
-    const float inv = fast ? 1.0f / norm : 0.0f;
+    const bool fast = norm >= kFastNormMin;
+    const float c = fast ? (1.0f / norm) * s24 : 0.0f;
     const size_t nslots = (n + 3) >> 2;
     const size_t nfull = n >> 2;
     const size_t stride = size_t(gridDim.x) * kThreads;
@@ -459,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_kernel(
                         if (WC == 0 && w0 + dw >= W)
                             break;
                         int lv[4];
-                        qsgd_levels4(g[dw], r[dw], norm, inv, s24, fast, lv);
+                        qsgd_levels4(g[dw], r[dw], norm, c, s24, fast, lv);
                         S += i32x4{lv[0], lv[1], lv[2], lv[3]};
                     }
                 }
@@ -476,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_kernel(
                 if (norm != 0.0f) {
                     int lv[4];
                     qsgd_levels4(g, philox4x32_10(U4{ctr0.x, ctr0.y, uint32_t(w), 0u}, k0, k1),
-                                 norm, inv, s24, fast, lv);
+                                 norm, c, s24, fast, lv);
                     S += i32x4{lv[0], lv[1], lv[2], lv[3]};
                 }
             }
@@ -769,8 +776,8 @@ __global__ __launch_bounds__(kGkQThreads) void grandk_quantize_scatter_kernel(
         lsum[e >> 2][e & 3] = 0;
     __syncthreads();
     const float norm = norm_sh;
-    const bool fast = norm >= 0x1p-120f;
-    const float inv = fast ? 1.0f / norm : 0.0f;
+    const bool fast = norm >= kFastNormMin;
+    const float c = fast ? (1.0f / norm) * s24 : 0.0f;
     const int spb = kGkQThreads / W;  // slots per workgroup pass (W <= 64: at least 4)
     const int ls = int(threadIdx.x) / W, w = int(threadIdx.x) % W;
     const size_t nslots = (size_t(K) + 3) >> 2;
@@ -786,7 +793,7 @@ __global__ __launch_bounds__(kGkQThreads) void grandk_quantize_scatter_kernel(
                     g[k] = 0.0f;
             int lv[4];
             qsgd_levels4(g, philox4x32_10(U4{uint32_t(q), uint32_t(q >> 32), uint32_t(w), 0u}, k0, k1),
-                         norm, inv, s24, fast, lv);
+                         norm, c, s24, fast, lv);
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 atomicAdd(&lsum[ls][k], lv[k]);

@@ -232,7 +232,7 @@ def test_qsgd_level_edges(gcq, s):
                                       err_msg=f"seed {seed}")
 
 
-@pytest.mark.parametrize("norm_scale", [1e-38, 2.0 ** -121, 1e-30, 1e30])
+@pytest.mark.parametrize("norm_scale", [1e-38, 2.0 ** -121, 1e-30, 2.0 ** -98, 2.0 ** -96, 1e30])
 def test_qsgd_extreme_norms(gcq, norm_scale):
     """Tiny norms (where 1/norm would overflow, so every value takes the
     exact division) and huge ones, through the whole QSGD step."""
@@ -243,6 +243,39 @@ def test_qsgd_extreme_norms(gcq, norm_scale):
     norm_or = oracle.maxnorm([g])
     assert norm.view(np.uint32) == norm_or.view(np.uint32)
     np.testing.assert_array_equal(levels[0], oracle.qsgd_quantize(g, norm_or, 127, 3, 0))
+
+
+@pytest.mark.parametrize("norm_bits", ["2^-96", "below 2^-96", "2^-95", "2^-120"])
+def test_qsgd_fast_path_threshold(gcq, norm_bits):
+    """Norms at and around the smallest one that takes the multiply-by-
+    reciprocal fast path (2^-96; one ulp below it every value divides):
+    per-worker quantize and the fused quantize-sum both equal the oracle."""
+    announce(f"qsgd fast-path threshold norm={norm_bits}")
+    base = {"2^-96": np.float32(2.0 ** -96), "2^-95": np.float32(2.0 ** -95),
+            "below 2^-96": np.nextafter(np.float32(2.0 ** -96), np.float32(0)),
+            "2^-120": np.float32(2.0 ** -120)}[norm_bits]
+    grads = []
+    for w in range(3):
+        g = si.normal_f32(300 + w, 20_011, 1.0)
+        g = (g / np.float32(np.abs(g).max() * 1.01) * base).astype(np.float32)
+        grads.append(g)
+    grads[1][7] = -base
+    for s in (7, 127):
+        norm, levels, sums, out = run_qsgd(gcq, grads, s, 19)
+        assert norm.view(np.uint32) == base.view(np.uint32)
+        lv_or = [oracle.qsgd_quantize(g, base, s, 19, w) for w, g in enumerate(grads)]
+        for w in range(3):
+            np.testing.assert_array_equal(levels[w], lv_or[w], err_msg=f"s={s} worker {w}")
+        s_or = oracle.level_sum(lv_or)
+        np.testing.assert_array_equal(sums, s_or)
+        check_deq(out, oracle.qsgd_dequantize(s_or, base, s))
+        fsums = gu.empty(20_011, torch.int32)
+        fout = gu.empty(20_011, torch.float32)
+        nt = torch.tensor([base], dtype=torch.float32, device=gu.DEV)
+        gcq.qsgd_quantize_sum([gu.dev(g) for g in grads], nt, s, 19, fout, sums=fsums)
+        gu.sync()
+        np.testing.assert_array_equal(gu.host(fsums), s_or)
+        check_deq(gu.host(fout), oracle.qsgd_dequantize(s_or, base, s))
 
 
 def test_grandk_step_in_hip_graph(gcq):
