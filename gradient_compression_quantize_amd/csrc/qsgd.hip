@@ -29,13 +29,21 @@ struct U4 {
     uint32_t x, y, z, w;
 };
 
+// Three-input XOR in one CDNA4 instruction (v_bitop3_b32, truth table 0x96:
+// the parity of the three input bits). The quantize kernels are bound by
+// VALU issue, and this halves the XORs of every Philox round.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c)
+{
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1)
 {
 #pragma unroll
     for (int round = 0; round < 10; ++round) {
         const uint64_t pa = uint64_t(0xD2511F53u) * c.x;
         const uint64_t pb = uint64_t(0xCD9E8D57u) * c.z;
-        c = U4{uint32_t(pb >> 32) ^ c.y ^ k0, uint32_t(pb), uint32_t(pa >> 32) ^ c.w ^ k1,
+        c = U4{xor3(uint32_t(pb >> 32), c.y, k0), uint32_t(pb), xor3(uint32_t(pa >> 32), c.w, k1),
                uint32_t(pa)};
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
