@@ -433,9 +433,11 @@ __global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_kernel(
 // kernel), forms the four levels with the same arithmetic and adds them into
 // int32 sums, then dequantizes. The int8 levels -- what each worker would put
 // on the wire -- are never written: a step reads 4 W n bytes and writes 8 n
-// (4 n without the sums) instead of 5 W n + W n + 8 n. WC > 0: W known at
-// compile time, all W loads in flight together and the W Philox chains
-// interleaved; WC == 0: groups of kFGroup workers.
+// (4 n without the sums) instead of 5 W n + W n + 8 n. Workers go in groups
+// of kFGroup (fewer when W < kFGroup is known at compile time): the group's
+// loads in flight together and its Philox chains interleaved. At W = 8,
+// groups of 4 (52 VGPRs) measured 0.97 ms against 1.01 ms for all 8 at once
+// (78 VGPRs) and 0.99 ms for groups of 2.
 constexpr int kFGroup = 4;
 
 template <int WC>
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_kernel(
         const U4 ctr0 = {uint32_t(q), uint32_t(q >> 32), 0u, 0u};
         i32x4 S = {0, 0, 0, 0};
         if (vec && q < nfull) {
-            constexpr int kG = WC > 0 ? WC : kFGroup;
+            constexpr int kG = (WC > 0 && WC < kFGroup) ? WC : kFGroup;
             for (int w0 = 0; w0 < W; w0 += kG) {
                 f32x4 g[kG];
 #pragma unroll
