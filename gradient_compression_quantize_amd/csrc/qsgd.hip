@@ -255,10 +255,11 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d)
 // Philox counter (q lo, q hi, worker, 0) of slot q gives the four words of
 // elements 4q .. 4q+3, and a lane's kQUnroll independent Philox chains
 // interleave to fill the VALU pipeline (the kernel is bound by that ALU
-// work, not by HBM). Full tiles take a branch-free vector path; the one
+// work, not by HBM; 8 quantizes of 138M values took 0.96 / 0.93 / 0.96 ms
+// with 2 / 4 / 8 chains). Full tiles take a branch-free vector path; the one
 // partial tile, and buffers without the vector alignment, take a checked
 // scalar path. kLoop = false: one tile per wave (the usual case).
-constexpr int kQUnroll = 2;
+constexpr int kQUnroll = 4;
 constexpr size_t kQTile = size_t(kWave) * kQUnroll;
 
 template <bool kLoop>
