@@ -46,6 +46,18 @@ def heavy_tailed_f32(seed: int, n: int, sigma: float, frac: float = 1e-3,
     return x
 
 
+def uniform_f32_device(seed: int, n: int, device: str = "cuda:0"):
+    """n values uniform in [-1, 1), float32, drawn on the device by torch's
+    seeded generator: for inputs too large to draw on the host (tens of GB).
+    Tests copy back the windows they check; both sides see the same bytes."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    x = torch.empty(n, dtype=torch.float32, device=device)
+    x.uniform_(-1.0, 1.0, generator=gen)
+    return x
+
+
 def bert_base_shapes() -> list[tuple[int, ...]]:
     """BERT-Base parameter tensors in model order: embeddings (word, position,
     token-type, LayerNorm as one 2x768 tensor), 12 encoder layers (four 768x768
