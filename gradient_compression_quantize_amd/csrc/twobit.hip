@@ -307,41 +307,40 @@ __global__ __launch_bounds__(kThreads) void decompress_2bit_scalar_kernel(
 
 // ---- many tensors ----------------------------------------------------------
 
-struct TensorDesc {
+// One workgroup's share: kBlockElems values of one tensor, with everything
+// the workgroup needs about that tensor in the same 48 bytes, so that it
+// starts streaming after a single (scalar) descriptor load.
+struct alignas(16) ChunkDesc {
     const float* grad;
     float* residual;
     uint64_t n;
     uint64_t word_off;  // first uint32 element of this tensor's block
     float n_f;          // (float)n, converted on the host
+    uint32_t chunk;     // index of the kBlockElems-sized chunk inside the tensor
     uint32_t vec_ok;    // grad and residual both 16-byte aligned
+    uint32_t pad;
 };
-
-// One workgroup's share: kBlockElems values of one tensor.
-struct ChunkDesc {
-    uint32_t tensor;
-    uint32_t chunk;  // index of the kBlockElems-sized chunk inside the tensor
-};
+static_assert(sizeof(ChunkDesc) == 48, "one 48-byte descriptor per chunk");
 
 template <bool kLoop>
 __global__ __launch_bounds__(kThreads) void compress_2bit_multi_kernel(
-    const TensorDesc* __restrict__ tensors, const ChunkDesc* __restrict__ chunks,
-    size_t nchunks, float neg, float pos, uint32_t* __restrict__ compr_base)
+    const ChunkDesc* __restrict__ chunks, size_t nchunks, float neg, float pos,
+    uint32_t* __restrict__ compr_base)
 {
     const int lane = threadIdx.x & (kWave - 1);
     for (size_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
         const ChunkDesc cd = chunks[c];
-        const TensorDesc td = tensors[cd.tensor];
-        uint32_t* blk = compr_base + td.word_off;
+        uint32_t* blk = compr_base + cd.word_off;
         if (cd.chunk == 0 && threadIdx.x == 0)
-            write_header(blk, neg, pos, td.n_f);
-        if (td.vec_ok) {
+            write_header(blk, neg, pos, cd.n_f);
+        if (cd.vec_ok) {
             const size_t q0 = size_t(cd.chunk) * (kBlockElems / 4) +
                               size_t(threadIdx.x / kWave) * kTileF4;
-            compress_tile(td.grad, td.residual, td.n, neg, pos, blk + 3, q0, lane);
+            compress_tile(cd.grad, cd.residual, cd.n, neg, pos, blk + 3, q0, lane);
         } else {
             const size_t j = size_t(cd.chunk) * (kBlockElems / 16) + threadIdx.x;
-            if (j < ((td.n + 15) >> 4))
-                blk[3 + j] = compress_word_scalar(td.grad, td.residual, td.n, neg, pos, j);
+            if (j < ((cd.n + 15) >> 4))
+                blk[3 + j] = compress_word_scalar(cd.grad, cd.residual, cd.n, neg, pos, j);
         }
         if (!kLoop)
             break;
@@ -370,7 +369,6 @@ struct gc_plan {
     size_t nchunks = 0;
     size_t total_words = 0;
     std::vector<size_t> offsets;
-    gcq::TensorDesc* d_tensors = nullptr;
     gcq::ChunkDesc* d_chunks = nullptr;
 };
 
@@ -508,7 +506,6 @@ GCQ_API int gc_plan_2bit_multi_create(const float* const* grads, float* const* r
     if (T < 1 || !grads || !residuals || !ns)
         return fail(GC_EINVAL, "gc_plan_2bit_multi_create: need T >= 1 and host arrays");
 
-    std::vector<TensorDesc> tensors(static_cast<size_t>(T));
     std::vector<ChunkDesc> chunks, first;
     std::vector<size_t> offsets(static_cast<size_t>(T));
     size_t off = 0;
@@ -521,7 +518,7 @@ GCQ_API int gc_plan_2bit_multi_create(const float* const* grads, float* const* r
         const size_t nch = std::max<size_t>(1, ceil_div(n, kBlockElems));
         if (nch > 0xFFFFFFFFull)
             return fail(GC_EUNSUPPORTED, "gc_plan_2bit_multi_create: tensor too large");
-        TensorDesc& d = tensors[static_cast<size_t>(t)];
+        ChunkDesc d{};
         d.grad = grads[t];
         d.residual = residuals[t];
         d.n = n;
@@ -533,10 +530,14 @@ GCQ_API int gc_plan_2bit_multi_create(const float* const* grads, float* const* r
         // a chunk holding a partial tile takes the slow scalar path: those go
         // first in the launch so that they overlap the streaming chunks
         const bool ragged = (n % kTileElems) != 0 || n == 0;
-        if (ragged)
-            first.push_back(ChunkDesc{static_cast<uint32_t>(t), static_cast<uint32_t>(nch - 1)});
-        for (size_t c = 0; c + (ragged ? 1 : 0) < nch; ++c)
-            chunks.push_back(ChunkDesc{static_cast<uint32_t>(t), static_cast<uint32_t>(c)});
+        if (ragged) {
+            d.chunk = static_cast<uint32_t>(nch - 1);
+            first.push_back(d);
+        }
+        for (size_t c = 0; c + (ragged ? 1 : 0) < nch; ++c) {
+            d.chunk = static_cast<uint32_t>(c);
+            chunks.push_back(d);
+        }
     }
     chunks.insert(chunks.begin(), first.begin(), first.end());
 
@@ -546,10 +547,7 @@ GCQ_API int gc_plan_2bit_multi_create(const float* const* grads, float* const* r
     p->total_words = off;
     p->offsets = std::move(offsets);
     if (hipGetDevice(&p->device) != hipSuccess ||
-        hipMalloc(&p->d_tensors, tensors.size() * sizeof(TensorDesc)) != hipSuccess ||
         hipMalloc(&p->d_chunks, chunks.size() * sizeof(ChunkDesc)) != hipSuccess ||
-        hipMemcpy(p->d_tensors, tensors.data(), tensors.size() * sizeof(TensorDesc),
-                  hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(p->d_chunks, chunks.data(), chunks.size() * sizeof(ChunkDesc),
                   hipMemcpyHostToDevice) != hipSuccess) {
         const hipError_t e = hipGetLastError();
@@ -587,12 +585,12 @@ GCQ_API int compress_2bit_multi(gc_plan* plan, float neg_threshold, float pos_th
     const size_t blocks = std::min(plan->nchunks, max_grid_blocks());
     if (blocks < plan->nchunks)
         hipLaunchKernelGGL(compress_2bit_multi_kernel<true>, dim3(blocks), dim3(kThreads), 0,
-                           stream, plan->d_tensors, plan->d_chunks, plan->nchunks, neg_threshold,
-                           pos_threshold, compr_base);
+                           stream, plan->d_chunks, plan->nchunks, neg_threshold, pos_threshold,
+                           compr_base);
     else
         hipLaunchKernelGGL(compress_2bit_multi_kernel<false>, dim3(blocks), dim3(kThreads), 0,
-                           stream, plan->d_tensors, plan->d_chunks, plan->nchunks, neg_threshold,
-                           pos_threshold, compr_base);
+                           stream, plan->d_chunks, plan->nchunks, neg_threshold, pos_threshold,
+                           compr_base);
     return check_launch("compress_2bit_multi");
 }
 
@@ -600,15 +598,12 @@ GCQ_API void gc_plan_destroy(gc_plan* plan)
 {
     if (!plan)
         return;
-    if (plan->d_tensors || plan->d_chunks) {
+    if (plan->d_chunks) {
         int cur = 0;
         (void)hipGetDevice(&cur);
         (void)hipSetDevice(plan->device);
         (void)hipDeviceSynchronize();
-        if (plan->d_tensors)
-            (void)hipFree(plan->d_tensors);
-        if (plan->d_chunks)
-            (void)hipFree(plan->d_chunks);
+        (void)hipFree(plan->d_chunks);
         (void)hipSetDevice(cur);
     }
     delete plan;
