@@ -420,7 +420,7 @@ struct gc_plan {
 
 using namespace gcq;
 
-GCQ_API size_t gc_compressed_2bit_words(size_t n) { return 3 + (n + 15) / 16; }
+GCQ_API size_t gc_compressed_2bit_words(size_t n) { return 3 + n / 16 + (n % 16 != 0 ? 1 : 0); }
 
 GCQ_API int compress_2bit(const float* grad, float* residual, size_t n, float neg_threshold,
                           float pos_threshold, uint32_t* compr, hipStream_t stream)

@@ -60,7 +60,7 @@ def test_library_exports_exactly_the_declared_symbols(lib):
     assert exported == names, (exported - names, names - exported)
 
 
-@pytest.mark.parametrize("n", [0, 1, 15, 16, 17, 4096, 25_557_032, 2 ** 33 + 5])
+@pytest.mark.parametrize("n", [0, 1, 15, 16, 17, 4096, 25_557_032, 2 ** 33 + 5, 2 ** 64 - 1])
 def test_compressed_words_matches_oracle(lib, n):
     assert lib.gc_compressed_2bit_words(n) == 3 + (n + 15) // 16
     if n < 10 ** 8:
