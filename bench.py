@@ -141,6 +141,24 @@ def traffic_from_profile(kernel: str) -> int | None:
     return int(m_b.group(1))
 
 
+# VALU peak: 256 CUs x 64 lanes (four 16-lane SIMDs) x 2.4 GHz, one
+# non-packed VALU instruction per lane per cycle.
+VALU_PEAK_T_LANE_INSTS = 256 * 64 * 2.4e9 / 1e12
+
+
+def valu_insts_from_profile(kernel: str) -> int | None:
+    """SQ_INSTS_VALU (wave-level VALU instructions) per launch of `kernel`
+    from the committed rocprofv3 summary, if taken on the current sources."""
+    if not PROFILE_VALU.exists():
+        return None
+    text = PROFILE_VALU.read_text()
+    m_h = re.search(r"^kernel_source_sha256:\s*([0-9a-f]+)", text, re.M)
+    m_v = re.search(rf"^valu_insts_per_launch\[{kernel}\]:\s*([0-9]+)", text, re.M)
+    if not (m_v and m_h) or m_h.group(1) != kernel_source_hash():
+        return None
+    return int(m_v.group(1))
+
+
 def _read_counters(path: pathlib.Path):
     import csv
     import collections
@@ -193,7 +211,11 @@ def summarize_valu(d: pathlib.Path) -> pathlib.Path | None:
         cs = rows[k]
         lines.append(f"| {k} | {len(cs.get('SQ_INSTS_VALU', []))} | {mean(cs.get('VALUBusy', [])):.1f} | "
                      f"{mean(cs.get('SQ_INSTS_VALU', [])):,.0f} | {mean(cs.get('SQ_INSTS_LDS', [])):,.0f} |")
-    lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
+    lines += ["", "Machine-readable (bench.py reads these while the kernel sources are unchanged):",
+              "", f"kernel_source_sha256: {kernel_source_hash()}"]
+    lines += [f"valu_insts_per_launch[{k}]: {int(round(mean(rows[k]['SQ_INSTS_VALU'])))}"
+              for k in sorted(rows) if rows[k].get("SQ_INSTS_VALU")]
+    lines.append("")
     PROFILE_VALU.write_text("\n".join(lines))
     return PROFILE_VALU
 
@@ -518,6 +540,22 @@ def bench_qsgd(gcq, torch, np, si, steps: int):
     torch.cuda.empty_cache()
     mean = lambda v: sum(v) / len(v)  # noqa: E731
     t = mean(tot) / 1e3
+    # the quantize is bound by VALU issue: its roofline counts VALU lane-
+    # instructions (from the committed counter profile) over the live
+    # per-launch time; the max-norm's is HBM bytes
+    q_launch_s = mean(qz) / W / 1e3
+    vi = valu_insts_from_profile("qsgd_quantize_kernel")
+    alu = None
+    if vi is not None:
+        ach = vi * 64 / q_launch_s / 1e12
+        alu = {"bound": "alu", "kernel": "qsgd_quantize", "achieved": round(ach, 2),
+               "peak": round(VALU_PEAK_T_LANE_INSTS, 2), "unit": "T VALU lane-instructions/s",
+               "frac": round(ach / VALU_PEAK_T_LANE_INSTS, 4), "valu_insts_per_launch": vi,
+               "launch_ms": round(q_launch_s * 1e3, 5)}
+    mx_gbs = 4 * W * n / (mean(mx) / 1e3) / 1e9
+    hbm = {"bound": "hbm", "kernel": "qsgd_global_maxnorm", "achieved": round(mx_gbs, 1),
+           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(mx_gbs / HBM_PEAK_GBS, 4),
+           "traffic": traffic_from_profile("maxabs_partial_kernel")}
     fused = {
         "workload": "the same step with qsgd_quantize_sum (W quantizes + level sum + dequantize "
                     "in one pass; the int8 levels are not written)",
@@ -538,6 +576,8 @@ def bench_qsgd(gcq, torch, np, si, steps: int):
                        "dequant_sum": (W + 8) * n / (mean(ds) / 1e3) / 1e9},
         "algorithmic_bytes": (4 * W + 5 * W + W + 8) * n,
         "steps": steps,
+        "roofline": alu,
+        "roofline_maxnorm": hbm,
         "fused": fused,
     }
 
