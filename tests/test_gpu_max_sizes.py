@@ -30,6 +30,8 @@ GiB = 1 << 30
 
 
 def need(bytes_):
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()  # memory earlier tests left in torch's cache
     free, _ = torch.cuda.mem_get_info()
     if free < bytes_ + 4 * GiB:
         pytest.skip(f"needs {bytes_ / GiB:.0f} GiB of free device memory, {free / GiB:.0f} GiB free")
