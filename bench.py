@@ -54,33 +54,33 @@ KERNEL_SOURCES = [ROOT / "gradient_compression_quantize_amd" / "csrc" / f
                             "qsgd.hip")]
 
 # The rocprofv3 runs the committed summaries come from (run from the repo
-# root; the output directories are scratch).
+# root; prof_out/ is scratch output, not kept in the repository).
 PROFILE_COMMANDS = {
-    "trace": "rocprofv3 --kernel-trace --stats -T -d gpurun_out/prof_bench -o bench "
+    "trace": "rocprofv3 --kernel-trace --stats -T -d prof_out/prof_bench -o bench "
              "--output-format csv -- python3 -u bench.py --steps 20 --warmup 5 --qsgd-steps 5 "
              "--skip-cpu-baseline --skip-extra",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_fetch -o fetch --output-format csv "
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -T -d prof_out/pmc_fetch -o fetch --output-format csv "
              "-- python3 -u bench.py --steps 3 --warmup 1 --qsgd-steps 1 --skip-cpu-baseline "
              "--skip-extra",
-    "write": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_write -o write --output-format csv "
+    "write": "rocprofv3 --pmc WRITE_SIZE -T -d prof_out/pmc_write -o write --output-format csv "
              "-- python3 -u bench.py --steps 3 --warmup 1 --qsgd-steps 1 --skip-cpu-baseline "
              "--skip-extra",
-    "trace_extra": "rocprofv3 --kernel-trace --stats -T -d gpurun_out/prof_extra -o extra "
+    "trace_extra": "rocprofv3 --kernel-trace --stats -T -d prof_out/prof_extra -o extra "
                    "--output-format csv -- python3 -u bench.py --extras-only",
-    "fetch_extra": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_fetch_extra -o fetch "
+    "fetch_extra": "rocprofv3 --pmc FETCH_SIZE -T -d prof_out/pmc_fetch_extra -o fetch "
                    "--output-format csv -- python3 -u bench.py --extras-only --extra-steps 3",
-    "write_extra": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_write_extra -o write "
+    "write_extra": "rocprofv3 --pmc WRITE_SIZE -T -d prof_out/pmc_write_extra -o write "
                    "--output-format csv -- python3 -u bench.py --extras-only --extra-steps 3",
-    "valu": "rocprofv3 --pmc VALUBusy SQ_INSTS_VALU SQ_INSTS_LDS -T -d gpurun_out/pmc_valu -o valu "
+    "valu": "rocprofv3 --pmc VALUBusy SQ_INSTS_VALU SQ_INSTS_LDS -T -d prof_out/pmc_valu -o valu "
             "--output-format csv -- python3 -u bench.py --steps 3 --warmup 1 --qsgd-steps 1 "
             "--skip-cpu-baseline --skip-extra",
-    "valu_extra": "rocprofv3 --pmc VALUBusy SQ_INSTS_VALU SQ_INSTS_LDS -T -d gpurun_out/pmc_valu_extra "
+    "valu_extra": "rocprofv3 --pmc VALUBusy SQ_INSTS_VALU SQ_INSTS_LDS -T -d prof_out/pmc_valu_extra "
                   "-o valu --output-format csv -- python3 -u bench.py --extras-only --extra-steps 3",
-    "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -T -d gpurun_out/pmc_cal_fetch -o cal "
+    "cal_fetch": "rocprofv3 --pmc FETCH_SIZE -T -d prof_out/pmc_cal_fetch -o cal "
                  "--output-format csv -- python3 -u bench.py --calibrate-copy",
-    "cal_write": "rocprofv3 --pmc WRITE_SIZE -T -d gpurun_out/pmc_cal_write -o cal "
+    "cal_write": "rocprofv3 --pmc WRITE_SIZE -T -d prof_out/pmc_cal_write -o cal "
                  "--output-format csv -- python3 -u bench.py --calibrate-copy",
-    "summary": "python3 bench.py --summarize-profiles gpurun_out",
+    "summary": "python3 bench.py --summarize-profiles prof_out",
 }
 
 

@@ -51,8 +51,8 @@ def load() -> ctypes.CDLL:
     if _lib is None:
         if not LIB_PATH.exists():
             raise RuntimeError(
-                f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
-                "(or python gradient_compression_quantize_amd/build.py)")
+                f"{LIB_PATH} is missing: build it with "
+                "python gradient_compression_quantize_amd/build.py")
         _lib = _declare(ctypes.CDLL(str(LIB_PATH)))
     return _lib
 

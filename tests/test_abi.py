@@ -34,7 +34,7 @@ def declared_functions() -> set[str]:
 @pytest.fixture(scope="module")
 def lib():
     if not gcq.LIB_PATH.exists():
-        pytest.fail("libgcq.so is not built (run __graft_entry__.build())")
+        pytest.fail("libgcq.so is not built (python gradient_compression_quantize_amd/build.py)")
     return gcq.load()
 
 

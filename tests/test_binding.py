@@ -38,7 +38,7 @@ class FakeStream:
 @pytest.fixture(scope="module", autouse=True)
 def lib():
     if not gcq.LIB_PATH.exists():
-        pytest.fail("libgcq.so is not built (run __graft_entry__.build())")
+        pytest.fail("libgcq.so is not built (python gradient_compression_quantize_amd/build.py)")
     gcq.load()
 
 
