@@ -189,66 +189,81 @@ __global__ __launch_bounds__(kFinalThreads) void max_final_kernel(const float* _
 // where floor(x * 2^24) < 2^31 and k < 2^24, so the sum fits in 32 bits.
 // s24 = s * 2^24 is exact, and fl(q * s24) = fl(q * s) * 2^24 whenever
 // fl(q * s) is a normal number; below that x < 2^-126 and every path gives
-// level 0. The conversion truncates, which is the floor for X >= 0.
+// level 0.
+//
+// The sign goes into the same integer. Scaling g itself (not |g|) gives
+// X = sign(g) * |X| exactly (every step is sign-symmetric), and the
+// truncating conversion gives F = sign(g) * floor(|X|). A value with its sign
+// bit set adds k' = (~r) >> 8 = 2^24 - 1 - k instead of k: for an integer
+// A = floor(|X|) + k >= 0, floor((2^24 - 1 - A) / 2^24) = -floor(A / 2^24),
+// so the arithmetic shift of the "slot" F + k' by 24 is the signed level
+// -floor(x + u). Either way the level is the slot's top byte read as int8
+// (|level| <= 127), which is the two's-complement byte the wire carries.
 //
 // The quotient: the exact path divides (IEEE, correctly rounded) and then
 // scales by s24. The fast path multiplies once, by c = fl(fl(1 / norm) * s24).
-// Each side takes rounded steps (fl(1/norm), fl(inv * s24), fl(a * c); and
-// fl(a / norm), fl(q * s24)), every one within 2^-24 relative of its real
+// Each side takes rounded steps (fl(1/norm), fl(inv * s24), fl(g * c); and
+// fl(g / norm), fl(q * s24)), every one within 2^-24 relative of its real
 // value while its result is a normal number -- which holds wherever the
-// level can be nonzero (X >= 1 needs a / norm >= 2^-31). So for |g| <= norm
-// the two values of X differ by at most 5 * 2^-24 * X < 5 * 127 = 635. With
-// t = floor(X) + k, the exact t therefore lies within kSlack = 2048 of the
-// fast one; when t - kSlack and t + kSlack fall in the same 2^24 bucket the
-// fast level is the exact level. Otherwise (about one value in 4000) the
-// lane recomputes its slot through the division. `fast` is false when norm
-// is so small that c could overflow (norm < 2^-96; c <= 2^96 * 127 * 2^24
-// stays finite): then every value divides.
+// level can be nonzero (|X| >= 1 needs |g| / norm >= 2^-31). So for
+// |g| <= norm the two values of |X| differ by at most 5 * 2^-24 * |X| <
+// 5 * 127 = 635, and so do the two slots. The fast slot carries a bias of
+// kSlack = 2048: when it lies at least 2 kSlack above a multiple of 2^24, the
+// exact (unbiased) slot lies in [fast - 2 kSlack, fast] and so in the same
+// 2^24 bucket, and the fast level is the exact level. Otherwise (about one
+// value in 4000) the four values of the float4 are recomputed through the
+// division. `fast` is false when norm is so small that c could overflow
+// (norm < 2^-96; c <= 2^96 * 127 * 2^24 stays finite): then every value
+// divides.
 constexpr uint32_t kSlack = 2048;
-
-__device__ __forceinline__ uint32_t level_from_quotient(float q, uint32_t r, float s24)
-{
-    return (static_cast<uint32_t>(q * s24) + (r >> 8)) >> 24;
-}
 
 // Smallest norm for which the fast path's multiplier stays finite.
 constexpr float kFastNormMin = 0x1p-96f;
 
-// Levels of four values (one float4 slot and its four Philox words), with the
-// sign of g applied. One branch per slot: the exact path runs for the slot
-// when any of its values is near a bucket edge, or when `fast` is off.
-// c = fl(fl(1 / norm) * s24) when fast.
-__device__ __forceinline__ void qsgd_levels4(f32x4 g, U4 r, float norm, float c, float s24,
-                                             bool fast, int lv[4])
+// Level slots of four values (one float4 slot and its four Philox words):
+// the level of value k is t[k] >> 24 (arithmetic), and byte 3 of t[k].
+// c = fl(fl(1 / norm) * s24) when fast. `fast` is uniform across the launch,
+// so its test is a scalar branch; the exact branch is taken per lane.
+__device__ __forceinline__ void qsgd_slots4(f32x4 g, U4 r, float norm, float c, float s24,
+                                            bool fast, int32_t t[4])
 {
     const uint32_t rr[4] = {r.x, r.y, r.z, r.w};
-    uint32_t m[4];
-    // t is within kSlack of a multiple of 2^24 iff (t + kSlack) mod 2^24 <
-    // 2 kSlack (t < 2^31 + 2^24, so t + kSlack does not wrap); the test also
-    // flags t < kSlack, which only sends those values to the exact path
-    uint32_t closest = fast ? 0xFFFFFFFFu : 0u;
+    uint32_t k[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t t = static_cast<uint32_t>(fabsf(g[k]) * c) + (rr[k] >> 8);
-        m[k] = t >> 24;
-        closest = min(closest, (t + kSlack) & 0x00FFFFFFu);
+    for (int j = 0; j < 4; ++j) {
+        // 0x00FFFFFF when g has its sign bit set, else 0: v_perm's byte
+        // selector 9 replicates bit 31 of its low operand, 12 gives 0x00
+        const uint32_t flip = __builtin_amdgcn_perm(0u, __float_as_uint(g[j]), 0x0C090909u);
+        k[j] = (rr[j] >> 8) ^ flip;
     }
-    if (closest < 2 * kSlack) {
+    bool exact = true;
+    if (fast) {
+        uint32_t low[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            m[k] = level_from_quotient(fabsf(g[k]) / norm, rr[k], s24);
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t tj = uint32_t(static_cast<int32_t>(g[j] * c)) + k[j] + kSlack;
+            t[j] = int32_t(tj);
+            low[j] = tj & 0x00FFFFFFu;
+        }
+        exact = min(min(low[0], low[1]), min(low[2], low[3])) < 2 * kSlack;
     }
+    if (exact) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int mi = static_cast<int>(m[k]);
-        lv[k] = g[k] < 0.0f ? -mi : mi;
+        for (int j = 0; j < 4; ++j)
+            t[j] = int32_t(uint32_t(static_cast<int32_t>((g[j] / norm) * s24)) + k[j]);
     }
 }
 
-__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d)
+__device__ __forceinline__ int level_of(int32_t slot) { return slot >> 24; }
+
+// The four levels as the little-endian int8 bytes of one word: byte 3 of
+// each slot, gathered by two byte permutes (selector 3 / 7: byte 3 of the
+// low / high operand; 12: 0x00).
+__device__ __forceinline__ uint32_t pack_levels4(const int32_t t[4])
 {
-    return (uint32_t(a) & 0xFFu) | ((uint32_t(b) & 0xFFu) << 8) | ((uint32_t(c) & 0xFFu) << 16) |
-           (uint32_t(d) << 24);
+    const uint32_t lo = __builtin_amdgcn_perm(uint32_t(t[1]), uint32_t(t[0]), 0x0C0C0703u);
+    const uint32_t hi = __builtin_amdgcn_perm(uint32_t(t[3]), uint32_t(t[2]), 0x07030C0Cu);
+    return lo | hi;
 }
 
 // Each wave takes tiles of kQTile float4 slots, kQUnroll per lane: the
@@ -294,9 +309,9 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
                 }
 #pragma unroll
                 for (int u = 0; u < kQUnroll; ++u) {
-                    int lv[4];
-                    qsgd_levels4(g[u], r[u], norm, c, s24, fast, lv);
-                    packed[u] = pack4(lv[0], lv[1], lv[2], lv[3]);
+                    int32_t t[4];
+                    qsgd_slots4(g[u], r[u], norm, c, s24, fast, t);
+                    packed[u] = pack_levels4(t);
                 }
             }
 #pragma unroll
@@ -304,25 +319,50 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
                 __builtin_nontemporal_store(packed[u], reinterpret_cast<uint32_t*>(levels) + q0 +
                                                            size_t(u) * kWave);
         } else {
-#pragma unroll 1
+            // the partial tile, or buffers without the vector alignment.
+            // With the alignment, whole float4 slots are still one load
+            // and one word, and every slot's load goes out before any math
+            // (the registers are zeroed first, so that no branch rewrites
+            // a register with a load in flight); the one slot that
+            // straddles n, and unaligned buffers, go element by element.
+            f32x4 g[kQUnroll];
+#pragma unroll
+            for (int u = 0; u < kQUnroll; ++u)
+                g[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (vec) {
+#pragma unroll
+                for (int u = 0; u < kQUnroll; ++u) {
+                    const size_t q = q0 + size_t(u) * kWave;
+                    if (q < nfull)
+                        g[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(grad) + q);
+                }
+            }
+#pragma unroll
             for (int u = 0; u < kQUnroll; ++u) {
                 const size_t q = q0 + size_t(u) * kWave;
                 if (q >= nslots)
-                    break;
-                f32x4 g;
+                    continue;
+                const bool whole = vec && q < nfull;
+                if (!whole) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    g[k] = (q * 4 + k < n) ? grad[q * 4 + k] : 0.0f;
-                int lv[4] = {0, 0, 0, 0};
+                    for (int k = 0; k < 4; ++k)
+                        g[u][k] = (q * 4 + k < n) ? grad[q * 4 + k] : 0.0f;
+                }
+                int32_t t[4] = {0, 0, 0, 0};
                 if (norm != 0.0f) {
                     const U4 r =
                         philox4x32_10(U4{uint32_t(q), uint32_t(q >> 32), worker, 0u}, k0, k1);
-                    qsgd_levels4(g, r, norm, c, s24, fast, lv);
+                    qsgd_slots4(g[u], r, norm, c, s24, fast, t);
                 }
+                if (whole) {
+                    __builtin_nontemporal_store(pack_levels4(t),
+                                                reinterpret_cast<uint32_t*>(levels) + q);
+                } else {
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    if (q * 4 + k < n)
-                        levels[q * 4 + k] = int8_t(lv[k]);
+                    for (int k = 0; k < 4; ++k)
+                        if (q * 4 + k < n)
+                            levels[q * 4 + k] = int8_t(level_of(t[k]));
+                }
             }
         }
         if (!kLoop)
@@ -476,9 +516,10 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_kernel(
                     for (int dw = 0; dw < kG; ++dw) {
                         if (WC == 0 && w0 + dw >= W)
                             break;
-                        int lv[4];
-                        qsgd_levels4(g[dw], r[dw], norm, c, s24, fast, lv);
-                        S += i32x4{lv[0], lv[1], lv[2], lv[3]};
+                        int32_t t[4];
+                        qsgd_slots4(g[dw], r[dw], norm, c, s24, fast, t);
+                        S += i32x4{level_of(t[0]), level_of(t[1]), level_of(t[2]),
+                                   level_of(t[3])};
                     }
                 }
             }
@@ -492,10 +533,10 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_kernel(
                 for (int k = 0; k < 4; ++k)
                     g[k] = (q * 4 + k < n) ? tab.p[w][q * 4 + k] : 0.0f;
                 if (norm != 0.0f) {
-                    int lv[4];
-                    qsgd_levels4(g, philox4x32_10(U4{ctr0.x, ctr0.y, uint32_t(w), 0u}, k0, k1),
-                                 norm, c, s24, fast, lv);
-                    S += i32x4{lv[0], lv[1], lv[2], lv[3]};
+                    int32_t t[4];
+                    qsgd_slots4(g, philox4x32_10(U4{ctr0.x, ctr0.y, uint32_t(w), 0u}, k0, k1),
+                                norm, c, s24, fast, t);
+                    S += i32x4{level_of(t[0]), level_of(t[1]), level_of(t[2]), level_of(t[3])};
                 }
             }
 #pragma unroll
@@ -723,19 +764,39 @@ constexpr unsigned kGkMaxGatherBlocks = 1024;
 constexpr int kGkQThreads = 256;
 
 // Launch 1 when K <= kRandKLdsMax: workgroup 0 draws the indices in LDS
-// while the others zero the dense output. The draw's 128 KB of LDS holds
+// while the others zero dense[0, fill_n). The draw's 128 KB of LDS holds
 // every workgroup of the launch to one per CU, which at 1024 threads still
 // gives the fill 16 waves per CU.
 __global__ __launch_bounds__(kRandKThreads) void grandk_draw_fill_kernel(
     size_t n, uint32_t K, uint32_t k0, uint32_t k1, uint32_t* __restrict__ idx, int hbits,
-    float* __restrict__ dense, int dense_vec)
+    float* __restrict__ dense, size_t fill_n, int dense_vec)
 {
     if (blockIdx.x == 0) {
         if (K > 0)
             grandk_draw_lds(n, K, k0, k1, idx, hbits);
         return;
     }
-    fill_zero_range<kRandKThreads>(dense, n, dense_vec, blockIdx.x - 1, gridDim.x - 1);
+    fill_zero_range<kRandKThreads>(dense, fill_n, dense_vec, blockIdx.x - 1, gridDim.x - 1);
+}
+
+// Share of the dense fill that runs beside the LDS draw in launch 1; the
+// rest runs beside the gathers in launch 2 (the scatter in launch 3 comes
+// after both). Launch 1 lasts about max(draw, its fill), launch 2 about
+// max(gathers, the rest of the fill), so the split puts about as much fill
+// beside the draw as the draw takes. Measured on MI355X: the draw costs
+// about 1.24 ns per index (12.4 us at K = 10000), the fill about 0.70 ps per
+// value (18 us for 25.6M), a ratio of ~1770; the factor used is a little
+// above it, so that the fill (the longer job) stays on the critical path.
+// Returns n, or a multiple of 4 below n, so that launch 2's part keeps
+// dense's float4 alignment.
+constexpr double kDrawPerFillValue = 1900.0;
+
+size_t grandk_fill_split(size_t n, uint32_t K)
+{
+    const double share = kDrawPerFillValue * double(K) / double(n);
+    if (share >= 1.0)
+        return n;
+    return size_t(share * double(n)) & ~size_t(3);
 }
 
 __global__ __launch_bounds__(kThreads) void grandk_gather_fill_kernel(
@@ -802,12 +863,12 @@ __global__ __launch_bounds__(kGkQThreads) void grandk_quantize_scatter_kernel(
             for (int k = 0; k < 4; ++k)
                 if (q * 4 + k >= K)
                     g[k] = 0.0f;
-            int lv[4];
-            qsgd_levels4(g, philox4x32_10(U4{uint32_t(q), uint32_t(q >> 32), uint32_t(w), 0u}, k0, k1),
-                         norm, c, s24, fast, lv);
+            int32_t t[4];
+            qsgd_slots4(g, philox4x32_10(U4{uint32_t(q), uint32_t(q >> 32), uint32_t(w), 0u}, k0, k1),
+                        norm, c, s24, fast, t);
 #pragma unroll
             for (int k = 0; k < 4; ++k)
-                atomicAdd(&lsum[ls][k], lv[k]);
+                atomicAdd(&lsum[ls][k], level_of(t[k]));
         }
         __syncthreads();
         for (int e = threadIdx.x; e < spb * 4; e += kGkQThreads) {
@@ -1132,13 +1193,14 @@ GCQ_API int grandk_mn_step(const float* const* grads, int W, size_t n, uint32_t 
     const int dense_vec = aligned16(dense) ? 1 : 0;
     // launch 1: the shared index draw; with the draw in LDS, the dense zero
     // fill runs beside it in the same launch
-    size_t fill_blocks = 0;  // fill workgroups left for launch 2
+    size_t split = 0;  // dense[0, split) is zeroed in launch 1, the rest in launch 2
     if (K <= kRandKLdsMax) {
+        split = grandk_fill_split(n, K);
         const size_t fb = std::max<size_t>(
-            1, std::min(ceil_div(ceil_div(n, 4 * kFillUnroll), kRandKThreads),
+            1, std::min(ceil_div(ceil_div(split, 4 * kFillUnroll), kRandKThreads),
                         cap > 1 ? cap - 1 : 1));
         hipLaunchKernelGGL(grandk_draw_fill_kernel, dim3(unsigned(1 + fb)), dim3(kRandKThreads),
-                           0, stream, n, K, k0, k1, idx, randk_lds_hash_bits(K), dense,
+                           0, stream, n, K, k0, k1, idx, randk_lds_hash_bits(K), dense, split,
                            dense_vec);
     } else {
         const int hbits = randk_hash_bits(K);
@@ -1147,16 +1209,18 @@ GCQ_API int grandk_mn_step(const float* const* grads, int W, size_t n, uint32_t 
         int32_t* next = reinterpret_cast<int32_t*>(target + K);
         hipLaunchKernelGGL(grandk_indices_kernel, dim3(1), dim3(kRandKThreads), 0, stream, n, K,
                            k0, k1, idx, target, next, heads, hbits);
-        fill_blocks = std::max<size_t>(
-            1, std::min(ceil_div(ceil_div(n, 4 * kFillUnroll), kThreads),
-                        cap > L.gather_blocks ? cap - L.gather_blocks : 1));
     }
     if (int rc = check_launch("grandk_mn_step (draw)"))
         return rc;
-    // launch 2: gathers and partial maxima (and the fill, if not done above)
+    // launch 2: gathers and partial maxima, and the fill of dense[split, n)
+    const size_t rest = n - split;
+    const size_t fill_blocks =
+        rest == 0 ? 0
+                  : std::max<size_t>(1, std::min(ceil_div(ceil_div(rest, 4 * kFillUnroll), kThreads),
+                                                 cap > L.gather_blocks ? cap - L.gather_blocks : 1));
     hipLaunchKernelGGL(grandk_gather_fill_kernel, dim3(unsigned(L.gather_blocks + fill_blocks)),
                        dim3(kThreads), 0, stream, tab, W, K, L.Kp, idx, gathered, partials,
-                       L.gather_blocks, dense, n, dense_vec);
+                       L.gather_blocks, dense + split, rest, dense_vec);
     if (int rc = check_launch("grandk_mn_step (gather, fill)"))
         return rc;
     // launch 3: norm, levels, sum, dequantize, scatter

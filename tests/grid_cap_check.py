@@ -136,8 +136,16 @@ def main():
                          oracle.scatter_dense(oracle.qsgd_dequantize(sk, norm_or, s), idx, n)),
           "scatter-dequantize")
     # the one-call GRandK step: one gather workgroup striding, a capped fill
-    print("[case] capped grandk_mn_step", flush=True)
-    n, K, W, s, seed = 200_003, 7_001, 8, 7, 9
+    # (all of it beside the draw at n = 200,003; split between the first two
+    # launches at n = 2,000,003)
+    for n, K in ((200_003, 7_001), (2_000_003, 150)):
+        capped_grandk_step(n, K)
+    print("OK", flush=True)
+
+
+def capped_grandk_step(n, K):
+    print(f"[case] capped grandk_mn_step n={n} K={K}", flush=True)
+    W, s, seed = 8, 7, 9
     gs = [si.normal_f32(500 + w, n, 0.01) for w in range(W)]
     g_dev = [gu.dev(g) for g in gs]
     idx = gu.empty(K, torch.int32)
@@ -153,8 +161,7 @@ def main():
     check(np.array_equal(gu.host(idx, np.uint32), idx_or), "grandk_mn_step indices")
     check(np.array_equal(gu.host(sums), S), "grandk_mn_step sums")
     check(np.array_equal(gu.host(dense), oracle.scatter_dense(oracle.qsgd_dequantize(S, nrm, s), idx_or, n)),
-          "grandk_mn_step dense")
-    print("OK", flush=True)
+          f"grandk_mn_step dense n={n} K={K}")
 
 
 if __name__ == "__main__":

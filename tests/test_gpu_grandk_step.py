@@ -61,7 +61,11 @@ def check(got, expect):
 @pytest.mark.parametrize("n,K,W,s", [(1, 1, 1, 127), (1, 0, 2, 7), (7, 7, 3, 7), (1000, 999, 8, 7),
                                      (100_003, 10_000, 8, 7), (65_536, 16_384, 4, 15),
                                      (70_001, 16_385, 5, 7), (300_007, 40_000, 9, 127),
-                                     (20_000, 5_003, 64, 3), (5_000, 4_001, 2, 1)])
+                                     (20_000, 5_003, 64, 3), (5_000, 4_001, 2, 1),
+                                     # n above ~1900 K: the dense fill is split between the
+                                     # draw's launch and the gathers' launch
+                                     (2_000_003, 100, 8, 7), (10_001, 0, 3, 7), (5_000, 1, 2, 7),
+                                     (4_000_000, 2_000, 4, 127)])
 def test_grandk_mn_step_small(gcq, n, K, W, s):
     announce(f"grandk_mn_step n={n} K={K} W={W} s={s}")
     seed = 0x9A9A + n + K
@@ -70,9 +74,10 @@ def test_grandk_mn_step_small(gcq, n, K, W, s):
 
 
 @pytest.mark.parametrize("misalign", [False, True])
-def test_grandk_mn_step_misaligned_dense_without_sums(gcq, misalign):
-    announce(f"grandk_mn_step dense misalign={misalign}, no sums")
-    n, K, W, s, seed = 123_457, 3_001, 8, 7, 11
+@pytest.mark.parametrize("n,K", [(123_457, 3_001), (1_000_001, 50)])
+def test_grandk_mn_step_misaligned_dense_without_sums(gcq, misalign, n, K):
+    announce(f"grandk_mn_step dense misalign={misalign}, no sums, n={n} K={K}")
+    W, s, seed = 8, 7, 11
     grads = [si.heavy_tailed_f32(si.grad_seed(w, 8), n, 0.02) for w in range(W)]
     idx, S, dense, norm = run_step(gcq, grads, K, s, seed, misalign=misalign, with_sums=False)
     assert S is None

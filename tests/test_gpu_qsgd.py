@@ -55,7 +55,8 @@ def check_deq(got, expect):
 
 @pytest.mark.parametrize("misalign", [False, True])
 @pytest.mark.parametrize("W,n,s", [(1, 1, 127), (2, 5, 7), (3, 4097, 127), (8, 1000, 1),
-                                   (5, 65536 + 3, 15), (64, 777, 127), (8, 1 << 20, 127)])
+                                   (5, 65536 + 3, 15), (64, 777, 127), (8, 1 << 20, 127),
+                                   (4, 5003, 7)])
 def test_qsgd_step_small(gcq, W, n, s, misalign):
     announce(f"qsgd W={W} n={n} s={s} misalign={misalign}")
     seed = 0xABCDEF0123 + n
