@@ -5,6 +5,9 @@ Python binding of ``libgcq.so`` (HIP kernels for gfx950 behind the C ABI of
 and only marshals arguments: torch tensors supply device memory and the
 stream, and every step of the computation runs in the library's kernels.
 There is no fallback: if ``libgcq.so`` is missing, ``load()`` raises.
+Tensors must be contiguous, of the documented dtype, and on torch's current
+device, which is where the library launches (an explicit ``stream`` must
+belong to that device too); anything else is refused before the call.
 
 Two method families (see include/gcq.h for exact semantics):
   * 2-bit threshold quantization with residual error feedback (apache MXNet
@@ -117,14 +120,37 @@ def _torch():
     return torch
 
 
+_gpu_present = None
+
+
+def _current_device():
+    """Index of torch's current device, or None when torch sees no GPU (then
+    there is nothing to compare against: every call fails validation or its
+    device-tensor checks first)."""
+    global _gpu_present
+    torch = _torch()
+    if _gpu_present is None:
+        _gpu_present = bool(torch.cuda.is_available())
+    return torch.cuda.current_device() if _gpu_present else None
+
+
 def _stream(stream) -> ctypes.c_void_p:
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
+    if stream is None:
+        s = torch.cuda.current_stream()
+    else:
+        s = stream
+        dev = getattr(s, "device", None)
+        cur = _current_device()
+        if dev is not None and cur is not None and dev.index != cur:
+            raise ValueError(f"stream is on cuda:{dev.index} but the current device is "
+                             f"cuda:{cur}; the library launches on the current device")
     return _vp(s.cuda_stream)
 
 
 def _dev(t, dtype, what: str) -> ctypes.c_void_p:
-    """Device pointer of a contiguous CUDA tensor of the given dtype."""
+    """Device pointer of a contiguous tensor of the given dtype on the current
+    device (the device the library launches on)."""
     if t is None:
         return _vp(None)
     if not t.is_cuda:
@@ -133,6 +159,10 @@ def _dev(t, dtype, what: str) -> ctypes.c_void_p:
         raise TypeError(f"{what}: expected {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise TypeError(f"{what}: expected a contiguous tensor")
+    cur = _current_device()
+    if cur is not None and t.get_device() != cur:
+        raise ValueError(f"{what}: on cuda:{t.get_device()} but the current device is "
+                         f"cuda:{cur}; the library launches on the current device")
     return _vp(t.data_ptr())
 
 

@@ -17,6 +17,7 @@ class FakeDev:
     def __init__(self, n, dtype=torch.float32, contiguous=True, addr=0x10000):
         self._n, self.dtype, self._c, self._a = n, dtype, contiguous, addr
         self.is_cuda = True
+        self.device_index = 0
 
     def numel(self):
         return self._n
@@ -29,6 +30,9 @@ class FakeDev:
 
     def data_ptr(self):
         return self._a
+
+    def get_device(self):
+        return self.device_index
 
 
 class FakeStream:
@@ -63,6 +67,28 @@ def test_dtype_and_layout_are_checked():
     with pytest.raises(TypeError, match="contiguous"):
         gcq.decompress_2bit(FakeDev(words, torch.int32), n, FakeDev(n, contiguous=False),
                             stream=FakeStream())
+
+
+def test_tensors_and_streams_on_another_device_are_rejected(monkeypatch):
+    """The library launches on the current device: a tensor or an explicit
+    stream on another one is refused before any call (torch's device queries
+    are stubbed so that the check runs without a GPU)."""
+    monkeypatch.setattr(gcq, "_gpu_present", True)
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
+    n = 64
+    words = gcq.gc_compressed_2bit_words(n)
+    other = FakeDev(n)
+    other.device_index = 1
+    with pytest.raises(ValueError, match="residual: on cuda:1 but the current device is cuda:0"):
+        gcq.compress_2bit(FakeDev(n), other, -1.0, 1.0, FakeDev(words, torch.int32),
+                          stream=FakeStream())
+
+    class OtherStream(FakeStream):
+        device = torch.device("cuda", 1)
+
+    with pytest.raises(ValueError, match="stream is on cuda:1"):
+        gcq.compress_2bit(FakeDev(n), FakeDev(n), -1.0, 1.0, FakeDev(words, torch.int32),
+                          stream=OtherStream())
 
 
 def test_undersized_buffers_are_rejected():
