@@ -23,8 +23,10 @@
  *    path.
  *  - Return value: GC_OK, or a negative gc_status. Arguments are validated
  *    on the host before anything is enqueued; on GC_EINVAL nothing was
- *    enqueued. GC_EHIP reports a failed launch. gc_last_error() gives a
- *    message for the calling thread's last failure.
+ *    enqueued. GC_EHIP reports a failed launch, read from HIP's last-error
+ *    state of the calling thread right after the launch (so an error left
+ *    pending there by an earlier HIP call surfaces here too). gc_last_error()
+ *    gives a message for the calling thread's last failure.
  *  - Inputs and outputs of one call must not overlap unless stated.
  *  - Alignment: a 16-byte-aligned float/int8 buffer takes the vectorized
  *    path; any 4-byte-aligned float buffer is accepted. Results are
