@@ -123,6 +123,22 @@ def main():
     s_or = oracle.level_sum(lv_or)
     check(np.array_equal(gu.host(sums), s_or), "qsgd sums")
     check(np.array_equal(gu.host(out), oracle.qsgd_dequantize(s_or, norm_or, s)), "qsgd dequantized")
+    # the fused quantize + level sum: W read at run time (3) and known at
+    # compile time (8), many more tiles than waves
+    for Wf in (3, 8):
+        print(f"[case] capped qsgd_quantize_sum W={Wf}", flush=True)
+        gf = gs if Wf == W else [si.heavy_tailed_f32(600 + w, n, 0.02) for w in range(Wf)]
+        gf_dev = [gu.dev(g) for g in gf]
+        nrm_f = oracle.maxnorm(gf)
+        norm_f = torch.tensor([nrm_f], dtype=torch.float32, device=gu.DEV)
+        sums_f = gu.empty(n, torch.int32)
+        out_f = gu.empty(n, torch.float32, fill=float("nan"))
+        gcq.qsgd_quantize_sum(gf_dev, norm_f, s, seed, out_f, sums=sums_f)
+        gu.sync()
+        S_f = oracle.level_sum([oracle.qsgd_quantize(g, nrm_f, s, seed, w) for w, g in enumerate(gf)])
+        check(np.array_equal(gu.host(sums_f), S_f), f"qsgd_quantize_sum sums W={Wf}")
+        check(np.array_equal(gu.host(out_f), oracle.qsgd_dequantize(S_f, nrm_f, s)),
+              f"qsgd_quantize_sum dequantized W={Wf}")
     idx = oracle.randk_indices(n, 5000, 3)
     gk = gu.empty(5000, torch.float32)
     gcq.gather_f32(g_dev[0], gu.dev(idx), gk)
