@@ -194,7 +194,9 @@ int qsgd_global_maxnorm(const float* const* grads, int W, size_t n,
  *   r = word (i mod 4) of Philox(key = (seed lo, seed hi),
  *                                counter = (i/4 lo, i/4 hi, worker, 0)),
  *   levels = 0 everywhere when *norm == 0.
- *   grad    [n] fp32;  norm  device fp32 scalar, >= max |grad|
+ *   grad    [n] fp32, finite (a NaN or infinite value, or an infinite
+ *           norm, gets an unspecified level);  norm  device fp32 scalar,
+ *           >= max |grad|
  *   s       1 .. 127 (levels lie in [-s, s]);  levels [n] int8 */
 int qsgd_maxnorm_quantize(const float* grad, size_t n, const float* norm,
                           int s, uint64_t seed, uint32_t worker,
