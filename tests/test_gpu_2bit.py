@@ -134,6 +134,35 @@ def test_dequantize_sum(gcq, W, n):
         np.testing.assert_array_equal(got, expect)  # same order -> bit-exact
 
 
+@pytest.mark.parametrize("W", [1, 3, 8])
+@pytest.mark.parametrize("n", [16, 1000, 4097, 100_003])
+def test_dequantize_arbitrary_words(gcq, W, n):
+    """Blocks whose words hold random bits: every 2-bit pattern occurs,
+    including 11, which the compressor never writes and which decodes to 0,
+    and the bits past n in the last word are not zero (they must be
+    ignored)."""
+    announce(f"2-bit dequantize of arbitrary words W={W} n={n}")
+    rng = np.random.default_rng(131 * n + W)
+    comprs = []
+    for w in range(W):
+        c = rng.integers(0, 2 ** 32, oracle.compressed_2bit_words(n), dtype=np.uint64).astype(np.uint32)
+        c[0] = np.float32(-0.25 - 0.01 * w).view(np.uint32)
+        c[1] = np.float32(0.5 + 0.01 * w).view(np.uint32)
+        c[2] = np.float32(n).view(np.uint32)
+        comprs.append(c)
+    codes = (comprs[0][3:, None] >> np.arange(30, -2, -2, dtype=np.uint32)) & 3
+    assert np.any(codes == 3)
+    out = gu.empty(n, torch.float32, fill=float("nan"))
+    gcq.decompress_2bit(gu.dev(comprs[0]), n, out)
+    gu.sync()
+    np.testing.assert_array_equal(gu.host(out), oracle.dequantize_2bit(comprs[0], n))
+    for misalign in (False, True):
+        out = gu.empty(n, torch.float32, misalign=misalign, fill=float("nan"))
+        gcq.decompress_2bit_sum([gu.dev(c) for c in comprs], n, out)
+        gu.sync()
+        np.testing.assert_array_equal(gu.host(out), oracle.dequantize_2bit_sum(comprs, n))
+
+
 @pytest.mark.slow
 def test_resnet50_flat_gradient_full_size(gcq):
     """25,557,032 values, W = 8 workers x 5 error-feedback iterations, then

@@ -72,6 +72,26 @@ def test_qsgd_step_small(gcq, W, n, s, misalign):
     check_deq(out, oracle.qsgd_dequantize(s_or, norm_or, s))
 
 
+@pytest.mark.parametrize("W,n", [(1, 1000), (3, 4097), (8, 100_003), (13, 777)])
+def test_level_sum_of_arbitrary_levels(gcq, W, n):
+    """The level sum and dequantize take any int8 levels, -128 and 127
+    included: the int32 sums are exact whatever the inputs."""
+    announce(f"qsgd level sum of arbitrary int8 levels W={W} n={n}")
+    rng = np.random.default_rng(977 * n + W)
+    levels = [rng.integers(-128, 128, n, dtype=np.int64).astype(np.int8) for _ in range(W)]
+    levels[0][:2] = (-128, 127)
+    norm_v, s = np.float32(0.0371), 127
+    norm = torch.tensor([norm_v], dtype=torch.float32, device=gu.DEV)
+    S_or = oracle.level_sum(levels)
+    for misalign in (False, True):
+        sums = gu.empty(n, torch.int32, misalign=misalign, fill=-7)
+        out = gu.empty(n, torch.float32, misalign=misalign, fill=float("nan"))
+        gcq.qsgd_dequant_sum([gu.dev(q, misalign) for q in levels], norm, s, out, sums=sums)
+        gu.sync()
+        np.testing.assert_array_equal(gu.host(sums), S_or)
+        check_deq(gu.host(out), oracle.qsgd_dequantize(S_or, norm_v, s))
+
+
 def test_qsgd_zero_gradient(gcq):
     announce("qsgd all-zero gradients")
     grads = [np.zeros(1000, np.float32), np.array([-0.0] * 1000, np.float32)]
