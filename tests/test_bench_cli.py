@@ -1,6 +1,7 @@
 """bench.py's command-line contract, on the CPU: more than one GPU is
 refused with a message (this library runs on one GPU), and a run with no
-GPU visible fails with a message instead of printing a result line."""
+GPU visible fails with a message instead of printing a result line. Also
+the rule that names a kernel's roofline bound."""
 import json
 import os
 import pathlib
@@ -38,3 +39,24 @@ def test_no_gpu_no_result_line():
         except ValueError:
             continue
         assert "value" not in obj
+
+
+def test_roofline_names_the_higher_fraction(monkeypatch):
+    """A kernel near both ceilings reports its HBM and VALU fractions over
+    the same launch time and is called bound by the higher one; without a
+    profile taken on these sources the VALU half is absent."""
+    sys.path.insert(0, str(ROOT))
+    import bench
+    monkeypatch.setattr(bench, "traffic_from_profile", lambda k: None)
+    monkeypatch.setattr(bench, "valu_insts_from_profile", lambda k: None)
+    r = bench.hbm_alu_roofline("k", "k_kernel", 4_000_000_000, 1e-3)  # 4 TB/s
+    assert r["bound"] == "hbm" and r["alu"] is None and abs(r["frac"] - 0.5) < 1e-9
+    # 0.8 of the VALU peak over 1 ms: more than the HBM half
+    insts = int(0.8 * bench.VALU_PEAK_T_LANE_INSTS * 1e12 * 1e-3 / 64)
+    monkeypatch.setattr(bench, "valu_insts_from_profile", lambda k: insts)
+    r = bench.hbm_alu_roofline("k", "k_kernel", 4_000_000_000, 1e-3)
+    assert r["bound"] == "alu" and abs(r["alu"]["frac"] - 0.8) < 1e-3
+    # 0.3 of it: HBM stays the bound
+    insts = int(0.3 * bench.VALU_PEAK_T_LANE_INSTS * 1e12 * 1e-3 / 64)
+    monkeypatch.setattr(bench, "valu_insts_from_profile", lambda k: insts)
+    assert bench.hbm_alu_roofline("k", "k_kernel", 4_000_000_000, 1e-3)["bound"] == "hbm"
