@@ -36,6 +36,8 @@ if str(ROOT) not in sys.path:
     sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+# values per worker in the oracle's timed QSGD-MN sample
+QSGD_ORACLE_SAMPLE = 1 << 22
 N_C2 = 25_557_032              # ResNet-50 parameter count
 W_C2 = 8
 THR_C2 = 0.01
@@ -623,7 +625,6 @@ def ternary_words(n: int) -> int:
 def bench_ternary(gcq, torch, np, si, steps: int):
     """The 2-bit step's workload with the codes packed five per byte:
     compress_ternary x 8 workers + decompress_ternary_sum W = 8."""
-    import oracle
     n, W = N_C2, W_C2
     r = bench_threshold_step(gcq, torch, si, steps, 3, "ternary", gcq.gc_compressed_ternary_words,
                              gcq.compress_ternary, gcq.decompress_ternary_sum)
@@ -633,14 +634,6 @@ def bench_ternary(gcq, torch, np, si, steps: int):
     deq_ms = sum(r["dequant_sum_ms"]) / len(r["dequant_sum_ms"])
     step_b = W * comp_b + deq_b
     comp_gbs = comp_b / (comp_ms / 1e3) / 1e9
-    # the oracle beside it: one worker's compress and the W-block sum
-    g = si.normal_f32(si.grad_seed(0, 0), n, SIGMA_C2)
-    c0 = time.perf_counter()
-    blk = oracle.quantize_ternary(g, np.zeros(n, np.float32), -THR_C2, THR_C2)
-    oracle_comp_ms = (time.perf_counter() - c0) * 1e3
-    c0 = time.perf_counter()
-    oracle.dequantize_ternary_sum([blk] * W, n)
-    oracle_deq_ms = (time.perf_counter() - c0) * 1e3
     return {"workload": "dense ternary packing (5 codes per byte): compress_ternary x 8 workers "
                         f"({n:,} fp32 each, thresholds +-{THR_C2}, residual carried) + "
                         "decompress_ternary_sum W=8",
@@ -657,8 +650,7 @@ def bench_ternary(gcq, torch, np, si, steps: int):
                          "traffic": traffic_from_profile("compress_ternary_vec_kernel")},
             "wire_bytes_per_worker": 4 * ternary_words(n),
             "wire_bytes_per_worker_2bit": 4 * (3 + (n + 15) // 16),
-            "oracle_ms": {"compress_one_worker": oracle_comp_ms, "dequant_sum_w8": oracle_deq_ms},
-            "oracle_cores": 1, "steps": steps}
+            "oracle_ms": None, "steps": steps}
 
 
 def multi_bytes(sizes) -> int:
@@ -668,7 +660,6 @@ def multi_bytes(sizes) -> int:
 def bench_multi(gcq, torch, np, si, steps: int):
     """Many-tensor 2-bit compress over the BERT-Base parameter list (198
     tensors, 109,482,240 values, thresholds +-0.005): one launch per step."""
-    import oracle
     sizes = si.bert_base_sizes()
     dev = "cuda"
     log(f"multi-tensor: generating {len(sizes)} tensors ({sum(sizes)} values)")
@@ -693,25 +684,19 @@ def bench_multi(gcq, torch, np, si, steps: int):
     torch.cuda.empty_cache()
     byts = multi_bytes(sizes)
     gbs = byts / (ms / 1e3) / 1e9
-    # the oracle beside it: one full pass over the same tensors
-    res_h = [np.zeros(n, np.float32) for n in sizes]
-    c0 = time.perf_counter()
-    for t in range(len(sizes)):
-        oracle.quantize_2bit(host[t], res_h[t], -0.005, 0.005)
-    oracle_ms = (time.perf_counter() - c0) * 1e3
+    del host
     return {"workload": "compress_2bit_multi over the BERT-Base parameter list: 198 tensors, "
                         f"{sum(sizes):,} fp32 values, thresholds +-0.005, one launch",
             "ms_per_call": ms, "algorithmic_bytes": byts, "gbs": gbs,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
-            "oracle_ms_per_call": oracle_ms, "oracle_cores": 1, "steps": steps}
+            "oracle_ms_per_call": None, "steps": steps}
 
 
 def bench_grandk(gcq, torch, np, si, steps: int):
     """GlobalRandK-MN at the ResNet-50 size: shared K = 10000 indices, gather
     for 8 workers, max-norm, quantize at s = 7, level sum and scatter into a
     dense fp32 buffer (the dense zero fill dominates the bytes)."""
-    import oracle
     n, K, W, s = N_C2, 10_000, W_C2, 7
     dev = "cuda"
     log("grandk: generating inputs")
@@ -794,13 +779,7 @@ def bench_grandk(gcq, torch, np, si, steps: int):
     tot = t0.elapsed_time(t1) / steps
     del graph, grads, dense, sws
     torch.cuda.empty_cache()
-    c0 = time.perf_counter()
-    idx_h = oracle.randk_indices(n, K, 0)
-    gk = [oracle.gather(h, idx_h) for h in host]
-    nrm = oracle.maxnorm(gk)
-    lv = [oracle.qsgd_quantize(gk[w], nrm, s, 0, w) for w in range(W)]
-    oracle.scatter_dense(oracle.qsgd_dequantize(oracle.level_sum(lv), nrm, s), idx_h, n)
-    oracle_ms = (time.perf_counter() - c0) * 1e3
+    del host
     dense_gbs = 4 * n / (fill / 1e3) / 1e9
     return {"workload": f"GRandK-MN: n={n:,}, K={K}, W={W}, s={s}: shared index draw, gather, "
                         "max-norm, quantize, level sum, scatter into a dense fp32 buffer",
@@ -817,18 +796,22 @@ def bench_grandk(gcq, torch, np, si, steps: int):
             "roofline": {"bound": "hbm", "kernel": "fill_zero + scatter (dense output)",
                          "achieved": round(dense_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(dense_gbs / HBM_PEAK_GBS, 4)},
-            "oracle_ms_per_step": oracle_ms, "oracle_cores": 1, "steps": steps}
+            "oracle_ms_per_step": None, "steps": steps}
 
 
-def cpu_baseline(np, si, budget_s: float):
+def cpu_baseline(np, si, budget_s: float, workloads=()):
     """The oracle, untouched, on the same 2-bit step (8 workers' compress +
-    the W = 8 dequantize-sum), repeated until the time budget is spent."""
+    the W = 8 dequantize-sum), repeated until the time budget is spent; then,
+    for each other workload the run measured (`workloads`), the oracle once
+    on that workload or a stated sample of it. Single-threaded, pinned to
+    one host core."""
     import oracle
     n, W = N_C2, W_C2
     log("cpu baseline: generating inputs")
     grads = [si.normal_f32(si.grad_seed(w, 0), n, SIGMA_C2) for w in range(W)]
     res = [np.zeros(n, np.float32) for _ in range(W)]
     oracle.lib()
+    per = {}
     # one core for the timed loop (the oracle is single-threaded); restored after
     saved = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
     pinned = None
@@ -846,6 +829,56 @@ def cpu_baseline(np, si, budget_s: float):
             log(f"cpu baseline: step {reps} done ({el:.1f} s)")
             if el >= budget_s:
                 break
+        del blocks, res
+        if "ternary" in workloads:
+            # one worker's compress and the W-block sum
+            c0 = time.perf_counter()
+            blk = oracle.quantize_ternary(grads[0], np.zeros(n, np.float32), -THR_C2, THR_C2)
+            comp_ms = (time.perf_counter() - c0) * 1e3
+            c0 = time.perf_counter()
+            oracle.dequantize_ternary_sum([blk] * W, n)
+            per["ternary"] = {"compress_one_worker": comp_ms,
+                              "dequant_sum_w8": (time.perf_counter() - c0) * 1e3}
+            log("cpu baseline: ternary done")
+        if "grandk" in workloads:
+            # the whole GRandK-MN step at K = 10000 on the same 8 gradients
+            K, s = 10_000, 7
+            c0 = time.perf_counter()
+            idx_h = oracle.randk_indices(n, K, 0)
+            gk = [oracle.gather(g, idx_h) for g in grads]
+            nrm = oracle.maxnorm(gk)
+            lv = [oracle.qsgd_quantize(gk[w], nrm, s, 0, w) for w in range(W)]
+            oracle.scatter_dense(oracle.qsgd_dequantize(oracle.level_sum(lv), nrm, s), idx_h, n)
+            per["grandk"] = (time.perf_counter() - c0) * 1e3
+            log("cpu baseline: grandk done")
+        del grads
+        if "multi" in workloads:
+            # one pass over the BERT-Base tensor list
+            sizes = si.bert_base_sizes()
+            host = [si.normal_f32(7919 * t, m, 0.005) for t, m in enumerate(sizes)]
+            res_h = [np.zeros(m, np.float32) for m in sizes]
+            c0 = time.perf_counter()
+            for t in range(len(sizes)):
+                oracle.quantize_2bit(host[t], res_h[t], -0.005, 0.005)
+            per["multi"] = (time.perf_counter() - c0) * 1e3
+            del host, res_h
+            log("cpu baseline: multi-tensor done")
+        if "qsgd" in workloads:
+            # the QSGD-MN step (max-norm, W quantizes, level sum, dequantize)
+            # on QSGD_ORACLE_SAMPLE values per worker, drawn by the same
+            # heavy-tailed generator: the full 8 x 138M step would take
+            # minutes on one core
+            m, Wq, sq = QSGD_ORACLE_SAMPLE, W_C3, S_C3
+            gq = [si.heavy_tailed_f32(si.grad_seed(w, 0), m, SIGMA_C3) for w in range(Wq)]
+            c0 = time.perf_counter()
+            nrm = oracle.maxnorm(gq)
+            lv = [oracle.qsgd_quantize(gq[w], nrm, sq, 0, w) for w in range(Wq)]
+            oracle.qsgd_dequantize(oracle.level_sum(lv), nrm, sq)
+            el_q = time.perf_counter() - c0
+            per["qsgd"] = {"sample": f"the step on {Wq} workers x {m:,} heavy-tailed values",
+                           "ms": el_q * 1e3,
+                           "values_per_s": Wq * m / el_q}
+            log("cpu baseline: qsgd sample done")
     finally:
         if saved:
             os.sched_setaffinity(0, saved)
@@ -856,7 +889,8 @@ def cpu_baseline(np, si, budget_s: float):
                       f"in {el:.1f} s, single-threaded C oracle pinned to host core {pinned} "
                       f"({cpu_model()}, {os.cpu_count()} visible)",
             "values_per_s": W * n / step_s,
-            "ms_per_step": step_s * 1e3}
+            "ms_per_step": step_s * 1e3,
+            "per_workload": per}
 
 
 def main() -> int:
@@ -953,7 +987,23 @@ def main() -> int:
         result["ternary"] = bench_ternary(gcq, torch, np, si, args.extra_steps)
 
     if not args.skip_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(np, si, args.cpu_seconds)
+        workloads = set()
+        if not args.skip_qsgd:
+            workloads.add("qsgd")
+        if not args.skip_extra:
+            workloads |= {"multi", "grandk", "ternary"}
+        cb = cpu_baseline(np, si, args.cpu_seconds, workloads)
+        result["cpu_baseline"] = cb
+        # each workload's object also carries the oracle's time beside its own
+        per = cb["per_workload"]
+        if "qsgd" in per:
+            result["qsgd_mn"]["oracle"] = dict(per["qsgd"], cores=1)
+        if "multi" in per:
+            result["multi_tensor"].update(oracle_ms_per_call=per["multi"], oracle_cores=1)
+        if "grandk" in per:
+            result["grandk_mn"].update(oracle_ms_per_step=per["grandk"], oracle_cores=1)
+        if "ternary" in per:
+            result["ternary"].update(oracle_ms=per["ternary"], oracle_cores=1)
     else:
         result["cpu_baseline"] = None
 
