@@ -622,6 +622,15 @@ GCQ_API int compress_2bit_multi(gc_plan* plan, float neg_threshold, float pos_th
         return rc;
     if (!aligned4(compr_base))
         return fail(GC_EINVAL, "compress_2bit_multi: compr_base must be 4-byte aligned");
+    // the descriptor table and the tensors it points to live on the plan's
+    // device: launching on another would read them from the wrong GPU
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess)
+        return fail(GC_EHIP, "compress_2bit_multi: hipGetDevice failed");
+    if (cur != plan->device)
+        return fail(GC_EINVAL, "compress_2bit_multi: the plan was created on device " +
+                                   std::to_string(plan->device) + ", the current device is " +
+                                   std::to_string(cur));
     const size_t blocks = std::min(plan->nchunks, max_grid_blocks());
     if (blocks < plan->nchunks)
         hipLaunchKernelGGL(compress_2bit_multi_kernel<true>, dim3(blocks), dim3(kThreads), 0,

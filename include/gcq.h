@@ -130,7 +130,9 @@ size_t gc_plan_compressed_words(const gc_plan* plan);
  * `offsets`. */
 int gc_plan_block_offsets(const gc_plan* plan, size_t* offsets);
 /* compress_2bit on every tensor of the plan with one pair of thresholds, in
- * one launch. Same arithmetic, validation and format as compress_2bit. */
+ * one launch. Same arithmetic, validation and format as compress_2bit. The
+ * device that was current at gc_plan_2bit_multi_create must be current
+ * here, else GC_EINVAL. */
 int compress_2bit_multi(gc_plan* plan, float neg_threshold,
                         float pos_threshold, uint32_t* compr_base,
                         hipStream_t stream);
