@@ -46,6 +46,32 @@ def heavy_tailed_f32(seed: int, n: int, sigma: float, frac: float = 1e-3,
     return x
 
 
+# IEEE values outside the Gaussian workloads: NaN, infinities, the largest
+# finite value, the smallest subnormal and normal magnitudes, signed zeros.
+IEEE_SPECIALS = np.array([np.nan, np.inf, -np.inf, np.finfo(np.float32).max,
+                          -np.finfo(np.float32).max, np.float32(2.0 ** -149),
+                          -np.float32(2.0 ** -149), np.finfo(np.float32).tiny,
+                          -np.finfo(np.float32).tiny, 0.0, -0.0], dtype=np.float32)
+
+
+def with_ieee_specials(seed: int, n: int, sigma: float, stride: int = 7) -> np.ndarray:
+    """normal_f32(seed, n, sigma) with every `stride`-th entry replaced by the
+    next value of IEEE_SPECIALS, in turn."""
+    x = normal_f32(seed, n, sigma)
+    at = np.arange(0, n, stride)
+    x[at] = IEEE_SPECIALS[np.arange(at.size) % IEEE_SPECIALS.size]
+    return x
+
+
+def subnormal_units(seed: int, n: int, span: int) -> np.ndarray:
+    """n float32 values m * 2^-149 (subnormal or zero) with m drawn uniformly
+    from the integers -span .. span (span < 2^23)."""
+    rng = np.random.default_rng(seed)
+    m = rng.integers(-span, span + 1, n, dtype=np.int64)
+    bits = np.where(m >= 0, m, 0x80000000 | -m).astype(np.uint32)
+    return bits.view(np.float32)
+
+
 def uniform_f32_device(seed: int, n: int, device: str = "cuda:0"):
     """n values uniform in [-1, 1), float32, drawn on the device by torch's
     seeded generator: for inputs too large to draw on the host (tens of GB).

@@ -115,6 +115,44 @@ def test_threshold_edges(gcq, thr):
     np.testing.assert_array_equal(r_gpu.view(np.uint32), r_or.view(np.uint32))
 
 
+def ieee_case(kind: str, n: int):
+    """Gradient, starting residual and thresholds of an IEEE edge case:
+    'specials' puts NaN, infinities, FLT_MAX, subnormals and signed zeros
+    among N(0, 0.01^2) values (thresholds +-0.01); 'subnormal' uses values,
+    residuals and thresholds that are all multiples of 2^-149."""
+    if kind == "specials":
+        return (si.with_ieee_specials(21, n, 0.01), si.normal_f32(22, n, 0.005),
+                np.float32(0.01))
+    return si.subnormal_units(23, n, 9), si.subnormal_units(24, n, 4), np.float32(2.0 ** -147)
+
+
+def assert_residuals_match(r_gpu, r_or):
+    """Bit for bit, except that NaN must meet NaN (payloads are not compared)."""
+    nan = np.isnan(r_or)
+    np.testing.assert_array_equal(np.isnan(r_gpu), nan)
+    np.testing.assert_array_equal(r_gpu[~nan].view(np.uint32), r_or[~nan].view(np.uint32))
+
+
+@pytest.mark.parametrize("misalign", [False, True])
+@pytest.mark.parametrize("kind", ["specials", "subnormal"])
+def test_ieee_specials_and_subnormals(gcq, kind, misalign):
+    n = 4099
+    announce(f"2-bit IEEE edge case {kind} misalign={misalign}")
+    g, r0, t = ieee_case(kind, n)
+    compr, r_gpu = gpu_compress(gcq, g, r0, -t, t, misalign)
+    r_or = r0.copy()
+    c_or = oracle.quantize_2bit(g, r_or, -t, t)
+    np.testing.assert_array_equal(compr, c_or)
+    assert_residuals_match(r_gpu, r_or)
+    # the blocks decode and sum like the oracle's (subnormal thresholds included)
+    blocks = [c_or, oracle.quantize_2bit(g, r_or.copy(), -t, t), c_or]
+    out = gu.empty(n, torch.float32, misalign=misalign, fill=float("nan"))
+    gcq.decompress_2bit_sum([gu.dev(c) for c in blocks], n, out)
+    gu.sync()
+    np.testing.assert_array_equal(gu.host(out).view(np.uint32),
+                                  oracle.dequantize_2bit_sum(blocks, n).view(np.uint32))
+
+
 @pytest.mark.parametrize("W", [1, 2, 3, 8, 64])
 @pytest.mark.parametrize("n", [1, 17, 1000, 4097, 100_003])
 def test_dequantize_sum(gcq, W, n):

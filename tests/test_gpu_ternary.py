@@ -85,6 +85,31 @@ def test_small_error_feedback_10_iterations(gcq):
         np.testing.assert_array_equal(gu.host(r_dev).view(np.uint32), r_or.view(np.uint32))
 
 
+@pytest.mark.parametrize("misalign", [False, True])
+@pytest.mark.parametrize("kind", ["specials", "subnormal"])
+def test_ieee_specials_and_subnormals(gcq, kind, misalign):
+    """NaN, infinities, FLT_MAX, subnormals and signed zeros among the values,
+    or values and thresholds that are all multiples of 2^-149."""
+    n = 5141
+    announce(f"ternary IEEE edge case {kind} misalign={misalign}")
+    if kind == "specials":
+        g, r0, t = si.with_ieee_specials(31, n, 0.01), si.normal_f32(32, n, 0.005), np.float32(0.01)
+    else:
+        g, r0, t = si.subnormal_units(33, n, 9), si.subnormal_units(34, n, 4), np.float32(2.0 ** -147)
+    compr, r_gpu = gpu_compress(gcq, g, r0, -t, t, misalign)
+    r_or = r0.copy()
+    c_or = oracle.quantize_ternary(g, r_or, -t, t)
+    np.testing.assert_array_equal(compr, c_or)
+    nan = np.isnan(r_or)
+    np.testing.assert_array_equal(np.isnan(r_gpu), nan)
+    np.testing.assert_array_equal(r_gpu[~nan].view(np.uint32), r_or[~nan].view(np.uint32))
+    out = gu.empty(n, torch.float32, misalign=misalign, fill=float("nan"))
+    gcq.decompress_ternary_sum([gu.dev(c_or)] * 3, n, out)
+    gu.sync()
+    np.testing.assert_array_equal(gu.host(out).view(np.uint32),
+                                  oracle.dequantize_ternary_sum([c_or] * 3, n).view(np.uint32))
+
+
 @pytest.mark.parametrize("thr", [0.5, 0.01, 2.0, 1e-30])
 def test_threshold_edges(gcq, thr):
     announce(f"ternary threshold edges thr={thr}")

@@ -129,6 +129,54 @@ def test_threshold_edges_inclusive(thr):
     np.testing.assert_array_equal(deq, np.array([pos, pos, 0, neg, neg, 0, 0, 0], np.float32))
 
 
+def test_ieee_special_values():
+    """NaN, infinities, FLT_MAX, subnormals and signed zeros go through the
+    inclusive comparisons of [MX] "Two bit quantization" as IEEE fixes them:
+    a NaN compares false both ways (code 00, residual NaN); an infinity is
+    beyond either threshold and stays infinite; FLT_MAX - 0.5 rounds back to
+    FLT_MAX; subnormals are kept (no flush to zero); -0 + 0 is +0."""
+    tiny = bits_f32(1)  # 2^-149
+    fmax = np.finfo(np.float32).max
+    g = np.array([np.nan, np.inf, -np.inf, fmax, -fmax, tiny, -tiny, 0.0, -0.0, 0.5, -0.5],
+                 np.float32)
+    r = np.zeros_like(g)
+    compr = oracle.quantize_2bit(g, r, -0.5, 0.5)
+    np.testing.assert_array_equal(
+        oracle.dequantize_2bit(compr, g.size),
+        np.array([0, 0.5, -0.5, 0.5, -0.5, 0, 0, 0, 0, 0.5, -0.5], np.float32))
+    assert np.isnan(r[0])
+    np.testing.assert_array_equal(
+        r[1:].view(np.uint32),
+        np.array([0x7F800000, 0xFF800000, 0x7F7FFFFF, 0xFF7FFFFF, 0x00000001, 0x80000001,
+                  0, 0, 0, 0], np.uint32))
+
+
+def test_subnormal_thresholds():
+    """Thresholds of 3 * 2^-149 and values k * 2^-149: every operation is exact
+    on subnormals, so the codes and residuals are those of integer
+    arithmetic on k (in units of 2^-149)."""
+    unit = lambda m: (m if m >= 0 else 0x80000000 | -m) if m != 0 else 0  # noqa: E731
+    ks = list(range(-5, 6))
+    g = np.array([bits_f32(unit(k)) for k in ks], np.float32)
+    t = np.float32(bits_f32(3))
+    r = np.zeros_like(g)
+    compr = oracle.quantize_2bit(g, r, -t, t)
+    deq = oracle.dequantize_2bit(compr, g.size)
+    code = [1 if k >= 3 else 2 if k <= -3 else 0 for k in ks]
+    np.testing.assert_array_equal(deq.view(np.uint32),
+                                  np.array([unit({0: 0, 1: 3, 2: -3}[c]) for c in code],
+                                           np.uint32))
+    np.testing.assert_array_equal(
+        r.view(np.uint32),
+        np.array([unit(k - {0: 0, 1: 3, 2: -3}[c]) for k, c in zip(ks, code)], np.uint32))
+    # the residual carries: 2 + 1 units reach the threshold exactly
+    g2 = np.array([bits_f32(2)] * 3, np.float32)
+    r2 = np.array([bits_f32(1), 0.0, bits_f32(0x80000001)], np.float32)
+    deq2 = oracle.dequantize_2bit(oracle.quantize_2bit(g2, r2, -t, t), 3)
+    np.testing.assert_array_equal(deq2.view(np.uint32), np.array([3, 0, 0], np.uint32))
+    np.testing.assert_array_equal(r2.view(np.uint32), np.array([0, 2, 1], np.uint32))
+
+
 def test_unused_code_11_dequantizes_to_zero():
     compr = np.array([f32_bits(-1.0), f32_bits(1.0), f32_bits(16.0), 0xFFFFFFFF], np.uint32)
     np.testing.assert_array_equal(oracle.dequantize_2bit(compr, 16), np.zeros(16, np.float32))
