@@ -195,3 +195,47 @@ def test_plan_rejects_bad_arguments(lib):
     assert lib.gc_plan_2bit_multi_create(ptrs, ptrs, ns, 1, ctypes.byref(handle)) == gcq.GC_EINVAL
     assert lib.gc_plan_2bit_multi_create(ptrs, ptrs, ns, 0, ctypes.byref(handle)) == gcq.GC_EINVAL
     assert handle.value is None
+
+
+def test_error_message_is_per_thread(lib):
+    """gc_last_error() reports the calling thread's own last failure: two
+    threads fail different calls in lockstep and each reads its own message
+    (ctypes drops the GIL inside the calls, so they run concurrently)."""
+    import threading
+
+    rounds = 2000
+    barrier = threading.Barrier(2, timeout=30)
+    errors = []
+    arr = (ctypes.c_void_p * 64)(*([FAKE] * 64))
+
+    def run(name, call, code, text):
+        try:
+            for _ in range(rounds):
+                barrier.wait()
+                if call() != code:
+                    errors.append(f"{name}: wrong return code")
+                barrier.wait()
+                if text not in lib.gc_last_error():
+                    errors.append(f"{name}: message of another thread")
+        except Exception as e:  # a failing thread must not leave the other waiting
+            errors.append(f"{name}: {e!r}")
+            barrier.abort()
+
+    threads = [
+        threading.Thread(target=run, args=(
+            "compress", lambda: _rc_compress(lib, FAKE, FAKE, 16, 1.0, -1.0, FAKE),
+            gcq.GC_EINVAL, b"threshold")),
+        threading.Thread(target=run, args=(
+            "sum", lambda: lib.decompress_2bit_sum(arr, 0, 16, FAKE, None),
+            gcq.GC_EINVAL, b"W must be")),
+    ]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads), "a thread did not finish"
+    assert not errors, errors[:3]
+    # a successful call clears the calling thread's message
+    size = ctypes.c_size_t(0)
+    assert lib.grandk_indices(100, 10, 0, NULL, NULL, ctypes.byref(size), None) == gcq.GC_OK
+    assert lib.gc_last_error() == b""

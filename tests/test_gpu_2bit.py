@@ -153,6 +153,38 @@ def test_ieee_specials_and_subnormals(gcq, kind, misalign):
                                   oracle.dequantize_2bit_sum(blocks, n).view(np.uint32))
 
 
+def test_workers_on_concurrent_streams(gcq):
+    """The workers' compresses run on two streams at once and the sum on a
+    third that waits for both; two error-feedback iterations, the second
+    ordered after the first sum. The calls share no state, so the results
+    are the oracle's."""
+    n, W, thr = 1_000_003, 6, 0.05
+    announce(f"2-bit EF on concurrent streams W={W} n={n}")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    sum_stream = torch.cuda.Stream()
+    grads = [si.normal_f32(si.grad_seed(w, 70), n, 0.05) for w in range(W)]
+    g_dev = [gu.dev(g) for g in grads]
+    r_dev = [torch.zeros(n, dtype=torch.float32, device=gu.DEV) for _ in range(W)]
+    c_dev = [gu.empty(gcq.gc_compressed_2bit_words(n), torch.int32, fill=-1) for _ in range(W)]
+    out = gu.empty(n, torch.float32, fill=float("nan"))
+    r_or = [np.zeros(n, np.float32) for _ in range(W)]
+    gu.sync()
+    for it in range(2):
+        for w in range(W):
+            gcq.compress_2bit(g_dev[w], r_dev[w], -thr, thr, c_dev[w], stream=streams[w % 2])
+        for st in streams:
+            sum_stream.wait_stream(st)
+        gcq.decompress_2bit_sum(c_dev, n, out, stream=sum_stream)
+        for st in streams:  # the next compresses overwrite what the sum reads
+            st.wait_stream(sum_stream)
+        c_or = [oracle.quantize_2bit(grads[w], r_or[w], -thr, thr) for w in range(W)]
+    gu.sync()
+    for w in range(W):
+        np.testing.assert_array_equal(gu.host(c_dev[w], np.uint32), c_or[w])
+        np.testing.assert_array_equal(gu.host(r_dev[w]).view(np.uint32), r_or[w].view(np.uint32))
+    np.testing.assert_array_equal(gu.host(out), oracle.dequantize_2bit_sum(c_or, n))
+
+
 @pytest.mark.parametrize("W", [1, 2, 3, 8, 64])
 @pytest.mark.parametrize("n", [1, 17, 1000, 4097, 100_003])
 def test_dequantize_sum(gcq, W, n):
