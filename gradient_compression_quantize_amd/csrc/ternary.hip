@@ -48,16 +48,6 @@ __host__ __device__ inline size_t payload_words(size_t n)
     return n / kWordValues + (n % kWordValues != 0 ? 1 : 0);
 }
 
-// Orders this wave's LDS accesses across its lanes: LDS operations of one
-// wave complete in issue order, so it suffices that the compiler moves no
-// LDS access across this point.
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Code of one value (0 zero, 1 pos, 2 neg) and its new residual.
 __device__ __forceinline__ uint32_t code_and_residual(float v, float neg, float pos, float& rn)
 {

@@ -58,29 +58,82 @@ __device__ __forceinline__ void classify4(f32x4 g, f32x4 r, float neg, float pos
     }
 }
 
-// One word of codes (16 values) by one thread, scalar accesses.
-__device__ __forceinline__ uint32_t compress_word_scalar(const float* __restrict__ grad,
-                                                         float* __restrict__ residual, size_t n,
-                                                         float neg, float pos, size_t j)
+// OR over the 16 lanes of each DPP row; every lane of the row gets the
+// result. A quad OR, then rotations by 4 and 8 lanes within the row
+// (row_ror:4 = 0x124, row_ror:8 = 0x128).
+__device__ __forceinline__ uint32_t row_or(uint32_t x)
 {
-    uint32_t word = 0;
-    // kept rolled: this path serves only buffers without 16-byte alignment,
-    // and unrolling it would raise the register count of the many-tensor
-    // kernel that inlines it
-#pragma unroll 1
-    for (int k = 0; k < 16; ++k) {
-        const size_t i = j * 16 + k;
-        if (i >= n)
-            break;
-        const float v = grad[i] + residual[i];
+    x = quad_or(x);
+    x |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(x), 0x124, 0xF, 0xF, true));
+    x |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(x), 0x128, 0xF, 0xF, true));
+    return x;
+}
+
+// One wave tile of kTileElems values starting at element e0 (a multiple of
+// 16), for grad and residual of any 4-byte alignment: lane-contiguous 4-byte
+// accesses, one value per lane in each of 16 steps (each load and store
+// instruction moves 256 contiguous bytes). In step j, row r of the wave
+// holds values e0 + 64 j + 16 r .. + 15, i.e. word 4 j + r of the tile; a
+// row OR forms it and lane 4 j + r keeps it, so the tile's 64 words still
+// leave in one coalesced store. kFull: the whole tile is below n; otherwise
+// values at or past n are neither read nor written (code 00) and only words
+// below ceil(n / 16) are stored.
+template <bool kFull>
+__device__ __forceinline__ void compress_dword_tile(const float* __restrict__ grad,
+                                                    float* __restrict__ residual, size_t n,
+                                                    float neg, float pos,
+                                                    uint32_t* __restrict__ payload, size_t e0,
+                                                    int lane)
+{
+    constexpr int kSteps = int(kTileElems) / kWave;
+    float g[kSteps], r[kSteps];
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+        const size_t e = e0 + size_t(j) * kWave + lane;
+        g[j] = 0.0f;
+        r[j] = 0.0f;
+        if (kFull || e < n) {
+            g[j] = __builtin_nontemporal_load(grad + e);
+            r[j] = __builtin_nontemporal_load(residual + e);
+        }
+    }
+    const uint32_t shift = 30u - 2u * uint32_t(lane & 15);
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+        const size_t e = e0 + size_t(j) * kWave + lane;
+        const float v = g[j] + r[j];
         const bool up = v >= pos;
         const bool dn = v <= neg;
         const float d = up ? pos : (dn ? neg : 0.0f);
-        residual[i] = v - d;
+        if (kFull || e < n)
+            __builtin_nontemporal_store(v - d, residual + e);
         const uint32_t c = up ? 1u : (dn ? 2u : 0u);
-        word |= c << (30 - 2 * k);
+        const uint32_t word = row_or(c << shift);
+        // lane 4 j + r takes row r's word (row r starts at lane 16 r)
+        const uint32_t w = static_cast<uint32_t>(
+            __builtin_amdgcn_ds_bpermute(64 * (lane & 3), static_cast<int>(word)));
+        if ((lane >> 2) == j)
+            mine = w;
     }
-    return word;
+    const size_t jw = (e0 >> 4) + lane;
+    if (kFull || jw < ((n + 15) >> 4))
+        __builtin_nontemporal_store(mine, payload + jw);
+}
+
+// Tile e0 for grad or residual without 16-byte alignment.
+__device__ __forceinline__ void compress_dword_tile_any(const float* __restrict__ grad,
+                                                        float* __restrict__ residual, size_t n,
+                                                        float neg, float pos,
+                                                        uint32_t* __restrict__ payload,
+                                                        size_t e0, int lane)
+{
+    if (e0 + kTileElems <= n)
+        compress_dword_tile<true>(grad, residual, n, neg, pos, payload, e0, lane);
+    else
+        compress_dword_tile<false>(grad, residual, n, neg, pos, payload, e0, lane);
 }
 
 // One full wave tile: float4 slots q0 .. q0 + kTileF4 - 1, all below n / 4.
@@ -208,17 +261,23 @@ __global__ __launch_bounds__(kThreads) void compress_2bit_vec_kernel(
     }
 }
 
-// Any 4-byte alignment: one thread per word.
-__global__ __launch_bounds__(kThreads) void compress_2bit_scalar_kernel(
+// Any 4-byte alignment of grad and residual: the same wave tiles through
+// lane-contiguous 4-byte accesses (compress_dword_tile).
+template <bool kLoop>
+__global__ __launch_bounds__(kThreads) void compress_2bit_dword_kernel(
     const float* __restrict__ grad, float* __restrict__ residual, size_t n, float neg,
-    float pos, float n_f, uint32_t* __restrict__ compr)
+    float pos, float n_f, uint32_t* __restrict__ compr, size_t ntiles)
 {
     if (blockIdx.x == 0 && threadIdx.x == 0)
         write_header(compr, neg, pos, n_f);
-    const size_t nwords = (n + 15) >> 4;
-    const size_t stride = size_t(gridDim.x) * blockDim.x;
-    for (size_t j = size_t(blockIdx.x) * blockDim.x + threadIdx.x; j < nwords; j += stride)
-        compr[3 + j] = compress_word_scalar(grad, residual, n, neg, pos, j);
+    const int lane = threadIdx.x & (kWave - 1);
+    const size_t stride = size_t(gridDim.x) * kWavesPerBlock;
+    for (size_t t = size_t(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave; t < ntiles;
+         t += stride) {
+        compress_dword_tile_any(grad, residual, n, neg, pos, compr + 3, t * kTileElems, lane);
+        if (!kLoop)
+            break;
+    }
 }
 
 // One wave tile of the W-block dequantize-and-sum (see compress_wave_tile).
@@ -228,11 +287,13 @@ __global__ __launch_bounds__(kThreads) void compress_2bit_scalar_kernel(
 // is fetched from memory twice. Decoding goes through the LDS nibble table.
 // WC > 0: W == WC is known at compile time, so every worker's word is loaded
 // before any is decoded; WC == 0: W read at run time, in groups of four.
-template <int WC, bool kAcc>
+// kDword: out without 16-byte alignment. The tile's float4 slots go to the
+// wave's LDS stage and leave as lane-contiguous 4-byte stores.
+template <int WC, bool kAcc, bool kDword>
 __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& tab, int W_rt,
                                                      const float2* lut,
                                                      float* __restrict__ out, size_t q0,
-                                                     int lane)
+                                                     int lane, f32x4* stage)
 {
     const int W = WC > 0 ? WC : W_rt;
     const size_t jmine = (q0 >> 2) + lane;  // the word this lane fetches
@@ -266,6 +327,24 @@ __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& t
                 acc[u] = (w == 0) ? d : acc[u] + d;
             }
         }
+    }
+    if (kDword) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            stage[u * kWave + lane] = acc[u];
+        wave_lds_sync();
+        const float* sf = reinterpret_cast<const float*>(stage);
+        float* o = out + q0 * 4;
+#pragma unroll
+        for (int j = 0; j < int(kTileElems) / kWave; ++j) {
+            const int e = j * kWave + lane;
+            float v = sf[e];
+            if (kAcc)
+                v = o[e] + v;
+            __builtin_nontemporal_store(v, o + e);
+        }
+        wave_lds_sync();  // these reads precede the next tile's writes
+        return;
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -306,13 +385,14 @@ __device__ __forceinline__ void decompress_tail_tile(const PtrTable<uint32_t>& t
     }
 }
 
-// Dequantize-and-sum of W blocks into a 16-byte-aligned out (kAcc: added to
-// what out holds).
-template <int WC, bool kAcc, bool kLoop>
+// Dequantize-and-sum of W blocks into out (kAcc: added to what out holds);
+// kDword: out is 4- but not 16-byte aligned.
+template <int WC, bool kAcc, bool kLoop, bool kDword>
 __global__ __launch_bounds__(kThreads) void decompress_2bit_vec_kernel(
     PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, size_t ntiles)
 {
     __shared__ float2 lut[16 * GC_MAX_WORKERS];
+    __shared__ f32x4 stage[kDword ? kWavesPerBlock : 1][kDword ? kTileF4 : 1];
     build_nibble_table(lut, tab, WC > 0 ? WC : W);
     const int lane = threadIdx.x & (kWave - 1);
     const size_t stride = size_t(gridDim.x) * kWavesPerBlock;
@@ -326,28 +406,12 @@ __global__ __launch_bounds__(kThreads) void decompress_2bit_vec_kernel(
     for (size_t t = blk * kWavesPerBlock + threadIdx.x / kWave; t < ntiles; t += stride) {
         const size_t q0 = (ntiles - 1 - t) * kTileF4;
         if (q0 + kTileF4 <= (n >> 2))
-            decompress_full_tile<WC, kAcc>(tab, W, lut, out, q0, lane);
+            decompress_full_tile<WC, kAcc, kDword>(tab, W, lut, out, q0, lane,
+                                                   stage[kDword ? threadIdx.x / kWave : 0]);
         else
             decompress_tail_tile(tab, WC > 0 ? WC : W, lut, n, out, kAcc ? 1 : 0, q0, lane);
         if (!kLoop)
             break;
-    }
-}
-
-// Any 4-byte-aligned out: one thread per value.
-__global__ __launch_bounds__(kThreads) void decompress_2bit_scalar_kernel(
-    PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, int accumulate)
-{
-    const size_t stride = size_t(gridDim.x) * blockDim.x;
-    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const uint32_t sh = 30u - 2u * uint32_t(i & 15);
-        float acc = 0.0f;
-        for (int w = 0; w < W; ++w) {
-            const uint32_t* b = tab.p[w];
-            const float d = code_value((b[3 + (i >> 4)] >> sh) & 3u, u2f(b[0]), u2f(b[1]));
-            acc = (w == 0) ? d : acc + d;
-        }
-        out[i] = accumulate ? out[i] + acc : acc;
     }
 }
 
@@ -384,16 +448,16 @@ __global__ __launch_bounds__(kThreads) void compress_2bit_multi_kernel(
                               size_t(threadIdx.x / kWave) * kTileF4;
             compress_tile(cd.grad, cd.residual, cd.n, neg, pos, blk + 3, q0, lane);
         } else {
-            const size_t j = size_t(cd.chunk) * (kBlockElems / 16) + threadIdx.x;
-            if (j < ((cd.n + 15) >> 4))
-                blk[3 + j] = compress_word_scalar(cd.grad, cd.residual, cd.n, neg, pos, j);
+            const size_t e0 = size_t(cd.chunk) * kBlockElems +
+                              size_t(threadIdx.x / kWave) * kTileElems;
+            if (e0 < cd.n)
+                compress_dword_tile_any(cd.grad, cd.residual, cd.n, neg, pos, blk + 3, e0, lane);
         }
         if (!kLoop)
             break;
     }
 }
 
-static_assert(kBlockElems / 16 == kThreads, "scalar multi path: one word per thread");
 
 size_t grid_for_tiles(size_t ntiles)
 {
@@ -445,29 +509,34 @@ GCQ_API int compress_2bit(const float* grad, float* residual, size_t n, float ne
             hipLaunchKernelGGL(compress_2bit_vec_kernel<false>, grid, block, 0, stream, grad,
                                residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles);
     } else {
-        const size_t blocks = std::min(ceil_div(ceil_div(n, 16), kThreads), max_grid_blocks());
-        hipLaunchKernelGGL(compress_2bit_scalar_kernel, dim3(blocks), dim3(kThreads), 0,
-                           stream, grad, residual, n, neg_threshold, pos_threshold, n_f, compr);
+        const size_t ntiles = ceil_div(n, kTileElems);
+        const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
+        if (tiles_need_loop(ntiles))
+            hipLaunchKernelGGL(compress_2bit_dword_kernel<true>, grid, block, 0, stream, grad,
+                               residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles);
+        else
+            hipLaunchKernelGGL(compress_2bit_dword_kernel<false>, grid, block, 0, stream, grad,
+                               residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles);
     }
     return check_launch("compress_2bit");
 }
 
-template <bool kLoop>
+template <bool kLoop, bool kDword>
 static void launch_decompress_vec(const PtrTable<uint32_t>& tab, int W, size_t n, float* out,
                                   int accumulate, size_t ntiles, dim3 grid, dim3 block,
                                   hipStream_t stream)
 {
     if (accumulate) {
         // only decompress_2bit accumulates (W == 1)
-        hipLaunchKernelGGL((decompress_2bit_vec_kernel<1, true, kLoop>), grid, block, 0, stream,
-                           tab, W, n, out, ntiles);
+        hipLaunchKernelGGL((decompress_2bit_vec_kernel<1, true, kLoop, kDword>), grid, block, 0,
+                           stream, tab, W, n, out, ntiles);
         return;
     }
     switch (W) {
 #define GCQ_DEC_CASE(k)                                                                    \
     case k:                                                                                \
-        hipLaunchKernelGGL((decompress_2bit_vec_kernel<k, false, kLoop>), grid, block, 0,  \
-                           stream, tab, W, n, out, ntiles);                                \
+        hipLaunchKernelGGL((decompress_2bit_vec_kernel<k, false, kLoop, kDword>), grid,    \
+                           block, 0, stream, tab, W, n, out, ntiles);                      \
         break;
         GCQ_DEC_CASE(1)
         GCQ_DEC_CASE(2)
@@ -479,8 +548,8 @@ static void launch_decompress_vec(const PtrTable<uint32_t>& tab, int W, size_t n
         GCQ_DEC_CASE(8)
 #undef GCQ_DEC_CASE
     default:
-        hipLaunchKernelGGL((decompress_2bit_vec_kernel<0, false, kLoop>), grid, block, 0, stream,
-                           tab, W, n, out, ntiles);
+        hipLaunchKernelGGL((decompress_2bit_vec_kernel<0, false, kLoop, kDword>), grid, block, 0,
+                           stream, tab, W, n, out, ntiles);
     }
 }
 
@@ -489,17 +558,19 @@ static int launch_decompress(const PtrTable<uint32_t>& tab, int W, size_t n, flo
 {
     if (n == 0)
         return GC_OK;
+    const size_t ntiles = ceil_div(n, kTileElems);
+    const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
+    const bool loop = tiles_need_loop(ntiles);
     if (aligned16(out)) {
-        const size_t ntiles = ceil_div(n, kTileElems);
-        const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
-        if (tiles_need_loop(ntiles))
-            launch_decompress_vec<true>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
+        if (loop)
+            launch_decompress_vec<true, false>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
         else
-            launch_decompress_vec<false>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
+            launch_decompress_vec<false, false>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
     } else {
-        const size_t blocks = std::min(ceil_div(n, kThreads), max_grid_blocks());
-        hipLaunchKernelGGL(decompress_2bit_scalar_kernel, dim3(blocks), dim3(kThreads), 0,
-                           stream, tab, W, n, out, accumulate);
+        if (loop)
+            launch_decompress_vec<true, true>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
+        else
+            launch_decompress_vec<false, true>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
     }
     return check_launch(what);
 }

@@ -29,14 +29,16 @@ def check(cond, what):
 def main():
     assert os.environ.get("GCQ_MAX_GRID_BLOCKS"), "run with GCQ_MAX_GRID_BLOCKS set"
     gcq.load()
-    # 2-bit: vector path over many more tiles than waves, ragged tail
-    for n in (40_000 + 5, 123_457):
-        print(f"[case] capped compress/decompress n={n}", flush=True)
+    # 2-bit: vector path over many more tiles than waves, ragged tail; and
+    # the same with buffers 4 bytes off 16-byte alignment (lane-contiguous
+    # 4-byte accesses)
+    for n, mis in ((40_000 + 5, False), (123_457, False), (40_000 + 5, True), (123_457, True)):
+        print(f"[case] capped compress/decompress n={n} misaligned={mis}", flush=True)
         g = si.normal_f32(n, n, 0.5)
         r0 = si.normal_f32(n + 1, n, 0.2)
-        r_dev = gu.dev(r0)
+        r_dev = gu.dev(r0, mis)
         compr = gu.empty(gcq.gc_compressed_2bit_words(n), torch.int32, fill=-1)
-        gcq.compress_2bit(gu.dev(g), r_dev, -0.5, 0.5, compr)
+        gcq.compress_2bit(gu.dev(g, mis), r_dev, -0.5, 0.5, compr)
         r_or = r0.copy()
         c_or = oracle.quantize_2bit(g, r_or, -0.5, 0.5)
         gu.sync()
@@ -44,7 +46,7 @@ def main():
         check(np.array_equal(gu.host(r_dev).view(np.uint32), r_or.view(np.uint32)),
               f"compress residual n={n}")
         base = si.normal_f32(n + 2, n, 1.0)
-        out = gu.dev(base)
+        out = gu.dev(base, mis)
         gcq.decompress_2bit(gu.dev(c_or), n, out, accumulate=True)
         gu.sync()
         check(np.array_equal(gu.host(out), (base + oracle.dequantize_2bit(c_or, n)).astype(np.float32)),
@@ -52,7 +54,7 @@ def main():
         for W in (8, 9):
             comprs = [oracle.quantize_2bit(si.normal_f32(7 * w + n, n, 0.5), np.zeros(n, np.float32),
                                            -0.3 - 0.01 * w, 0.3 + 0.01 * w) for w in range(W)]
-            out = gu.empty(n, torch.float32, fill=float("nan"))
+            out = gu.empty(n, torch.float32, misalign=mis, fill=float("nan"))
             gcq.decompress_2bit_sum([gu.dev(c) for c in comprs], n, out)
             gu.sync()
             check(np.array_equal(gu.host(out), oracle.dequantize_2bit_sum(comprs, n)),

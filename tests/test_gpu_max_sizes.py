@@ -88,6 +88,40 @@ def test_2bit_and_ternary_beyond_2e32_values(gcq):
     release()
 
 
+def test_2bit_misaligned_beyond_2e32_values(gcq):
+    """The lane-contiguous 4-byte paths (gradient, residual and output 4 bytes
+    off 16-byte alignment) past the 32-bit index boundaries."""
+    n = (1 << 32) + 1029
+    need(3 * (n + 1) * 4 + 2 * GiB)
+    announce(f"max size: 2-bit, buffers 4 bytes off alignment, n={n}")
+    g_buf = si.uniform_f32_device(43, n + 1)
+    g_buf.mul_(0.5)
+    r_buf = si.uniform_f32_device(44, n + 1)
+    r_buf.mul_(0.25)
+    g, r = g_buf[1:], r_buf[1:]
+    assert g.data_ptr() % 16 != 0 and r.data_ptr() % 16 != 0
+    c2 = gu.empty(gcq.gc_compressed_2bit_words(n), torch.int32, fill=-1)
+    wins = [(0, 8000), ((1 << 31) - 4000, (1 << 31) + 4000), ((1 << 32) - 4000, n)]
+    r_before = [r[lo:hi].cpu().numpy() for lo, hi in wins]
+    g_win = [g[lo:hi].cpu().numpy() for lo, hi in wins]
+    gcq.compress_2bit(g, r, -0.3, 0.3, c2)
+    del g_buf, g
+    out_buf = gu.empty(n + 1, torch.float32, fill=float("nan"))
+    out = out_buf[1:]
+    gcq.decompress_2bit(c2, n, out)
+    gu.sync()
+    for (lo, hi), gw, rw in zip(wins, g_win, r_before):
+        announce(f"max size misaligned: window [{lo}, {hi})")
+        r_or = rw.copy()
+        w2 = oracle.quantize_2bit(gw, r_or, -0.3, 0.3)[3:]
+        np.testing.assert_array_equal(c2[3 + lo // 16:3 + lo // 16 + w2.size].cpu().numpy().view(np.uint32), w2)
+        np.testing.assert_array_equal(r[lo:hi].cpu().numpy().view(np.uint32), r_or.view(np.uint32))
+        np.testing.assert_array_equal(out[lo:hi].cpu().numpy(),
+                                      oracle.dequantize_2bit(oracle.quantize_2bit(gw, rw.copy(), -0.3, 0.3), hi - lo))
+    del r_buf, r, c2, out_buf, out
+    release()
+
+
 def test_qsgd_beyond_2e32_slots(gcq):
     n = (1 << 34) + 4109
     need(n * 4 + n + 2 * GiB)
