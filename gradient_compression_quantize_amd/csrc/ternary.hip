@@ -153,13 +153,58 @@ __device__ __forceinline__ void compress_full_tile(const float* __restrict__ gra
     __builtin_nontemporal_store(fold_base3(c), payload + q0 / kSlots + lane);
 }
 
+// The same full tile for grad and residual of any 4-byte alignment:
+// lane-contiguous 4-byte accesses, one value per lane in each of 20 steps
+// (256 bytes per load and store instruction). A quad OR gathers the codes
+// of 4 consecutive values into the dword the vector path writes for their
+// float4 slot; the fold and the store are the vector path's.
+__device__ __forceinline__ void compress_dword_full_tile(const float* __restrict__ grad,
+                                                         float* __restrict__ residual, float neg,
+                                                         float pos,
+                                                         uint32_t* __restrict__ payload,
+                                                         size_t q0, int lane, uint32_t* codes)
+{
+    constexpr int kSteps = int(kTileF4) * 4 / kWave;
+    const size_t e0 = q0 * 4;
+    float g[kSteps], r[kSteps];
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+        const size_t e = e0 + size_t(j) * kWave + lane;
+        g[j] = __builtin_nontemporal_load(grad + e);
+        r[j] = __builtin_nontemporal_load(residual + e);
+    }
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+        const size_t e = e0 + size_t(j) * kWave + lane;
+        float rn;
+        const uint32_t c = code_and_residual(g[j] + r[j], neg, pos, rn);
+        __builtin_nontemporal_store(rn, residual + e);
+        // value 64 j + lane of the tile: byte lane % 4 of dword 16 j + lane / 4
+        const uint32_t four = quad_or(c << (8 * (lane & 3)));
+        if ((lane & 3) == 0)
+            codes[16 * j + (lane >> 2)] = four;
+    }
+    wave_lds_sync();
+    uint32_t c[kSlots];
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k)
+        c[k] = codes[kSlots * lane + k];
+    wave_lds_sync();  // these reads precede the next tile's writes
+    __builtin_nontemporal_store(fold_base3(c), payload + q0 / kSlots + lane);
+}
+
+// kDword: grad or residual without 16-byte alignment.
+template <bool kDword>
 __device__ __forceinline__ void compress_tile(const float* __restrict__ grad,
                                               float* __restrict__ residual, size_t n, float neg,
                                               float pos, uint32_t* __restrict__ payload,
                                               size_t q0, int lane, uint32_t* codes)
 {
     if (q0 + kTileF4 <= (n >> 2)) {
-        compress_full_tile(grad, residual, neg, pos, payload, q0, lane, codes);
+        if (kDword)
+            compress_dword_full_tile(grad, residual, neg, pos, payload, q0, lane, codes);
+        else
+            compress_full_tile(grad, residual, neg, pos, payload, q0, lane, codes);
     } else {
         const size_t j = q0 / kSlots + lane;
         if (j < payload_words(n))
@@ -167,8 +212,9 @@ __device__ __forceinline__ void compress_tile(const float* __restrict__ grad,
     }
 }
 
-// 16-byte-aligned grad and residual. kLoop: a capped grid strides over tiles.
-template <bool kLoop>
+// kLoop: a capped grid strides over tiles. kDword: grad or residual is 4-
+// but not 16-byte aligned.
+template <bool kLoop, bool kDword>
 __global__ __launch_bounds__(kThreads) void compress_ternary_vec_kernel(
     const float* __restrict__ grad, float* __restrict__ residual, size_t n, float neg,
     float pos, float n_f, uint32_t* __restrict__ compr, size_t ntiles)
@@ -180,23 +226,11 @@ __global__ __launch_bounds__(kThreads) void compress_ternary_vec_kernel(
     const int wave = threadIdx.x / kWave;
     const size_t stride = size_t(gridDim.x) * kWavesPerBlock;
     for (size_t t = size_t(blockIdx.x) * kWavesPerBlock + wave; t < ntiles; t += stride) {
-        compress_tile(grad, residual, n, neg, pos, compr + 3, t * kTileF4, lane, codes[wave]);
+        compress_tile<kDword>(grad, residual, n, neg, pos, compr + 3, t * kTileF4, lane,
+                              codes[wave]);
         if (!kLoop)
             break;
     }
-}
-
-// Any 4-byte alignment: one thread per element.
-__global__ __launch_bounds__(kThreads) void compress_ternary_scalar_kernel(
-    const float* __restrict__ grad, float* __restrict__ residual, size_t n, float neg,
-    float pos, float n_f, uint32_t* __restrict__ compr)
-{
-    if (blockIdx.x == 0 && threadIdx.x == 0)
-        write_header(compr, neg, pos, n_f);
-    const size_t nwords = payload_words(n);
-    const size_t stride = size_t(gridDim.x) * blockDim.x;
-    for (size_t j = size_t(blockIdx.x) * blockDim.x + threadIdx.x; j < nwords; j += stride)
-        compr[3 + j] = compress_word_scalar(grad, residual, n, neg, pos, j);
 }
 
 // Pair table in LDS: for worker w, entry 16w + p (p = 3a + b < 16) holds
@@ -269,7 +303,9 @@ __device__ __forceinline__ void decode_element(uint32_t word, const float2* t,
 // One full wave tile of the W-block dequantize-and-sum. WC > 0: W == WC at
 // compile time, every worker's element in flight at once; WC == 0: W read at
 // run time, in groups of four. `stage` is this wave's kTileF4-float4 buffer.
-template <int WC, bool kAcc>
+// kDword: out without 16-byte alignment; the staged tile leaves as
+// lane-contiguous 4-byte stores.
+template <int WC, bool kAcc, bool kDword>
 __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& tab, int W_rt,
                                                      const float2* lut, float* __restrict__ out,
                                                      size_t q0, int lane, f32x4* stage)
@@ -300,14 +336,27 @@ __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& t
         stage[kSlots * lane + k] =
             f32x4{acc[4 * k], acc[4 * k + 1], acc[4 * k + 2], acc[4 * k + 3]};
     wave_lds_sync();
-    f32x4* o4 = reinterpret_cast<f32x4*>(out);
+    if (kDword) {
+        const float* sf = reinterpret_cast<const float*>(stage);
+        float* o = out + q0 * 4;
 #pragma unroll
-    for (int u = 0; u < kSlots; ++u) {
-        const size_t q = q0 + size_t(u) * kWave + lane;
-        f32x4 v = stage[u * kWave + lane];
-        if (kAcc)
-            v = o4[q] + v;
-        __builtin_nontemporal_store(v, o4 + q);
+        for (int k = 0; k < kSlots * 4; ++k) {
+            const int e = k * kWave + lane;
+            float v = sf[e];
+            if (kAcc)
+                v = o[e] + v;
+            __builtin_nontemporal_store(v, o + e);
+        }
+    } else {
+        f32x4* o4 = reinterpret_cast<f32x4*>(out);
+#pragma unroll
+        for (int u = 0; u < kSlots; ++u) {
+            const size_t q = q0 + size_t(u) * kWave + lane;
+            f32x4 v = stage[u * kWave + lane];
+            if (kAcc)
+                v = o4[q] + v;
+            __builtin_nontemporal_store(v, o4 + q);
+        }
     }
     wave_lds_sync();  // these reads precede the next tile's writes
 }
@@ -340,7 +389,7 @@ __device__ __forceinline__ void decompress_tail_tile(const PtrTable<uint32_t>& t
 // 256-byte element runs share edge cache lines meet in one L2. The pair
 // table holds WC workers when W is known at compile time (less LDS per
 // workgroup, more workgroups per CU).
-template <int WC, bool kAcc, bool kLoop>
+template <int WC, bool kAcc, bool kLoop, bool kDword>
 __global__ __launch_bounds__(kThreads) void decompress_ternary_vec_kernel(
     PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, size_t ntiles)
 {
@@ -354,34 +403,11 @@ __global__ __launch_bounds__(kThreads) void decompress_ternary_vec_kernel(
     for (size_t t = blk * kWavesPerBlock + wave; t < ntiles; t += stride) {
         const size_t q0 = (ntiles - 1 - t) * kTileF4;
         if (q0 + kTileF4 <= (n >> 2))
-            decompress_full_tile<WC, kAcc>(tab, W, lut, out, q0, lane, stage[wave]);
+            decompress_full_tile<WC, kAcc, kDword>(tab, W, lut, out, q0, lane, stage[wave]);
         else
             decompress_tail_tile(tab, WC > 0 ? WC : W, lut, n, out, kAcc ? 1 : 0, q0, lane);
         if (!kLoop)
             break;
-    }
-}
-
-// Any 4-byte-aligned out: one thread per value.
-__global__ __launch_bounds__(kThreads) void decompress_ternary_scalar_kernel(
-    PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, int accumulate)
-{
-    __shared__ float2 lut[16 * GC_MAX_WORKERS];
-    build_pair_table(lut, tab, W);
-    const size_t stride = size_t(gridDim.x) * blockDim.x;
-    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const size_t byte_i = i / 5;
-        const uint32_t k = uint32_t(i % 5);
-        float acc = 0.0f;
-        for (int w = 0; w < W; ++w) {
-            const uint8_t* bytes = reinterpret_cast<const uint8_t*>(tab.p[w] + 3);
-            const Digits d = split_byte(bytes[byte_i]);
-            // digits 0, 1 in pair p0; 2, 3 in pair p1; 4 alone (entry 3 c4)
-            const float2 q = lut[16 * w + (k < 2u ? d.p0 : (k < 4u ? d.p1 : 3u * d.c4))];
-            const float v = (k & 1u) ? q.y : q.x;
-            acc = (w == 0) ? v : acc + v;
-        }
-        out[i] = accumulate ? out[i] + acc : acc;
     }
 }
 
@@ -395,22 +421,22 @@ bool tiles_need_loop(size_t ntiles)
     return ceil_div(ntiles, kWavesPerBlock) > max_grid_blocks();
 }
 
-template <bool kLoop>
+template <bool kLoop, bool kDword>
 void launch_decompress_vec(const PtrTable<uint32_t>& tab, int W, size_t n, float* out,
                            int accumulate, size_t ntiles, dim3 grid, dim3 block,
                            hipStream_t stream)
 {
     if (accumulate) {
         // only decompress_ternary accumulates (W == 1)
-        hipLaunchKernelGGL((decompress_ternary_vec_kernel<1, true, kLoop>), grid, block, 0,
-                           stream, tab, W, n, out, ntiles);
+        hipLaunchKernelGGL((decompress_ternary_vec_kernel<1, true, kLoop, kDword>), grid, block,
+                           0, stream, tab, W, n, out, ntiles);
         return;
     }
     switch (W) {
 #define GCQ_TDEC_CASE(k)                                                                    \
     case k:                                                                                 \
-        hipLaunchKernelGGL((decompress_ternary_vec_kernel<k, false, kLoop>), grid, block, 0, \
-                           stream, tab, W, n, out, ntiles);                                 \
+        hipLaunchKernelGGL((decompress_ternary_vec_kernel<k, false, kLoop, kDword>), grid,   \
+                           block, 0, stream, tab, W, n, out, ntiles);                       \
         break;
         GCQ_TDEC_CASE(1)
         GCQ_TDEC_CASE(2)
@@ -422,8 +448,8 @@ void launch_decompress_vec(const PtrTable<uint32_t>& tab, int W, size_t n, float
         GCQ_TDEC_CASE(8)
 #undef GCQ_TDEC_CASE
     default:
-        hipLaunchKernelGGL((decompress_ternary_vec_kernel<0, false, kLoop>), grid, block, 0,
-                           stream, tab, W, n, out, ntiles);
+        hipLaunchKernelGGL((decompress_ternary_vec_kernel<0, false, kLoop, kDword>), grid, block,
+                           0, stream, tab, W, n, out, ntiles);
     }
 }
 
@@ -432,17 +458,19 @@ int launch_decompress(const PtrTable<uint32_t>& tab, int W, size_t n, float* out
 {
     if (n == 0)
         return GC_OK;
+    const size_t ntiles = ceil_div(n, kTileElems);
+    const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
+    const bool loop = tiles_need_loop(ntiles);
     if (aligned16(out)) {
-        const size_t ntiles = ceil_div(n, kTileElems);
-        const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
-        if (tiles_need_loop(ntiles))
-            launch_decompress_vec<true>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
+        if (loop)
+            launch_decompress_vec<true, false>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
         else
-            launch_decompress_vec<false>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
+            launch_decompress_vec<false, false>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
     } else {
-        const size_t blocks = std::min(ceil_div(n, kThreads), max_grid_blocks());
-        hipLaunchKernelGGL(decompress_ternary_scalar_kernel, dim3(blocks), dim3(kThreads), 0,
-                           stream, tab, W, n, out, accumulate);
+        if (loop)
+            launch_decompress_vec<true, true>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
+        else
+            launch_decompress_vec<false, true>(tab, W, n, out, accumulate, ntiles, grid, block, stream);
     }
     return check_launch(what);
 }
@@ -467,21 +495,22 @@ GCQ_API int compress_ternary(const float* grad, float* residual, size_t n, float
     if (!aligned4(compr) || !aligned4(grad) || !aligned4(residual))
         return fail(GC_EINVAL, "compress_ternary: buffers must be 4-byte aligned");
     const float n_f = static_cast<float>(n);
-    if (n == 0 || (aligned16(grad) && aligned16(residual))) {
-        const size_t ntiles = ceil_div(n, kTileElems);
-        const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
-        if (tiles_need_loop(ntiles))
-            hipLaunchKernelGGL(compress_ternary_vec_kernel<true>, grid, block, 0, stream, grad,
-                               residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles);
-        else
-            hipLaunchKernelGGL(compress_ternary_vec_kernel<false>, grid, block, 0, stream, grad,
-                               residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles);
-    } else {
-        const size_t blocks =
-            std::min(ceil_div(payload_words(n), kThreads), max_grid_blocks());
-        hipLaunchKernelGGL(compress_ternary_scalar_kernel, dim3(blocks), dim3(kThreads), 0,
-                           stream, grad, residual, n, neg_threshold, pos_threshold, n_f, compr);
-    }
+    const size_t ntiles = ceil_div(n, kTileElems);
+    const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
+    const bool loop = tiles_need_loop(ntiles);
+    const bool dword = n > 0 && !(aligned16(grad) && aligned16(residual));
+#define GCQ_TCOMP(L, D)                                                                        \
+    hipLaunchKernelGGL((compress_ternary_vec_kernel<L, D>), grid, block, 0, stream, grad,     \
+                       residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles)
+    if (loop && dword)
+        GCQ_TCOMP(true, true);
+    else if (loop)
+        GCQ_TCOMP(true, false);
+    else if (dword)
+        GCQ_TCOMP(false, true);
+    else
+        GCQ_TCOMP(false, false);
+#undef GCQ_TCOMP
     return check_launch("compress_ternary");
 }
 

@@ -59,14 +59,14 @@ def main():
             gu.sync()
             check(np.array_equal(gu.host(out), oracle.dequantize_2bit_sum(comprs, n)),
                   f"decompress sum W={W} n={n}")
-    # ternary packing: same shapes
-    for n in (40_000 + 7, 123_457):
-        print(f"[case] capped ternary n={n}", flush=True)
+    # ternary packing: same shapes, aligned and 4 bytes off alignment
+    for n, mis in ((40_000 + 7, False), (123_457, False), (40_000 + 7, True), (123_457, True)):
+        print(f"[case] capped ternary n={n} misaligned={mis}", flush=True)
         g = si.normal_f32(n + 3, n, 0.5)
         r0 = si.normal_f32(n + 4, n, 0.2)
-        r_dev = gu.dev(r0)
+        r_dev = gu.dev(r0, mis)
         compr = gu.empty(gcq.gc_compressed_ternary_words(n), torch.int32, fill=-1)
-        gcq.compress_ternary(gu.dev(g), r_dev, -0.5, 0.5, compr)
+        gcq.compress_ternary(gu.dev(g, mis), r_dev, -0.5, 0.5, compr)
         r_or = r0.copy()
         c_or = oracle.quantize_ternary(g, r_or, -0.5, 0.5)
         gu.sync()
@@ -74,7 +74,7 @@ def main():
         check(np.array_equal(gu.host(r_dev).view(np.uint32), r_or.view(np.uint32)),
               f"ternary residual n={n}")
         base = si.normal_f32(n + 5, n, 1.0)
-        out = gu.dev(base)
+        out = gu.dev(base, mis)
         gcq.decompress_ternary(gu.dev(c_or), n, out, accumulate=True)
         gu.sync()
         check(np.array_equal(gu.host(out), (base + oracle.dequantize_ternary(c_or, n)).astype(np.float32)),
@@ -82,7 +82,7 @@ def main():
         for W in (8, 9):
             comprs = [oracle.quantize_ternary(si.normal_f32(11 * w + n, n, 0.5), np.zeros(n, np.float32),
                                               -0.3 - 0.01 * w, 0.3 + 0.02 * w) for w in range(W)]
-            out = gu.empty(n, torch.float32, fill=float("nan"))
+            out = gu.empty(n, torch.float32, misalign=mis, fill=float("nan"))
             gcq.decompress_ternary_sum([gu.dev(c) for c in comprs], n, out)
             gu.sync()
             check(np.array_equal(gu.host(out), oracle.dequantize_ternary_sum(comprs, n)),
