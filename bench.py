@@ -110,9 +110,9 @@ def parse_args():
     ap.add_argument("--skip-qsgd", action="store_true", help="time only the 2-bit step")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-extra", action="store_true",
-                    help="skip the many-tensor, GlobalRandK and ternary measurements")
+                    help="skip the many-tensor, GlobalRandK, ternary and misaligned-buffer measurements")
     ap.add_argument("--extras-only", action="store_true",
-                    help="only the many-tensor, GlobalRandK and ternary measurements (profiling)")
+                    help="only the many-tensor, GlobalRandK, ternary and misaligned-buffer measurements (profiling)")
     ap.add_argument("--extra-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline sample")
@@ -653,6 +653,63 @@ def bench_ternary(gcq, torch, np, si, steps: int):
             "oracle_ms": None, "steps": steps}
 
 
+def bench_misaligned(gcq, torch, si, steps: int):
+    """The 2-bit and ternary kernels on buffers 4 bytes off 16-byte alignment
+    (views at element offset 1, as inside a flat bucket of odd-sized
+    tensors), beside the same calls on aligned buffers: compress of one
+    ResNet-50-sized worker and the W = 8 dequantize-sum."""
+    n, W = N_C2, W_C2
+    dev = "cuda:0"
+    grads = []
+    for w in range(W):
+        g = si.uniform_f32_device(7000 + w, n + 1, dev)
+        g.mul_(2 * SIGMA_C2)
+        grads.append(g)
+    res = torch.zeros(n + 1, dtype=torch.float32, device=dev)
+    out = torch.empty(n + 1, dtype=torch.float32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def per_call(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    result = {"workload": f"compress of one worker and the W={W} dequantize-sum, n={n:,}, on "
+                          "buffers 4 bytes off 16-byte alignment (element offset 1) and on "
+                          "aligned buffers", "steps": steps}
+    for name, words, comp, dsum in (("2bit", gcq.gc_compressed_2bit_words, gcq.compress_2bit,
+                                     gcq.decompress_2bit_sum),
+                                    ("ternary", gcq.gc_compressed_ternary_words,
+                                     gcq.compress_ternary, gcq.decompress_ternary_sum)):
+        blocks = [torch.empty(words(n), dtype=torch.int32, device=dev) for _ in range(W)]
+        comp_b = 12 * n + 4 * words(n)
+        deq_b = 4 * W * words(n) + 4 * n
+        entry = {}
+        for off, key in ((1, "misaligned"), (0, "aligned")):
+            views = [g[off:off + n] for g in grads]
+            r, o = res[off:off + n], out[off:off + n]
+            for w in range(W):
+                comp(views[w], r, -THR_C2, THR_C2, blocks[w])
+            c_ms = per_call(lambda: comp(views[0], r, -THR_C2, THR_C2, blocks[0]))
+            d_ms = per_call(lambda: dsum(blocks, n, o))
+            entry[key] = {"compress_ms": round(c_ms, 5),
+                          "compress_gbs": round(comp_b / (c_ms / 1e3) / 1e9, 1),
+                          "dequant_sum_ms": round(d_ms, 5),
+                          "dequant_sum_gbs": round(deq_b / (d_ms / 1e3) / 1e9, 1)}
+        result[name] = entry
+        del blocks
+    del grads, res, out
+    torch.cuda.empty_cache()
+    return result
+
+
 def multi_bytes(sizes) -> int:
     return sum(12 * n + 4 * (3 + (n + 15) // 16) for n in sizes)
 
@@ -920,7 +977,8 @@ def main() -> int:
     if args.extras_only:
         print(json.dumps({"multi_tensor": bench_multi(gcq, torch, np, si, args.extra_steps),
                           "grandk_mn": bench_grandk(gcq, torch, np, si, args.extra_steps),
-                          "ternary": bench_ternary(gcq, torch, np, si, args.extra_steps)}),
+                          "ternary": bench_ternary(gcq, torch, np, si, args.extra_steps),
+                          "misaligned": bench_misaligned(gcq, torch, si, args.extra_steps)}),
               flush=True)
         return 0
 
@@ -985,6 +1043,7 @@ def main() -> int:
         result["multi_tensor"] = bench_multi(gcq, torch, np, si, args.extra_steps)
         result["grandk_mn"] = bench_grandk(gcq, torch, np, si, args.extra_steps)
         result["ternary"] = bench_ternary(gcq, torch, np, si, args.extra_steps)
+        result["misaligned"] = bench_misaligned(gcq, torch, si, args.extra_steps)
 
     if not args.skip_cpu_baseline:
         workloads = set()

@@ -215,9 +215,10 @@ __device__ __forceinline__ void compress_tile(const float* __restrict__ grad,
 // kLoop: a capped grid strides over tiles. kDword: grad or residual is 4-
 // but not 16-byte aligned.
 template <bool kLoop, bool kDword>
-__global__ __launch_bounds__(kThreads) void compress_ternary_vec_kernel(
-    const float* __restrict__ grad, float* __restrict__ residual, size_t n, float neg,
-    float pos, float n_f, uint32_t* __restrict__ compr, size_t ntiles)
+__device__ __forceinline__ void compress_ternary_body(const float* __restrict__ grad,
+                                                      float* __restrict__ residual, size_t n,
+                                                      float neg, float pos, float n_f,
+                                                      uint32_t* __restrict__ compr, size_t ntiles)
 {
     __shared__ uint32_t codes[kWavesPerBlock][kTileF4];
     if (blockIdx.x == 0 && threadIdx.x == 0)
@@ -231,6 +232,24 @@ __global__ __launch_bounds__(kThreads) void compress_ternary_vec_kernel(
         if (!kLoop)
             break;
     }
+}
+
+// Entry kernels of the body above, named apart so that profiles keep the
+// aligned and the 4-byte-aligned paths separate.
+template <bool kLoop>
+__global__ __launch_bounds__(kThreads) void compress_ternary_vec_kernel(
+    const float* __restrict__ grad, float* __restrict__ residual, size_t n, float neg,
+    float pos, float n_f, uint32_t* __restrict__ compr, size_t ntiles)
+{
+    compress_ternary_body<kLoop, false>(grad, residual, n, neg, pos, n_f, compr, ntiles);
+}
+
+template <bool kLoop>
+__global__ __launch_bounds__(kThreads) void compress_ternary_dword_kernel(
+    const float* __restrict__ grad, float* __restrict__ residual, size_t n, float neg,
+    float pos, float n_f, uint32_t* __restrict__ compr, size_t ntiles)
+{
+    compress_ternary_body<kLoop, true>(grad, residual, n, neg, pos, n_f, compr, ntiles);
 }
 
 // Pair table in LDS: for worker w, entry 16w + p (p = 3a + b < 16) holds
@@ -390,8 +409,9 @@ __device__ __forceinline__ void decompress_tail_tile(const PtrTable<uint32_t>& t
 // table holds WC workers when W is known at compile time (less LDS per
 // workgroup, more workgroups per CU).
 template <int WC, bool kAcc, bool kLoop, bool kDword>
-__global__ __launch_bounds__(kThreads) void decompress_ternary_vec_kernel(
-    PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, size_t ntiles)
+__device__ __forceinline__ void decompress_ternary_body(const PtrTable<uint32_t>& tab, int W,
+                                                        size_t n, float* __restrict__ out,
+                                                        size_t ntiles)
 {
     __shared__ float2 lut[16 * (WC > 0 ? WC : GC_MAX_WORKERS)];
     __shared__ f32x4 stage[kWavesPerBlock][kTileF4];
@@ -411,6 +431,20 @@ __global__ __launch_bounds__(kThreads) void decompress_ternary_vec_kernel(
     }
 }
 
+template <int WC, bool kAcc, bool kLoop>
+__global__ __launch_bounds__(kThreads) void decompress_ternary_vec_kernel(
+    PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, size_t ntiles)
+{
+    decompress_ternary_body<WC, kAcc, kLoop, false>(tab, W, n, out, ntiles);
+}
+
+template <int WC, bool kAcc, bool kLoop>
+__global__ __launch_bounds__(kThreads) void decompress_ternary_dword_kernel(
+    PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, size_t ntiles)
+{
+    decompress_ternary_body<WC, kAcc, kLoop, true>(tab, W, n, out, ntiles);
+}
+
 size_t grid_for_tiles(size_t ntiles)
 {
     return std::max<size_t>(1, std::min(ceil_div(ntiles, kWavesPerBlock), max_grid_blocks()));
@@ -428,15 +462,23 @@ void launch_decompress_vec(const PtrTable<uint32_t>& tab, int W, size_t n, float
 {
     if (accumulate) {
         // only decompress_ternary accumulates (W == 1)
-        hipLaunchKernelGGL((decompress_ternary_vec_kernel<1, true, kLoop, kDword>), grid, block,
-                           0, stream, tab, W, n, out, ntiles);
+        if (kDword)
+            hipLaunchKernelGGL((decompress_ternary_dword_kernel<1, true, kLoop>), grid, block, 0,
+                               stream, tab, W, n, out, ntiles);
+        else
+            hipLaunchKernelGGL((decompress_ternary_vec_kernel<1, true, kLoop>), grid, block, 0,
+                               stream, tab, W, n, out, ntiles);
         return;
     }
     switch (W) {
 #define GCQ_TDEC_CASE(k)                                                                    \
     case k:                                                                                 \
-        hipLaunchKernelGGL((decompress_ternary_vec_kernel<k, false, kLoop, kDword>), grid,   \
-                           block, 0, stream, tab, W, n, out, ntiles);                       \
+        if (kDword)                                                                         \
+            hipLaunchKernelGGL((decompress_ternary_dword_kernel<k, false, kLoop>), grid,    \
+                               block, 0, stream, tab, W, n, out, ntiles);                   \
+        else                                                                                \
+            hipLaunchKernelGGL((decompress_ternary_vec_kernel<k, false, kLoop>), grid,      \
+                               block, 0, stream, tab, W, n, out, ntiles);                   \
         break;
         GCQ_TDEC_CASE(1)
         GCQ_TDEC_CASE(2)
@@ -448,8 +490,12 @@ void launch_decompress_vec(const PtrTable<uint32_t>& tab, int W, size_t n, float
         GCQ_TDEC_CASE(8)
 #undef GCQ_TDEC_CASE
     default:
-        hipLaunchKernelGGL((decompress_ternary_vec_kernel<0, false, kLoop, kDword>), grid, block,
-                           0, stream, tab, W, n, out, ntiles);
+        if (kDword)
+            hipLaunchKernelGGL((decompress_ternary_dword_kernel<0, false, kLoop>), grid, block, 0,
+                               stream, tab, W, n, out, ntiles);
+        else
+            hipLaunchKernelGGL((decompress_ternary_vec_kernel<0, false, kLoop>), grid, block, 0,
+                               stream, tab, W, n, out, ntiles);
     }
 }
 
@@ -499,17 +545,17 @@ GCQ_API int compress_ternary(const float* grad, float* residual, size_t n, float
     const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
     const bool loop = tiles_need_loop(ntiles);
     const bool dword = n > 0 && !(aligned16(grad) && aligned16(residual));
-#define GCQ_TCOMP(L, D)                                                                        \
-    hipLaunchKernelGGL((compress_ternary_vec_kernel<L, D>), grid, block, 0, stream, grad,     \
-                       residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles)
+#define GCQ_TCOMP(K, L)                                                                        \
+    hipLaunchKernelGGL((K<L>), grid, block, 0, stream, grad, residual, n, neg_threshold,     \
+                       pos_threshold, n_f, compr, ntiles)
     if (loop && dword)
-        GCQ_TCOMP(true, true);
+        GCQ_TCOMP(compress_ternary_dword_kernel, true);
     else if (loop)
-        GCQ_TCOMP(true, false);
+        GCQ_TCOMP(compress_ternary_vec_kernel, true);
     else if (dword)
-        GCQ_TCOMP(false, true);
+        GCQ_TCOMP(compress_ternary_dword_kernel, false);
     else
-        GCQ_TCOMP(false, false);
+        GCQ_TCOMP(compress_ternary_vec_kernel, false);
 #undef GCQ_TCOMP
     return check_launch("compress_ternary");
 }

@@ -388,8 +388,8 @@ __device__ __forceinline__ void decompress_tail_tile(const PtrTable<uint32_t>& t
 // Dequantize-and-sum of W blocks into out (kAcc: added to what out holds);
 // kDword: out is 4- but not 16-byte aligned.
 template <int WC, bool kAcc, bool kLoop, bool kDword>
-__global__ __launch_bounds__(kThreads) void decompress_2bit_vec_kernel(
-    PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, size_t ntiles)
+__device__ __forceinline__ void decompress_2bit_body(const PtrTable<uint32_t>& tab, int W, size_t n,
+                                                     float* __restrict__ out, size_t ntiles)
 {
     __shared__ float2 lut[16 * GC_MAX_WORKERS];
     __shared__ f32x4 stage[kDword ? kWavesPerBlock : 1][kDword ? kTileF4 : 1];
@@ -413,6 +413,22 @@ __global__ __launch_bounds__(kThreads) void decompress_2bit_vec_kernel(
         if (!kLoop)
             break;
     }
+}
+
+// The two entry kernels of the body above, named apart so that profiles
+// keep the aligned and the 4-byte-aligned paths separate.
+template <int WC, bool kAcc, bool kLoop>
+__global__ __launch_bounds__(kThreads) void decompress_2bit_vec_kernel(
+    PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, size_t ntiles)
+{
+    decompress_2bit_body<WC, kAcc, kLoop, false>(tab, W, n, out, ntiles);
+}
+
+template <int WC, bool kAcc, bool kLoop>
+__global__ __launch_bounds__(kThreads) void decompress_2bit_dword_kernel(
+    PtrTable<uint32_t> tab, int W, size_t n, float* __restrict__ out, size_t ntiles)
+{
+    decompress_2bit_body<WC, kAcc, kLoop, true>(tab, W, n, out, ntiles);
 }
 
 // ---- many tensors ----------------------------------------------------------
@@ -528,15 +544,23 @@ static void launch_decompress_vec(const PtrTable<uint32_t>& tab, int W, size_t n
 {
     if (accumulate) {
         // only decompress_2bit accumulates (W == 1)
-        hipLaunchKernelGGL((decompress_2bit_vec_kernel<1, true, kLoop, kDword>), grid, block, 0,
-                           stream, tab, W, n, out, ntiles);
+        if (kDword)
+            hipLaunchKernelGGL((decompress_2bit_dword_kernel<1, true, kLoop>), grid, block, 0,
+                               stream, tab, W, n, out, ntiles);
+        else
+            hipLaunchKernelGGL((decompress_2bit_vec_kernel<1, true, kLoop>), grid, block, 0,
+                               stream, tab, W, n, out, ntiles);
         return;
     }
     switch (W) {
 #define GCQ_DEC_CASE(k)                                                                    \
     case k:                                                                                \
-        hipLaunchKernelGGL((decompress_2bit_vec_kernel<k, false, kLoop, kDword>), grid,    \
-                           block, 0, stream, tab, W, n, out, ntiles);                      \
+        if (kDword)                                                                        \
+            hipLaunchKernelGGL((decompress_2bit_dword_kernel<k, false, kLoop>), grid,      \
+                               block, 0, stream, tab, W, n, out, ntiles);                  \
+        else                                                                               \
+            hipLaunchKernelGGL((decompress_2bit_vec_kernel<k, false, kLoop>), grid, block, \
+                               0, stream, tab, W, n, out, ntiles);                         \
         break;
         GCQ_DEC_CASE(1)
         GCQ_DEC_CASE(2)
@@ -548,8 +572,12 @@ static void launch_decompress_vec(const PtrTable<uint32_t>& tab, int W, size_t n
         GCQ_DEC_CASE(8)
 #undef GCQ_DEC_CASE
     default:
-        hipLaunchKernelGGL((decompress_2bit_vec_kernel<0, false, kLoop, kDword>), grid, block, 0,
-                           stream, tab, W, n, out, ntiles);
+        if (kDword)
+            hipLaunchKernelGGL((decompress_2bit_dword_kernel<0, false, kLoop>), grid, block, 0,
+                               stream, tab, W, n, out, ntiles);
+        else
+            hipLaunchKernelGGL((decompress_2bit_vec_kernel<0, false, kLoop>), grid, block, 0,
+                               stream, tab, W, n, out, ntiles);
     }
 }
 
