@@ -74,4 +74,14 @@ __device__ __forceinline__ uint32_t quad_or(uint32_t x)
     return x;
 }
 
+// Orders this wave's LDS accesses across its lanes: LDS operations of one
+// wave complete in issue order, so it suffices that the compiler moves no
+// LDS access across this point.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 }  // namespace gcq

@@ -104,44 +104,45 @@ MaxNormGrid maxnorm_grid(size_t n)
     return MaxNormGrid{unsigned(gx), chunk4};
 }
 
-// blockIdx.y = worker. Workgroup x takes float4 slots [x chunk4, (x+1) chunk4)
-// (the scalar tail n mod 4 goes to workgroup 0) and writes their max |g|.
-// Buffers without 16-byte alignment take element chunks of 4 chunk4, the
-// last workgroup extending to n.
+// blockIdx.y = worker. The max is order-free, so a buffer off 16-byte
+// alignment splits into a head of at most 3 values and a 16-byte-aligned
+// rest. Workgroup x takes float4 slots [x chunk4, (x+1) chunk4) of the rest
+// and writes their max |g|; workgroup 0 also takes the head and the scalar
+// tail of the rest.
 __global__ __launch_bounds__(kThreads) void maxabs_partial_kernel(PtrTable<float> tab, size_t n,
                                                                   size_t chunk4,
                                                                   float* __restrict__ partials)
 {
     const float* __restrict__ g = tab.p[blockIdx.y];
+    const size_t head =
+        std::min<size_t>(((16u - (reinterpret_cast<uintptr_t>(g) & 15u)) & 15u) / 4u, n);
+    const float* __restrict__ ga = g + head;
+    const size_t na = n - head;
     float m = 0.0f;
-    if ((reinterpret_cast<uintptr_t>(g) & 15u) == 0) {
-        const f32x4* g4 = reinterpret_cast<const f32x4*>(g);
-        const size_t nfull = n >> 2;
-        const size_t lo = size_t(blockIdx.x) * chunk4;
-        const size_t hi = std::min(lo + chunk4, nfull);
-        size_t q = lo + threadIdx.x;
-        for (; q + (kMaxAbsUnroll - 1) * kThreads < hi; q += kMaxAbsUnroll * kThreads) {
-            f32x4 v[kMaxAbsUnroll];
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(ga);
+    const size_t nfull = na >> 2;
+    const size_t lo = size_t(blockIdx.x) * chunk4;
+    const size_t hi = std::min(lo + chunk4, nfull);
+    size_t q = lo + threadIdx.x;
+    for (; q + (kMaxAbsUnroll - 1) * kThreads < hi; q += kMaxAbsUnroll * kThreads) {
+        f32x4 v[kMaxAbsUnroll];
 #pragma unroll
-            for (int u = 0; u < kMaxAbsUnroll; ++u)
-                v[u] = __builtin_nontemporal_load(g4 + q + u * kThreads);
+        for (int u = 0; u < kMaxAbsUnroll; ++u)
+            v[u] = __builtin_nontemporal_load(g4 + q + u * kThreads);
 #pragma unroll
-            for (int u = 0; u < kMaxAbsUnroll; ++u)
-                m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)),
-                                   fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
-        }
-        for (; q < hi; q += kThreads) {
-            const f32x4 v = __builtin_nontemporal_load(g4 + q);
-            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-        }
-        if (blockIdx.x == 0)
-            for (size_t i = nfull * 4 + threadIdx.x; i < n; i += kThreads)
-                m = fmaxf(m, fabsf(g[i]));
-    } else {
-        const size_t lo = size_t(blockIdx.x) * chunk4 * 4;
-        const size_t hi = blockIdx.x + 1 == gridDim.x ? n : std::min(lo + chunk4 * 4, n);
-        for (size_t i = lo + threadIdx.x; i < hi; i += kThreads)
-            m = fmaxf(m, fabsf(g[i]));
+        for (int u = 0; u < kMaxAbsUnroll; ++u)
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)),
+                               fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
+    }
+    for (; q < hi; q += kThreads) {
+        const f32x4 v = __builtin_nontemporal_load(g4 + q);
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    if (blockIdx.x == 0) {
+        for (size_t i = nfull * 4 + threadIdx.x; i < na; i += kThreads)
+            m = fmaxf(m, fabsf(ga[i]));
+        if (threadIdx.x < head)
+            m = fmaxf(m, fabsf(g[threadIdx.x]));
     }
     m = block_max<kThreads>(m);
     if (threadIdx.x == 0)
@@ -277,11 +278,47 @@ __device__ __forceinline__ uint32_t pack_levels4(const int32_t t[4])
 constexpr int kQUnroll = 4;
 constexpr size_t kQTile = size_t(kWave) * kQUnroll;
 
-template <bool kLoop>
-__global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
-    const float* __restrict__ grad, size_t n, const float* __restrict__ norm_ptr, float s24,
-    uint32_t k0, uint32_t k1, uint32_t worker, int8_t* __restrict__ levels, int vec)
+// Float4 slots tb + u kWave + lane (u < U) of g, one per lane per u. kDword:
+// g is only 4-byte aligned, so the tile's 4 U kWave values come in as
+// lane-contiguous 4-byte loads (256 bytes per instruction) and are regrouped
+// into the lanes' float4 slots through the wave's LDS stage (4 U kWave
+// floats).
+template <int U, bool kDword>
+__device__ __forceinline__ void load_slots(const float* __restrict__ g, size_t tb, int lane,
+                                           f32x4 (&v)[U], float* stage)
 {
+    if (!kDword) {
+        const size_t q0 = tb + lane;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g) + q0 +
+                                              size_t(u) * kWave);
+        return;
+    }
+    const float* base = g + tb * 4;
+    float x[4 * U];
+#pragma unroll
+    for (int j = 0; j < 4 * U; ++j)
+        x[j] = __builtin_nontemporal_load(base + j * kWave + lane);
+#pragma unroll
+    for (int j = 0; j < 4 * U; ++j)
+        stage[j * kWave + lane] = x[j];
+    wave_lds_sync();
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        v[u] = reinterpret_cast<const f32x4*>(stage)[u * kWave + lane];
+    wave_lds_sync();  // these reads precede the next tile's writes
+}
+
+// kDword: grad 4- but not 16-byte aligned (loads through load_slots).
+template <bool kLoop, bool kDword>
+__device__ __forceinline__ void qsgd_quantize_body(const float* __restrict__ grad, size_t n,
+                                                   const float* __restrict__ norm_ptr, float s24,
+                                                   uint32_t k0, uint32_t k1, uint32_t worker,
+                                                   int8_t* __restrict__ levels, int vec)
+{
+    __shared__ float stage[kDword ? kThreads / kWave : 1][kDword ? 4 * kQTile : 1];
+    const bool gvec = vec && !kDword;  // grad itself 16-byte aligned
     const float norm = *norm_ptr;
     const bool fast = norm >= kFastNormMin;
     const float c = fast ? (1.0f / norm) * s24 : 0.0f;
@@ -295,10 +332,8 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
         const size_t q0 = t * kQTile + lane;
         if (vec && (t + 1) * kQTile <= nfull) {
             f32x4 g[kQUnroll];
-#pragma unroll
-            for (int u = 0; u < kQUnroll; ++u)
-                g[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(grad) + q0 +
-                                                  size_t(u) * kWave);
+            load_slots<kQUnroll, kDword>(grad, t * kQTile, lane, g,
+                                         stage[kDword ? threadIdx.x / kWave : 0]);
             uint32_t packed[kQUnroll] = {};
             if (norm != 0.0f) {
                 U4 r[kQUnroll];
@@ -329,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
 #pragma unroll
             for (int u = 0; u < kQUnroll; ++u)
                 g[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            if (vec) {
+            if (gvec) {
 #pragma unroll
                 for (int u = 0; u < kQUnroll; ++u) {
                     const size_t q = q0 + size_t(u) * kWave;
@@ -342,8 +377,8 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
                 const size_t q = q0 + size_t(u) * kWave;
                 if (q >= nslots)
                     continue;
-                const bool whole = vec && q < nfull;
-                if (!whole) {
+                const bool whole = vec && q < nfull;  // the slot's levels as one word
+                if (!(gvec && q < nfull)) {
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
                         g[u][k] = (q * 4 + k < n) ? grad[q * 4 + k] : 0.0f;
@@ -368,6 +403,24 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
         if (!kLoop)
             break;
     }
+}
+
+// Entry kernels of the body above, named apart so that profiles keep the
+// aligned and the 4-byte-aligned gradients separate.
+template <bool kLoop>
+__global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
+    const float* __restrict__ grad, size_t n, const float* __restrict__ norm_ptr, float s24,
+    uint32_t k0, uint32_t k1, uint32_t worker, int8_t* __restrict__ levels, int vec)
+{
+    qsgd_quantize_body<kLoop, false>(grad, n, norm_ptr, s24, k0, k1, worker, levels, vec);
+}
+
+template <bool kLoop>
+__global__ __launch_bounds__(kThreads) void qsgd_quantize_dword_kernel(
+    const float* __restrict__ grad, size_t n, const float* __restrict__ norm_ptr, float s24,
+    uint32_t k0, uint32_t k1, uint32_t worker, int8_t* __restrict__ levels, int vec)
+{
+    qsgd_quantize_body<kLoop, true>(grad, n, norm_ptr, s24, k0, k1, worker, levels, vec);
 }
 
 // ---- level sum + dequantize ------------------------------------------------
@@ -401,11 +454,17 @@ __device__ __forceinline__ void dequant_store(float norm, float s_f, i32x4 S, in
     __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(out) + q);
 }
 
-template <int WC>
-__global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_kernel(
-    PtrTable<int8_t> tab, int W_rt, size_t n, const float* __restrict__ norm_ptr, float s_f,
-    int32_t* __restrict__ sums, float* __restrict__ out, int vec)
+// kDword: sums and out 4- but not 16-byte aligned (levels 4-byte aligned):
+// a full tile's sums and values pass through the wave's LDS stage and leave
+// as lane-contiguous 4-byte stores.
+template <int WC, bool kDword>
+__device__ __forceinline__ void qsgd_dequant_sum_body(const PtrTable<int8_t>& tab, int W_rt,
+                                                      size_t n, const float* __restrict__ norm_ptr,
+                                                      float s_f, int32_t* __restrict__ sums,
+                                                      float* __restrict__ out, int vec)
 {
+    __shared__ i32x4 st_s[kDword ? kThreads / kWave : 1][kDword ? kDqTile : 1];
+    __shared__ f32x4 st_o[kDword ? kThreads / kWave : 1][kDword ? kDqTile : 1];
     const int W = WC > 0 ? WC : W_rt;
     const float norm = *norm_ptr;
     const size_t nslots = (n + 3) >> 2;
@@ -443,9 +502,32 @@ __global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_kernel(
                         S[u].w += sbyte(words[dw][u], 3);
                     }
             }
+            if (kDword) {
+                const int wave = threadIdx.x / kWave;
 #pragma unroll
-            for (int u = 0; u < kDqUnroll; ++u)
-                dequant_store(norm, s_f, S[u], sums, out, q0 + size_t(u) * kWave);
+                for (int u = 0; u < kDqUnroll; ++u) {
+                    st_s[wave][u * kWave + lane] = S[u];
+                    st_o[wave][u * kWave + lane] =
+                        f32x4{dequant(norm, S[u].x, s_f), dequant(norm, S[u].y, s_f),
+                              dequant(norm, S[u].z, s_f), dequant(norm, S[u].w, s_f)};
+                }
+                wave_lds_sync();
+                const int32_t* ss = reinterpret_cast<const int32_t*>(st_s[wave]);
+                const float* so = reinterpret_cast<const float*>(st_o[wave]);
+                const size_t i0 = t * kDqTile * 4;
+#pragma unroll
+                for (int j = 0; j < int(kDqTile) * 4 / kWave; ++j) {
+                    const int e = j * kWave + lane;
+                    if (sums)
+                        __builtin_nontemporal_store(ss[e], sums + i0 + e);
+                    __builtin_nontemporal_store(so[e], out + i0 + e);
+                }
+                wave_lds_sync();  // these reads precede the next tile's writes
+            } else {
+#pragma unroll
+                for (int u = 0; u < kDqUnroll; ++u)
+                    dequant_store(norm, s_f, S[u], sums, out, q0 + size_t(u) * kWave);
+            }
         } else {
             // the partial tile, or buffers without the vector alignment
 #pragma unroll 1
@@ -464,6 +546,24 @@ __global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_kernel(
             }
         }
     }
+}
+
+// Entry kernels of the body above, named apart so that profiles keep the
+// aligned and the 4-byte-aligned outputs separate.
+template <int WC>
+__global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_kernel(
+    PtrTable<int8_t> tab, int W, size_t n, const float* __restrict__ norm_ptr, float s_f,
+    int32_t* __restrict__ sums, float* __restrict__ out, int vec)
+{
+    qsgd_dequant_sum_body<WC, false>(tab, W, n, norm_ptr, s_f, sums, out, vec);
+}
+
+template <int WC>
+__global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_dword_kernel(
+    PtrTable<int8_t> tab, int W, size_t n, const float* __restrict__ norm_ptr, float s_f,
+    int32_t* __restrict__ sums, float* __restrict__ out, int vec)
+{
+    qsgd_dequant_sum_body<WC, true>(tab, W, n, norm_ptr, s_f, sums, out, vec);
 }
 
 // ---- fused quantize + level sum + dequantize --------------------------------
@@ -485,12 +585,19 @@ __global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_kernel(
 constexpr int kFUnroll = 4;
 constexpr size_t kFTile = size_t(kWave) * kFUnroll;
 
-template <int WC, bool kLoop>
-__global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_kernel(
-    PtrTable<float> tab, int W_rt, size_t n, const float* __restrict__ norm_ptr, float s24,
-    float s_f, uint32_t k0, uint32_t k1, int32_t* __restrict__ sums, float* __restrict__ out,
-    int vec)
+// kDword: some gradient, or out or sums, is 4- but not 16-byte aligned. Each
+// worker's tile comes in through load_slots' LDS stage, and the same stage
+// then regroups the sums and the values for lane-contiguous 4-byte stores.
+template <int WC, bool kLoop, bool kDword>
+__device__ __forceinline__ void qsgd_quantize_sum_body(const PtrTable<float>& tab, int W_rt,
+                                                       size_t n,
+                                                       const float* __restrict__ norm_ptr,
+                                                       float s24, float s_f, uint32_t k0,
+                                                       uint32_t k1, int32_t* __restrict__ sums,
+                                                       float* __restrict__ out, int vec)
 {
+    __shared__ float stage_all[kDword ? kThreads / kWave : 1][kDword ? 4 * kFTile : 1];
+    float* stage = stage_all[kDword ? threadIdx.x / kWave : 0];
     const int W = WC > 0 ? WC : W_rt;
     const float norm = *norm_ptr;
     const bool fast = norm >= kFastNormMin;
@@ -512,10 +619,7 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_kernel(
 #pragma unroll 1
                 for (int w = 0; w < W; ++w) {
                     f32x4 g[kFUnroll];
-#pragma unroll
-                    for (int u = 0; u < kFUnroll; ++u)
-                        g[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(tab.p[w]) +
-                                                          q0 + size_t(u) * kWave);
+                    load_slots<kFUnroll, kDword>(tab.p[w], t * kFTile, lane, g, stage);
                     U4 r[kFUnroll];
 #pragma unroll
                     for (int u = 0; u < kFUnroll; ++u) {
@@ -532,9 +636,38 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_kernel(
                     }
                 }
             }
+            if (kDword) {
+                const size_t i0 = t * kFTile * 4;
+                if (sums) {
 #pragma unroll
-            for (int u = 0; u < kFUnroll; ++u)
-                dequant_store(norm, s_f, S[u], sums, out, q0 + size_t(u) * kWave);
+                    for (int u = 0; u < kFUnroll; ++u)
+                        reinterpret_cast<i32x4*>(stage)[u * kWave + lane] = S[u];
+                    wave_lds_sync();
+#pragma unroll
+                    for (int j = 0; j < 4 * kFUnroll; ++j) {
+                        const int e = j * kWave + lane;
+                        __builtin_nontemporal_store(reinterpret_cast<const int32_t*>(stage)[e],
+                                                    sums + i0 + e);
+                    }
+                    wave_lds_sync();
+                }
+#pragma unroll
+                for (int u = 0; u < kFUnroll; ++u)
+                    reinterpret_cast<f32x4*>(stage)[u * kWave + lane] =
+                        f32x4{dequant(norm, S[u].x, s_f), dequant(norm, S[u].y, s_f),
+                              dequant(norm, S[u].z, s_f), dequant(norm, S[u].w, s_f)};
+                wave_lds_sync();
+#pragma unroll
+                for (int j = 0; j < 4 * kFUnroll; ++j) {
+                    const int e = j * kWave + lane;
+                    __builtin_nontemporal_store(stage[e], out + i0 + e);
+                }
+                wave_lds_sync();  // these reads precede the next tile's writes
+            } else {
+#pragma unroll
+                for (int u = 0; u < kFUnroll; ++u)
+                    dequant_store(norm, s_f, S[u], sums, out, q0 + size_t(u) * kWave);
+            }
         } else {
             // the partial tile, or buffers without the vector alignment
 #pragma unroll 1
@@ -573,6 +706,28 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_kernel(
         if (!kLoop)
             break;
     }
+}
+
+// Entry kernels of the body above, named apart so that profiles keep the
+// aligned and the 4-byte-aligned buffers separate.
+template <int WC, bool kLoop>
+__global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_kernel(
+    PtrTable<float> tab, int W, size_t n, const float* __restrict__ norm_ptr, float s24,
+    float s_f, uint32_t k0, uint32_t k1, int32_t* __restrict__ sums, float* __restrict__ out,
+    int vec)
+{
+    qsgd_quantize_sum_body<WC, kLoop, false>(tab, W, n, norm_ptr, s24, s_f, k0, k1, sums, out,
+                                             vec);
+}
+
+template <int WC, bool kLoop>
+__global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_dword_kernel(
+    PtrTable<float> tab, int W, size_t n, const float* __restrict__ norm_ptr, float s24,
+    float s_f, uint32_t k0, uint32_t k1, int32_t* __restrict__ sums, float* __restrict__ out,
+    int vec)
+{
+    qsgd_quantize_sum_body<WC, kLoop, true>(tab, W, n, norm_ptr, s24, s_f, k0, k1, sums, out,
+                                            vec);
 }
 
 constexpr int kFillUnroll = 4;
@@ -991,17 +1146,28 @@ GCQ_API int qsgd_maxnorm_quantize(const float* grad, size_t n, const float* norm
         return fail(GC_EINVAL, "qsgd_maxnorm_quantize: grad must be 4-byte aligned");
     if (n == 0)
         return GC_OK;
-    const int vec = (aligned16(grad) && aligned4(levels)) ? 1 : 0;
+    // vec: whole slots of levels as words (levels 4-byte aligned); the
+    // gradient's loads are float4 when it is 16-byte aligned, else staged
+    const int vec = aligned4(levels) ? 1 : 0;
+    const bool dword = vec && !aligned16(grad);
     const size_t ntiles = ceil_div(ceil_div(n, 4), kQTile);
     const size_t want = ceil_div(ntiles, kThreads / kWave);
     const dim3 grid(std::min(want, max_grid_blocks())), block(kThreads);
     const float s24 = float(s) * 16777216.0f;  // exact: s <= 127
-    if (want > max_grid_blocks())
-        hipLaunchKernelGGL(qsgd_quantize_kernel<true>, grid, block, 0, stream, grad, n, norm, s24,
-                           uint32_t(seed), uint32_t(seed >> 32), worker, levels, vec);
+    const int vec_kernel = (vec && aligned16(grad)) ? 1 : 0;
+#define GCQ_Q_LAUNCH(K, L, V)                                                                 \
+    hipLaunchKernelGGL((K<L>), grid, block, 0, stream, grad, n, norm, s24, uint32_t(seed),   \
+                       uint32_t(seed >> 32), worker, levels, V)
+    const bool loop = want > max_grid_blocks();
+    if (dword && loop)
+        GCQ_Q_LAUNCH(qsgd_quantize_dword_kernel, true, vec);
+    else if (dword)
+        GCQ_Q_LAUNCH(qsgd_quantize_dword_kernel, false, vec);
+    else if (loop)
+        GCQ_Q_LAUNCH(qsgd_quantize_kernel, true, vec_kernel);
     else
-        hipLaunchKernelGGL(qsgd_quantize_kernel<false>, grid, block, 0, stream, grad, n, norm,
-                           s24, uint32_t(seed), uint32_t(seed >> 32), worker, levels, vec);
+        GCQ_Q_LAUNCH(qsgd_quantize_kernel, false, vec_kernel);
+#undef GCQ_Q_LAUNCH
     return check_launch("qsgd_maxnorm_quantize");
 }
 
@@ -1035,7 +1201,10 @@ GCQ_API int qsgd_dequant_sum(const int8_t* const* levels, int W, size_t n, const
     if (!scatter_idx) {
         if (n == 0)
             return GC_OK;
-        const int vec = (lv_aligned && aligned16(out) && (!sums || aligned16(sums))) ? 1 : 0;
+        const bool out_aligned = aligned16(out) && (!sums || aligned16(sums));
+        // levels 4-byte aligned: word loads; outputs staged when not 16-byte aligned
+        const bool dword = lv_aligned && !out_aligned;
+        const int vec = lv_aligned ? 1 : 0;
         const size_t ntiles = ceil_div(ceil_div(n, 4), kDqTile);
         const dim3 grid(std::max<size_t>(1, std::min(ceil_div(ntiles, kThreads / kWave),
                                                      max_grid_blocks()))),
@@ -1043,8 +1212,12 @@ GCQ_API int qsgd_dequant_sum(const int8_t* const* levels, int W, size_t n, const
         switch (W) {
 #define GCQ_DQ_CASE(k)                                                                      \
     case k:                                                                                 \
-        hipLaunchKernelGGL((qsgd_dequant_sum_kernel<k>), grid, block, 0, stream, tab, W, n, \
-                           norm, s_f, sums, out, vec);                                      \
+        if (dword)                                                                          \
+            hipLaunchKernelGGL((qsgd_dequant_sum_dword_kernel<k>), grid, block, 0, stream,  \
+                               tab, W, n, norm, s_f, sums, out, vec);                       \
+        else                                                                                \
+            hipLaunchKernelGGL((qsgd_dequant_sum_kernel<k>), grid, block, 0, stream, tab, W, \
+                               n, norm, s_f, sums, out, out_aligned ? vec : 0);             \
         break;
             GCQ_DQ_CASE(1)
             GCQ_DQ_CASE(2)
@@ -1056,8 +1229,12 @@ GCQ_API int qsgd_dequant_sum(const int8_t* const* levels, int W, size_t n, const
             GCQ_DQ_CASE(8)
 #undef GCQ_DQ_CASE
         default:
-            hipLaunchKernelGGL((qsgd_dequant_sum_kernel<0>), grid, block, 0, stream, tab, W, n,
-                               norm, s_f, sums, out, vec);
+            if (dword)
+                hipLaunchKernelGGL((qsgd_dequant_sum_dword_kernel<0>), grid, block, 0, stream,
+                                   tab, W, n, norm, s_f, sums, out, vec);
+            else
+                hipLaunchKernelGGL((qsgd_dequant_sum_kernel<0>), grid, block, 0, stream, tab, W,
+                                   n, norm, s_f, sums, out, out_aligned ? vec : 0);
         }
         return check_launch("qsgd_dequant_sum");
     }
@@ -1109,9 +1286,17 @@ GCQ_API int qsgd_quantize_sum(const float* const* grads, int W, size_t n, const 
     const float s24 = float(s) * 16777216.0f;  // exact: s <= 127
     const float s_f = float(s);
     const uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
+    // every buffer is 4-byte aligned here; without 16-byte alignment
+    // everywhere, the staged kernel keeps whole tiles on the vector path
 #define GCQ_QS_LAUNCH(k)                                                                       \
     do {                                                                                       \
-        if (loop)                                                                              \
+        if (!vec && loop)                                                                      \
+            hipLaunchKernelGGL((qsgd_quantize_sum_dword_kernel<k, true>), grid, block, 0,     \
+                               stream, tab, W, n, norm, s24, s_f, k0, k1, sums, out, 1);      \
+        else if (!vec)                                                                         \
+            hipLaunchKernelGGL((qsgd_quantize_sum_dword_kernel<k, false>), grid, block, 0,    \
+                               stream, tab, W, n, norm, s24, s_f, k0, k1, sums, out, 1);      \
+        else if (loop)                                                                         \
             hipLaunchKernelGGL((qsgd_quantize_sum_kernel<k, true>), grid, block, 0, stream,   \
                                tab, W, n, norm, s24, s_f, k0, k1, sums, out, vec);            \
         else                                                                                   \

@@ -48,16 +48,6 @@ __device__ __forceinline__ void build_nibble_table(float2* lut, const PtrTable<u
     __syncthreads();
 }
 
-// Orders this wave's LDS accesses across its lanes: LDS operations of one
-// wave complete in issue order, so it suffices that the compiler moves no
-// LDS access across this point.
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Host: thresholds must satisfy neg < 0 < pos (so 0 is always code 0).
 inline int check_thresholds(float neg, float pos)
 {

@@ -141,6 +141,29 @@ def main():
         check(np.array_equal(gu.host(sums_f), S_f), f"qsgd_quantize_sum sums W={Wf}")
         check(np.array_equal(gu.host(out_f), oracle.qsgd_dequantize(S_f, nrm_f, s)),
               f"qsgd_quantize_sum dequantized W={Wf}")
+    # the same QSGD calls on buffers 4 bytes off 16-byte alignment (staged
+    # loads and stores), many more tiles than waves
+    print("[case] capped qsgd, misaligned buffers", flush=True)
+    gm_dev = [gu.dev(g, True) for g in gs]
+    gcq.qsgd_global_maxnorm(gm_dev, norm, ws)
+    lvm = [gu.empty(n, torch.int8, misalign=True) for _ in range(W)]
+    for w in range(W):
+        gcq.qsgd_maxnorm_quantize(gm_dev[w], norm, s, seed, w, lvm[w])
+    sums_m = gu.empty(n, torch.int32, misalign=True)
+    out_m = gu.empty(n, torch.float32, misalign=True, fill=float("nan"))
+    gcq.qsgd_dequant_sum(lvm, norm, s, out_m, sums=sums_m)
+    fsums_m = gu.empty(n, torch.int32, misalign=True)
+    fout_m = gu.empty(n, torch.float32, misalign=True, fill=float("nan"))
+    gcq.qsgd_quantize_sum(gm_dev, norm, s, seed, fout_m, sums=fsums_m)
+    gu.sync()
+    check(float(gu.host(norm)[0]) == float(norm_or), "qsgd misaligned norm")
+    for w in range(W):
+        check(np.array_equal(gu.host(lvm[w]), lv_or[w]), f"qsgd misaligned levels worker {w}")
+    check(np.array_equal(gu.host(sums_m), s_or) and np.array_equal(gu.host(fsums_m), s_or),
+          "qsgd misaligned sums")
+    d_or = oracle.qsgd_dequantize(s_or, norm_or, s)
+    check(np.array_equal(gu.host(out_m), d_or) and np.array_equal(gu.host(fout_m), d_or),
+          "qsgd misaligned dequantized")
     idx = oracle.randk_indices(n, 5000, 3)
     gk = gu.empty(5000, torch.float32)
     gcq.gather_f32(g_dev[0], gu.dev(idx), gk)
