@@ -336,7 +336,8 @@ def summarize_profiles(out_dir: str) -> None:
     if extra:
         stats = list(csv.DictReader(open(extra[0])))
         lines = [
-            "# Kernel durations from rocprofv3: many-tensor compress, GlobalRandK, ternary",
+            "# Kernel durations from rocprofv3: many-tensor compress, GlobalRandK, ternary, "
+            "misaligned buffers",
             "",
             "Command (repo root):",
             "",
@@ -348,7 +349,11 @@ def summarize_profiles(out_dir: str) -> None:
             "GlobalRandK-MN: n = 25,557,032, K = 10000, W = 8, s = 7; eager steps, then graph "
             "replays of the whole step. Ternary: the 2-bit step's workload (n = 25,557,032, "
             "W = 8, thresholds +-0.01) with compress_ternary + decompress_ternary_sum; 3 "
-            "warm-up, then timed, kernel-timing and graph-replayed steps.",
+            "warm-up, then timed, kernel-timing and graph-replayed steps. Misaligned "
+            "buffers: the 2-bit and ternary compress and W = 8 dequantize-sum at the "
+            "ResNet-50 size, and the QSGD-MN max-norm, quantize, level sum and fused "
+            "quantize-sum at the VGG16 size, each on buffers 4 bytes off 16-byte alignment "
+            "(the *_dword_kernel rows) and on aligned buffers.",
             "",
             "| kernel | calls | average us | min us | max us | share of GPU time |",
             "|---|---|---|---|---|---|",
@@ -706,6 +711,48 @@ def bench_misaligned(gcq, torch, si, steps: int):
         result[name] = entry
         del blocks
     del grads, res, out
+    torch.cuda.empty_cache()
+    # QSGD-MN at the VGG16 size: max-norm over the W workers, one worker's
+    # quantize, the W-level sum, and the fused quantize-sum
+    nq, s, seed = N_C3, S_C3, 0
+    qgrads = []
+    for w in range(W):
+        g = si.uniform_f32_device(7100 + w, nq + 1, dev)
+        g.mul_(2 * SIGMA_C3)
+        qgrads.append(g)
+    norm = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(gcq.qsgd_maxnorm_ws_bytes(W, nq), dtype=torch.uint8, device=dev)
+    lv_buf = [torch.empty(nq + 4, dtype=torch.int8, device=dev) for _ in range(W)]
+    sums_buf = torch.empty(nq + 1, dtype=torch.int32, device=dev)
+    out_buf = torch.empty(nq + 1, dtype=torch.float32, device=dev)
+    qsteps = max(2, steps // 4)
+    entry = {"workload": f"QSGD-MN, s={s}, W={W} x {nq:,} values; misaligned: gradients, sums "
+                         "and outputs at element offset 1, levels at byte offset 4"}
+    for off, key in ((1, "misaligned"), (0, "aligned")):
+        gv = [g[off:off + nq] for g in qgrads]
+        lv = [b[4 * off:4 * off + nq] for b in lv_buf]
+        sm, o = sums_buf[off:off + nq], out_buf[off:off + nq]
+        gcq.qsgd_global_maxnorm(gv, norm, ws)
+        for w in range(W):
+            gcq.qsgd_maxnorm_quantize(gv[w], norm, s, seed, w, lv[w])
+        entry[key] = {
+            "maxnorm_ms": round(per_call(lambda: gcq.qsgd_global_maxnorm(gv, norm, ws)), 5),
+            "quantize_one_worker_ms": round(per_call(
+                lambda: gcq.qsgd_maxnorm_quantize(gv[0], norm, s, seed, 0, lv[0])), 5),
+            "dequant_sum_ms": round(per_call(lambda: gcq.qsgd_dequant_sum(lv, norm, s, o, sums=sm)), 5),
+        }
+        for _ in range(2):
+            gcq.qsgd_quantize_sum(gv, norm, s, seed, o, sums=sm)
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(qsteps):
+            gcq.qsgd_quantize_sum(gv, norm, s, seed, o, sums=sm)
+        b.record()
+        torch.cuda.synchronize()
+        entry[key]["quantize_sum_ms"] = round(a.elapsed_time(b) / qsteps, 5)
+    result["qsgd"] = entry
+    del qgrads, lv_buf, sums_buf, out_buf, ws
     torch.cuda.empty_cache()
     return result
 
