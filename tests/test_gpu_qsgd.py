@@ -53,6 +53,39 @@ def check_deq(got, expect):
     np.testing.assert_array_equal(got, expect)
 
 
+@pytest.mark.parametrize("byte_off", [1, 2, 3])
+def test_levels_at_odd_byte_offsets(gcq, byte_off):
+    """int8 levels 1-3 bytes off 4-byte alignment take the element-by-element
+    quantize and level sum; gradients at a 4-byte offset, outputs aligned."""
+    n, W, s, seed = 70_001, 3, 127, 19
+    announce(f"qsgd levels at byte offset {byte_off}")
+    grads = [si.heavy_tailed_f32(si.grad_seed(w, 13), n, 0.02) for w in range(W)]
+    g_dev = [gu.dev(g, True) for g in grads]
+    norm = torch.empty(1, dtype=torch.float32, device=gu.DEV)
+    ws = torch.empty(gcq.qsgd_maxnorm_ws_bytes(W, n), dtype=torch.uint8, device=gu.DEV)
+    gcq.qsgd_global_maxnorm(g_dev, norm, ws)
+    bufs = [torch.full((n + 4,), 99, dtype=torch.int8, device=gu.DEV) for _ in range(W)]
+    levels = [b[byte_off:byte_off + n] for b in bufs]
+    assert all(lv.data_ptr() % 4 == byte_off % 4 for lv in levels)
+    for w in range(W):
+        gcq.qsgd_maxnorm_quantize(g_dev[w], norm, s, seed, w, levels[w])
+    sums = gu.empty(n, torch.int32, fill=-7)
+    out = gu.empty(n, torch.float32, fill=float("nan"))
+    gcq.qsgd_dequant_sum(levels, norm, s, out, sums=sums)
+    gu.sync()
+    norm_or = oracle.maxnorm(grads)
+    assert np.float32(gu.host(norm)[0]) == norm_or
+    lv_or = [oracle.qsgd_quantize(g, norm_or, s, seed, w) for w, g in enumerate(grads)]
+    for w in range(W):
+        np.testing.assert_array_equal(gu.host(levels[w]), lv_or[w])
+        # nothing written outside the view
+        np.testing.assert_array_equal(gu.host(bufs[w][:byte_off]), np.full(byte_off, 99, np.int8))
+        np.testing.assert_array_equal(gu.host(bufs[w][byte_off + n:]), np.full(4 - byte_off, 99, np.int8))
+    S = oracle.level_sum(lv_or)
+    np.testing.assert_array_equal(gu.host(sums), S)
+    check_deq(gu.host(out), oracle.qsgd_dequantize(S, norm_or, s))
+
+
 @pytest.mark.parametrize("misalign", [False, True])
 @pytest.mark.parametrize("W,n,s", [(1, 1, 127), (2, 5, 7), (3, 4097, 127), (8, 1000, 1),
                                    (5, 65536 + 3, 15), (64, 777, 127), (8, 1 << 20, 127),
