@@ -732,41 +732,43 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_sum_dword_kernel(
 
 constexpr int kFillUnroll = 4;
 
-// Zero out[0, n) with workgroups b = 0 .. nb-1 (of NT threads) of a launch:
-// lane-contiguous non-temporal float4 stores when out is 16-byte aligned
-// (vec), scalar stores otherwise.
+// Zero out[0, n) (out 4-byte aligned) with workgroups b = 0 .. nb-1 (of NT
+// threads) of a launch: lane-contiguous non-temporal float4 stores. A buffer
+// off 16-byte alignment has its head of at most 3 values zeroed by
+// workgroup 0 and the 16-byte-aligned rest filled the same way (a fill does
+// not care in which order the values are written).
 template <int NT = kThreads>
-__device__ __forceinline__ void fill_zero_range(float* __restrict__ out, size_t n, int vec,
-                                                size_t b, size_t nb)
+__device__ __forceinline__ void fill_zero_range(float* __restrict__ out, size_t n, size_t b,
+                                                size_t nb)
 {
+    const size_t head =
+        std::min<size_t>(((16u - (reinterpret_cast<uintptr_t>(out) & 15u)) & 15u) / 4u, n);
+    if (b == 0 && threadIdx.x < head)
+        out[threadIdx.x] = 0.0f;
+    out += head;
+    n -= head;
     const size_t stride = nb * NT;
     const size_t tid = b * NT + threadIdx.x;
-    if (vec) {
-        const size_t nfull = n >> 2;
-        f32x4* o4 = reinterpret_cast<f32x4*>(out);
-        const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-        // blocks of kFillUnroll * NT float4, lane-contiguous
-        const size_t per = size_t(kFillUnroll) * NT;
-        for (size_t c = b * per; c < nfull; c += nb * per) {
+    const size_t nfull = n >> 2;
+    f32x4* o4 = reinterpret_cast<f32x4*>(out);
+    const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    // blocks of kFillUnroll * NT float4, lane-contiguous
+    const size_t per = size_t(kFillUnroll) * NT;
+    for (size_t c = b * per; c < nfull; c += nb * per) {
 #pragma unroll
-            for (int u = 0; u < kFillUnroll; ++u) {
-                const size_t q = c + size_t(u) * NT + threadIdx.x;
-                if (q < nfull)
-                    __builtin_nontemporal_store(z, o4 + q);
-            }
+        for (int u = 0; u < kFillUnroll; ++u) {
+            const size_t q = c + size_t(u) * NT + threadIdx.x;
+            if (q < nfull)
+                __builtin_nontemporal_store(z, o4 + q);
         }
-        for (size_t i = nfull * 4 + tid; i < n; i += stride)
-            out[i] = 0.0f;
-    } else {
-        for (size_t i = tid; i < n; i += stride)
-            out[i] = 0.0f;
     }
+    for (size_t i = nfull * 4 + tid; i < n; i += stride)
+        out[i] = 0.0f;
 }
 
-__global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__ out, size_t n,
-                                                             int vec)
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__ out, size_t n)
 {
-    fill_zero_range(out, n, vec, blockIdx.x, gridDim.x);
+    fill_zero_range(out, n, blockIdx.x, gridDim.x);
 }
 
 // Sparse form: value k lands at out[idx[k]] (out already zeroed).
@@ -947,14 +949,14 @@ constexpr int kGkQThreads = 256;
 // gives the fill 16 waves per CU.
 __global__ __launch_bounds__(kRandKThreads) void grandk_draw_fill_kernel(
     size_t n, uint32_t K, uint32_t k0, uint32_t k1, uint32_t* __restrict__ idx, int hbits,
-    float* __restrict__ dense, size_t fill_n, int dense_vec)
+    float* __restrict__ dense, size_t fill_n)
 {
     if (blockIdx.x == 0) {
         if (K > 0)
             grandk_draw_lds(n, K, k0, k1, idx, hbits);
         return;
     }
-    fill_zero_range<kRandKThreads>(dense, fill_n, dense_vec, blockIdx.x - 1, gridDim.x - 1);
+    fill_zero_range<kRandKThreads>(dense, fill_n, blockIdx.x - 1, gridDim.x - 1);
 }
 
 // Share of the dense fill that runs beside the LDS draw in launch 1; the
@@ -980,10 +982,10 @@ size_t grandk_fill_split(size_t n, uint32_t K)
 __global__ __launch_bounds__(kThreads) void grandk_gather_fill_kernel(
     PtrTable<float> tab, int W, uint32_t K, size_t Kp, const uint32_t* __restrict__ idx,
     float* __restrict__ gathered, float* __restrict__ partials, unsigned gather_blocks,
-    float* __restrict__ dense, size_t n, int dense_vec)
+    float* __restrict__ dense, size_t n)
 {
     if (blockIdx.x >= gather_blocks) {
-        fill_zero_range(dense, n, dense_vec, blockIdx.x - gather_blocks,
+        fill_zero_range(dense, n, blockIdx.x - gather_blocks,
                         gridDim.x - gather_blocks);
         return;
     }
@@ -1240,7 +1242,7 @@ GCQ_API int qsgd_dequant_sum(const int8_t* const* levels, int W, size_t n, const
     }
     if (dense_n > 0) {
         hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(ceil_div(dense_n, 4 * kFillUnroll))),
-                           dim3(kThreads), 0, stream, out, dense_n, aligned16(out) ? 1 : 0);
+                           dim3(kThreads), 0, stream, out, dense_n);
         if (int rc = check_launch("qsgd_dequant_sum (fill)"))
             return rc;
     }
@@ -1401,7 +1403,6 @@ GCQ_API int grandk_mn_step(const float* const* grads, int W, size_t n, uint32_t 
     float* partials = reinterpret_cast<float*>(base + L.partials_off);
     const uint32_t k0 = uint32_t(seed), k1 = uint32_t(seed >> 32);
     const size_t cap = max_grid_blocks();
-    const int dense_vec = aligned16(dense) ? 1 : 0;
     // launch 1: the shared index draw; with the draw in LDS, the dense zero
     // fill runs beside it in the same launch
     size_t split = 0;  // dense[0, split) is zeroed in launch 1, the rest in launch 2
@@ -1411,8 +1412,7 @@ GCQ_API int grandk_mn_step(const float* const* grads, int W, size_t n, uint32_t 
             1, std::min(ceil_div(ceil_div(split, 4 * kFillUnroll), kRandKThreads),
                         cap > 1 ? cap - 1 : 1));
         hipLaunchKernelGGL(grandk_draw_fill_kernel, dim3(unsigned(1 + fb)), dim3(kRandKThreads),
-                           0, stream, n, K, k0, k1, idx, randk_lds_hash_bits(K), dense, split,
-                           dense_vec);
+                           0, stream, n, K, k0, k1, idx, randk_lds_hash_bits(K), dense, split);
     } else {
         const int hbits = randk_hash_bits(K);
         int32_t* heads = reinterpret_cast<int32_t*>(base + L.draw_off);
@@ -1431,7 +1431,7 @@ GCQ_API int grandk_mn_step(const float* const* grads, int W, size_t n, uint32_t 
                                                  cap > L.gather_blocks ? cap - L.gather_blocks : 1));
     hipLaunchKernelGGL(grandk_gather_fill_kernel, dim3(unsigned(L.gather_blocks + fill_blocks)),
                        dim3(kThreads), 0, stream, tab, W, K, L.Kp, idx, gathered, partials,
-                       L.gather_blocks, dense + split, rest, dense_vec);
+                       L.gather_blocks, dense + split, rest);
     if (int rc = check_launch("grandk_mn_step (gather, fill)"))
         return rc;
     // launch 3: norm, levels, sum, dequantize, scatter
