@@ -270,11 +270,13 @@ __device__ __forceinline__ uint32_t pack_levels4(const int32_t t[4])
 // Each wave takes tiles of kQTile float4 slots, kQUnroll per lane: the
 // Philox counter (q lo, q hi, worker, 0) of slot q gives the four words of
 // elements 4q .. 4q+3, and a lane's kQUnroll independent Philox chains
-// interleave to fill the VALU pipeline (the kernel is bound by that ALU
-// work, not by HBM; 8 quantizes of 138M values took 0.96 / 0.93 / 0.96 ms
-// with 2 / 4 / 8 chains). Full tiles take a branch-free vector path; the one
-// partial tile, and buffers without the vector alignment, take a checked
-// scalar path. kLoop = false: one tile per wave (the usual case).
+// interleave to fill the VALU pipeline (8 quantizes of 138M values took
+// 0.96 / 0.93 / 0.96 ms with 2 / 4 / 8 chains; the kernel sits at its HBM
+// ceiling with the Philox rounds close behind). Full tiles take a
+// branch-free vector path, through load_slots' LDS stage when the gradient
+// is only 4-byte aligned; the one partial tile, and levels without 4-byte
+// alignment, take a checked element path. kLoop = false: one tile per wave
+// (the usual case).
 constexpr int kQUnroll = 4;
 constexpr size_t kQTile = size_t(kWave) * kQUnroll;
 
@@ -354,12 +356,13 @@ __device__ __forceinline__ void qsgd_quantize_body(const float* __restrict__ gra
                 __builtin_nontemporal_store(packed[u], reinterpret_cast<uint32_t*>(levels) + q0 +
                                                            size_t(u) * kWave);
         } else {
-            // the partial tile, or buffers without the vector alignment.
-            // With the alignment, whole float4 slots are still one load
-            // and one word, and every slot's load goes out before any math
-            // (the registers are zeroed first, so that no branch rewrites
-            // a register with a load in flight); the one slot that
-            // straddles n, and unaligned buffers, go element by element.
+            // the partial tile, or levels without 4-byte alignment. Whole
+            // float4 slots are still one load (16-byte-aligned gradient)
+            // and one word (4-byte-aligned levels), and every slot's load
+            // goes out before any math (the registers are zeroed first, so
+            // that no branch rewrites a register with a load in flight); the
+            // one slot that straddles n, and other alignments, go element by
+            // element.
             f32x4 g[kQUnroll];
 #pragma unroll
             for (int u = 0; u < kQUnroll; ++u)
@@ -529,7 +532,7 @@ __device__ __forceinline__ void qsgd_dequant_sum_body(const PtrTable<int8_t>& ta
                     dequant_store(norm, s_f, S[u], sums, out, q0 + size_t(u) * kWave);
             }
         } else {
-            // the partial tile, or buffers without the vector alignment
+            // the partial tile, or levels without 4-byte alignment
 #pragma unroll 1
             for (int u = 0; u < kDqUnroll; ++u) {
                 const size_t q = q0 + size_t(u) * kWave;
@@ -579,9 +582,9 @@ __global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_dword_kernel(
 // every worker's 4 KB of the tile is one contiguous stream of loads, with
 // the lane's kFUnroll Philox chains interleaved. At W = 8 over 138M values
 // this measured 4-5% faster than one slot per thread with the workers'
-// loads grouped by four. Full tiles take a branch-free vector path; the one
-// partial tile, and buffers without the vector alignment, go slot by slot.
-// kLoop = false: one tile per wave (the usual case).
+// loads grouped by four. Full tiles take a branch-free vector path (staged
+// through LDS for buffers only 4-byte aligned); the one partial tile goes
+// slot by slot. kLoop = false: one tile per wave (the usual case).
 constexpr int kFUnroll = 4;
 constexpr size_t kFTile = size_t(kWave) * kFUnroll;
 
@@ -669,7 +672,7 @@ __device__ __forceinline__ void qsgd_quantize_sum_body(const PtrTable<float>& ta
                     dequant_store(norm, s_f, S[u], sums, out, q0 + size_t(u) * kWave);
             }
         } else {
-            // the partial tile, or buffers without the vector alignment
+            // the partial tile
 #pragma unroll 1
             for (int u = 0; u < kFUnroll; ++u) {
                 const size_t q = q0 + size_t(u) * kWave;

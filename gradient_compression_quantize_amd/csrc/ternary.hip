@@ -402,8 +402,9 @@ __device__ __forceinline__ void decompress_tail_tile(const PtrTable<uint32_t>& t
     }
 }
 
-// Dequantize-and-sum of W blocks into a 16-byte-aligned out (kAcc: added to
-// what out holds). Last tile first, XCD-contiguous, as in the 2-bit kernel:
+// Dequantize-and-sum of W blocks into out (kAcc: added to what out holds;
+// kDword: out 4- but not 16-byte aligned). Last tile first, XCD-contiguous,
+// as in the 2-bit kernel:
 // the partial tile's scalar path starts with the first wave, and tiles whose
 // 256-byte element runs share edge cache lines meet in one L2. The pair
 // table holds WC workers when W is known at compile time (less LDS per
