@@ -28,9 +28,11 @@
  *    pending there by an earlier HIP call surfaces here too). gc_last_error()
  *    gives a message for the calling thread's last failure.
  *  - Inputs and outputs of one call must not overlap unless stated.
- *  - Alignment: a 16-byte-aligned float/int8 buffer takes the vectorized
- *    path; any 4-byte-aligned float buffer is accepted. Results are
- *    identical either way.
+ *  - Alignment: float buffers need 4-byte alignment. 16-byte-aligned ones
+ *    take float4 accesses; others (views into a flat bucket, say) take the
+ *    same tiles through 4-byte accesses, at close to the same speed. int8
+ *    level buffers may have any alignment (4-byte-aligned ones are read and
+ *    written a word at a time). Results are identical in every case.
  */
 #ifndef GCQ_H
 #define GCQ_H
