@@ -183,6 +183,15 @@ def test_qsgd_vgg16_full_size_sampled(gcq):
         total += q
     np.testing.assert_array_equal(sums, total)
     check_deq(out, oracle.qsgd_dequantize(total, norm_or, s))
+    # the same step on buffers 4 bytes off 16-byte alignment (the staged
+    # kernels at full size) must reproduce the checked results bit for bit
+    announce("qsgd full size: the step on buffers 4 bytes off alignment")
+    norm_m, levels_m, sums_m, out_m = run_qsgd(gcq, grads, s, seed, misalign=True)
+    assert norm_m.view(np.uint32) == norm.view(np.uint32)
+    for w in range(W):
+        np.testing.assert_array_equal(levels_m[w], levels[w], err_msg=f"worker {w}")
+    np.testing.assert_array_equal(sums_m, sums)
+    np.testing.assert_array_equal(out_m.view(np.uint32), out.view(np.uint32))
 
 
 @pytest.mark.parametrize("n,K", [(1, 1), (1, 0), (7, 7), (1000, 1000), (100_000, 10_000),

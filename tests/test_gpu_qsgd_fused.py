@@ -121,6 +121,16 @@ def test_fused_vgg16_full_size_sampled(gcq):
     norm, sums, out = fused(gcq, g_dev, s, seed, n)
     del g_dev
     torch.cuda.empty_cache()
+    # the same step on buffers 4 bytes off 16-byte alignment (the staged
+    # kernel at full size): bit for bit the aligned results checked below
+    announce("qsgd fused full size: the step on buffers 4 bytes off alignment")
+    gm_dev = [gu.dev(g, True) for g in grads]
+    norm_m, sums_m, out_m = fused(gcq, gm_dev, s, seed, n, misalign=True)
+    del gm_dev
+    torch.cuda.empty_cache()
+    assert norm_m.view(np.uint32) == norm.view(np.uint32)
+    np.testing.assert_array_equal(sums_m, sums)
+    np.testing.assert_array_equal(out_m.view(np.uint32), out.view(np.uint32))
     announce("qsgd fused full size: oracle on samples")
     norm_or = oracle.maxnorm(grads)
     assert norm.view(np.uint32) == norm_or.view(np.uint32)

@@ -214,3 +214,17 @@ def test_resnet50_flat_gradient_full_size(gcq):
     expect = oracle.dequantize_ternary_sum(c_or, n)
     assert np.all(np.abs(got - expect) <= 1e-6 * np.abs(expect))
     assert np.array_equal(got, expect)
+    # one more iteration of worker 0 and the sum with the gradient, residual
+    # and output 4 bytes off 16-byte alignment (the 4-byte-access kernels at
+    # full size)
+    announce("ternary full size, buffers 4 bytes off alignment")
+    g = si.normal_f32(si.grad_seed(0, T), n, 0.01)
+    r_mis = gu.dev(r_or[0], True)
+    gcq.compress_ternary(gu.dev(g, True), r_mis, -thr, thr, c_dev[0])
+    c_or[0] = oracle.quantize_ternary(g, r_or[0], -thr, thr)
+    out_mis = gu.empty(n, torch.float32, misalign=True, fill=float("nan"))
+    gcq.decompress_ternary_sum(c_dev, n, out_mis)
+    gu.sync()
+    assert np.array_equal(gu.host(c_dev[0], np.uint32), c_or[0])
+    assert np.array_equal(gu.host(r_mis).view(np.uint32), r_or[0].view(np.uint32))
+    assert np.array_equal(gu.host(out_mis), oracle.dequantize_ternary_sum(c_or, n))
