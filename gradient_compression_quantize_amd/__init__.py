@@ -166,6 +166,13 @@ def _dev(t, dtype, what: str) -> ctypes.c_void_p:
     return _vp(t.data_ptr())
 
 
+def _need_norm(norm, what: str) -> None:
+    """The shared max-norm is one fp32 device scalar: refuse an empty tensor
+    (the kernels read element 0, and qsgd_global_maxnorm writes it)."""
+    if norm is not None and norm.numel() < 1:
+        raise ValueError(f"{what}: norm must hold at least one element")
+
+
 def _ptr_array(ts, dtype, what: str):
     arr = (_vp * len(ts))()
     for k, t in enumerate(ts):
@@ -335,6 +342,7 @@ def qsgd_global_maxnorm(grads: Sequence, norm, ws, stream=None) -> None:
     for g in grads:
         if g.numel() != n:
             raise ValueError("qsgd_global_maxnorm: gradients differ in size")
+    _need_norm(norm, "qsgd_global_maxnorm")
     size = _sz(ws.numel())
     _check(load().qsgd_global_maxnorm(_ptr_array(grads, torch.float32, "grads"), len(grads), n,
                                       _dev(norm, torch.float32, "norm"),
@@ -348,6 +356,7 @@ def qsgd_maxnorm_quantize(grad, norm, s: int, seed: int, worker: int, levels,
     n = grad.numel()
     if levels.numel() < n:
         raise ValueError("qsgd_maxnorm_quantize: levels too small")
+    _need_norm(norm, "qsgd_maxnorm_quantize")
     _check(load().qsgd_maxnorm_quantize(_dev(grad, torch.float32, "grad"), n,
                                         _dev(norm, torch.float32, "norm"), int(s), int(seed),
                                         int(worker), _dev(levels, torch.int8, "levels"),
@@ -367,6 +376,9 @@ def qsgd_dequant_sum(levels: Sequence, norm, s: int, out, sums=None, scatter_idx
     else:
         if scatter_idx.numel() != n or out.numel() < dense_n:
             raise ValueError("qsgd_dequant_sum: scatter_idx / out size mismatch")
+        if sums is not None and sums.numel() < n:
+            raise ValueError("qsgd_dequant_sum: sums too small")
+    _need_norm(norm, "qsgd_dequant_sum")
     _check(load().qsgd_dequant_sum(_ptr_array(levels, torch.int8, "levels"), len(levels), n,
                                    _dev(norm, torch.float32, "norm"), int(s),
                                    _dev(sums, torch.int32, "sums"),
@@ -385,6 +397,7 @@ def qsgd_quantize_sum(grads: Sequence, norm, s: int, seed: int, out, sums=None,
         raise ValueError("qsgd_quantize_sum: gradients differ in size")
     if out.numel() < n or (sums is not None and sums.numel() < n):
         raise ValueError("qsgd_quantize_sum: out or sums too small")
+    _need_norm(norm, "qsgd_quantize_sum")
     arr = _ptr_array(grads, torch.float32, "grads")
     _check(load().qsgd_quantize_sum(arr, len(grads), n, _dev(norm, torch.float32, "norm"),
                                     int(s), int(seed) & (2 ** 64 - 1),
@@ -435,6 +448,7 @@ def grandk_mn_step(grads: Sequence, K: int, seed: int, s: int, idx, dense, ws, s
         raise ValueError("grandk_mn_step: gradients differ in size")
     if idx.numel() < K or dense.numel() < n or (sums is not None and sums.numel() < K):
         raise ValueError("grandk_mn_step: idx, sums or dense too small")
+    _need_norm(norm, "grandk_mn_step")
     arr = _ptr_array(grads, torch.float32, "grads")
     size = _sz(ws.numel() * ws.element_size())
     _check(load().grandk_mn_step(arr, len(grads), n, K, int(seed) & (2 ** 64 - 1), int(s),

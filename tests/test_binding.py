@@ -115,6 +115,28 @@ def test_undersized_buffers_are_rejected():
                            FakeDev(1 << 20, torch.uint8))
 
 
+def test_scatter_sums_and_norm_sizes_are_checked():
+    """The scatter form writes sums[k] for every k < n, and every QSGD call
+    reads (or writes) norm[0]: short buffers are refused before the call."""
+    n, dense_n = 100, 1000
+    lv = [FakeDev(n, torch.int8), FakeDev(n, torch.int8)]
+    with pytest.raises(ValueError, match="sums too small"):
+        gcq.qsgd_dequant_sum(lv, FakeDev(1), 7, FakeDev(dense_n), sums=FakeDev(n - 1, torch.int32),
+                             scatter_idx=FakeDev(n, torch.int32), dense_n=dense_n)
+    empty_norm = FakeDev(0)
+    with pytest.raises(ValueError, match="norm must hold"):
+        gcq.qsgd_dequant_sum(lv, empty_norm, 7, FakeDev(n))
+    with pytest.raises(ValueError, match="norm must hold"):
+        gcq.qsgd_global_maxnorm([FakeDev(n)], empty_norm, FakeDev(1 << 16, torch.uint8))
+    with pytest.raises(ValueError, match="norm must hold"):
+        gcq.qsgd_maxnorm_quantize(FakeDev(n), empty_norm, 7, 0, 0, FakeDev(n, torch.int8))
+    with pytest.raises(ValueError, match="norm must hold"):
+        gcq.qsgd_quantize_sum([FakeDev(n)], empty_norm, 7, 0, FakeDev(n))
+    with pytest.raises(ValueError, match="norm must hold"):
+        gcq.grandk_mn_step([FakeDev(n)], 10, 0, 7, FakeDev(10, torch.int32), FakeDev(n),
+                           FakeDev(1 << 20, torch.uint8), norm=empty_norm)
+
+
 def test_library_validation_surfaces_as_gcq_error():
     n = 64
     words = gcq.gc_compressed_2bit_words(n)
