@@ -36,8 +36,6 @@ if str(ROOT) not in sys.path:
     sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
-# values per worker in the oracle's timed QSGD-MN sample
-QSGD_ORACLE_SAMPLE = 1 << 22
 N_C2 = 25_557_032              # ResNet-50 parameter count
 W_C2 = 8
 THR_C2 = 0.01
@@ -919,6 +917,15 @@ def cpu_baseline(np, si, budget_s: float, workloads=()):
     log("cpu baseline: generating inputs")
     grads = [si.normal_f32(si.grad_seed(w, 0), n, SIGMA_C2) for w in range(W)]
     res = [np.zeros(n, np.float32) for _ in range(W)]
+    gq = None
+    if "qsgd" in workloads:
+        # the whole VGG16-sized workload, drawn before the process is pinned
+        # to one core (one thread per worker; not timed)
+        from concurrent.futures import ThreadPoolExecutor
+        log(f"cpu baseline: generating the QSGD-MN inputs ({W_C3} x {N_C3})")
+        with ThreadPoolExecutor(max(1, min(W_C3, os.cpu_count() or 1))) as ex:
+            gq = list(ex.map(lambda w: si.heavy_tailed_f32(si.grad_seed(w, 0), N_C3, SIGMA_C3),
+                             range(W_C3)))
     oracle.lib()
     per = {}
     # one core for the timed loop (the oracle is single-threaded); restored after
@@ -973,21 +980,21 @@ def cpu_baseline(np, si, budget_s: float, workloads=()):
             del host, res_h
             log("cpu baseline: multi-tensor done")
         if "qsgd" in workloads:
-            # the QSGD-MN step (max-norm, W quantizes, level sum, dequantize)
-            # on QSGD_ORACLE_SAMPLE values per worker, drawn by the same
-            # heavy-tailed generator: the full 8 x 138M step would take
-            # minutes on one core
-            m, Wq, sq = QSGD_ORACLE_SAMPLE, W_C3, S_C3
-            gq = [si.heavy_tailed_f32(si.grad_seed(w, 0), m, SIGMA_C3) for w in range(Wq)]
+            # the whole QSGD-MN step (max-norm, W quantizes, level sum,
+            # dequantize) on the full workload: about 15 s on one core
+            Wq, sq = W_C3, S_C3
             c0 = time.perf_counter()
             nrm = oracle.maxnorm(gq)
             lv = [oracle.qsgd_quantize(gq[w], nrm, sq, 0, w) for w in range(Wq)]
             oracle.qsgd_dequantize(oracle.level_sum(lv), nrm, sq)
             el_q = time.perf_counter() - c0
-            per["qsgd"] = {"sample": f"the step on {Wq} workers x {m:,} heavy-tailed values",
+            del lv
+            per["qsgd"] = {"sample": f"the whole step on {Wq} workers x {N_C3:,} heavy-tailed "
+                                     "values (the full workload)",
                            "ms": el_q * 1e3,
-                           "values_per_s": Wq * m / el_q}
-            log("cpu baseline: qsgd sample done")
+                           "values_per_s": Wq * N_C3 / el_q}
+            log(f"cpu baseline: qsgd step done ({el_q:.1f} s)")
+        del gq
     finally:
         if saved:
             os.sched_setaffinity(0, saved)

@@ -6,8 +6,8 @@ composition of its per-worker quantize, level sum and dequantize.
 Workloads: ragged sizes and worker counts (compile-time and run-time W),
 both alignments, with and without the sums output; zero and extreme norms;
 level edges; and the VGG16-sized heavy-tailed gradient (W = 8 x 138,357,544
-values ~ N(0, 0.02^2), entries scaled by 50 with probability 0.001, s = 127)
-checked on sampled elements plus properties over every element.
+values ~ N(0, 0.02^2), entries scaled by 50 with probability 0.001, s = 127),
+every element against the oracle.
 """
 import numpy as np
 import pytest
@@ -108,49 +108,24 @@ def test_fused_level_edges(gcq, s):
 
 
 @pytest.mark.slow
-def test_fused_vgg16_full_size_sampled(gcq):
+def test_fused_vgg16_full_size(gcq):
     """8 workers x 138,357,544 heavy-tailed values, s = 127, seed 0: the fused
-    kernel in the launch configuration the benchmark times."""
-    n, W, s, seed = si.VGG16_PARAMS, 8, 127, 0
-    g_dev, grads = [], []
-    for w in range(W):
-        announce(f"qsgd fused full size: generating worker {w}")
-        grads.append(si.heavy_tailed_f32(si.grad_seed(w, 0), n, 0.02))
-        g_dev.append(gu.dev(grads[-1]))
-    announce("qsgd fused full size: device step")
-    norm, sums, out = fused(gcq, g_dev, s, seed, n)
-    del g_dev
-    torch.cuda.empty_cache()
-    # the same step on buffers 4 bytes off 16-byte alignment (the staged
-    # kernel at full size): bit for bit the aligned results checked below
-    announce("qsgd fused full size: the step on buffers 4 bytes off alignment")
-    gm_dev = [gu.dev(g, True) for g in grads]
-    norm_m, sums_m, out_m = fused(gcq, gm_dev, s, seed, n, misalign=True)
-    del gm_dev
-    torch.cuda.empty_cache()
-    assert norm_m.view(np.uint32) == norm.view(np.uint32)
-    np.testing.assert_array_equal(sums_m, sums)
-    np.testing.assert_array_equal(out_m.view(np.uint32), out.view(np.uint32))
-    announce("qsgd fused full size: oracle on samples")
-    norm_or = oracle.maxnorm(grads)
-    assert norm.view(np.uint32) == norm_or.view(np.uint32)
-    rng = np.random.default_rng(321)
-    samp = np.unique(np.concatenate([rng.integers(0, n, 400_000),
-                                     np.arange(0, 64), np.arange(n - 64, n)])).astype(np.uint64)
-    si_ = samp.astype(np.int64)
-    lv = [oracle.qsgd_quantize_at(grads[w][si_], samp, norm_or, s, seed, w) for w in range(W)]
-    S_or = oracle.level_sum(lv)
-    np.testing.assert_array_equal(sums[si_], S_or)
-    check_deq(out[si_], oracle.qsgd_dequantize(S_or, norm_or, s))
-    announce("qsgd fused full size: properties over every element")
-    # each sum lies between the sums of the floors and of the floors + 1
-    lo = np.zeros(n, np.int64)
-    hi = np.zeros(n, np.int64)
-    for g in grads:
-        x = (np.abs(g) / norm_or).astype(np.float32) * np.float32(s)
-        fl = np.floor(x).astype(np.int64)
-        sg = np.sign(g).astype(np.int64)
-        lo += np.minimum(sg * fl, sg * (fl + 1))
-        hi += np.maximum(sg * fl, sg * (fl + 1))
-    assert np.all((sums >= lo) & (sums <= hi))
-    check_deq(out, oracle.qsgd_dequantize(sums, norm_or, s))
+    kernel in the launch configuration the benchmark times, and on buffers 4
+    bytes off 16-byte alignment (the staged kernel at full size). Every int32
+    sum and every dequantized value against the oracle's run over all
+    elements."""
+    import vgg16_case as vc
+    announce(f"qsgd fused full size: generating {vc.W} workers x {vc.N} values")
+    grads = vc.grads()
+    for misalign in (False, True):
+        announce(f"qsgd fused full size: device step (misalign={misalign})")
+        g_dev = [gu.dev(g, misalign) for g in grads]
+        norm, sums, out = fused(gcq, g_dev, vc.S, vc.SEED, vc.N, misalign=misalign)
+        del g_dev
+        torch.cuda.empty_cache()
+        announce("qsgd fused full size: oracle over every element")
+        norm_or, _, S_or, out_or = vc.oracle_step()
+        assert norm.view(np.uint32) == norm_or.view(np.uint32)
+        np.testing.assert_array_equal(sums, S_or, err_msg=f"misalign={misalign}")
+        check_deq(out, out_or)
+        del sums, out
