@@ -21,9 +21,12 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB_PATH = PKG / "libgcq.so"
+CEILINGS_LIB_PATH = PKG / "libgcq_ceilings.so"
 BUILD_DIR = PKG / "_build"
 
 SOURCES = ["status.hip", "twobit.hip", "ternary.hip", "qsgd.hip"]
+# the benchmark's HBM ceiling kernels: a library of their own
+CEILINGS_SOURCES = ["hbm_ceilings.hip"]
 
 # Options of both passes.
 COMMON_FLAGS = [
@@ -84,11 +87,17 @@ def link_shared(objs, lib_path: pathlib.Path, verbose: bool = False) -> pathlib.
 
 
 def build(verbose: bool = False) -> pathlib.Path:
-    """Compile every HIP source into libgcq.so (always recompiles)."""
+    """Compile every HIP source into libgcq.so, and the benchmark's ceiling
+    kernels into libgcq_ceilings.so (always recompiles)."""
     out = BUILD_DIR / "gcq"
     out.mkdir(parents=True, exist_ok=True)
     objs = [compile_source(CSRC / s, out, (INCLUDE, CSRC), verbose) for s in SOURCES]
-    return link_shared(objs, LIB_PATH, verbose)
+    link_shared(objs, LIB_PATH, verbose)
+    cout = BUILD_DIR / "ceilings"
+    cout.mkdir(parents=True, exist_ok=True)
+    cobjs = [compile_source(CSRC / s, cout, (INCLUDE,), verbose) for s in CEILINGS_SOURCES]
+    link_shared(cobjs, CEILINGS_LIB_PATH, verbose)
+    return LIB_PATH
 
 
 if __name__ == "__main__":
