@@ -15,7 +15,8 @@ Two method families (see include/gcq.h for exact semantics):
     Plan2bitMulti / compress_2bit_multi, and the same codes packed five per
     byte: compress_ternary, decompress_ternary, decompress_ternary_sum;
   * QSGDMaxNorm stochastic quantization and GlobalRandK (vineeths96
-    "Gradient-Compression"): qsgd_global_maxnorm, qsgd_maxnorm_quantize,
+    "Gradient-Compression"): qsgd_global_maxnorm (and qsgd_global_maxnorm_noalloc,
+    which needs no workspace), qsgd_maxnorm_quantize,
     qsgd_dequant_sum, qsgd_quantize_sum (the W quantizes and the level sum fused),
     grandk_indices, gather_f32, and grandk_mn_step (the whole GRandK-MN step).
 """
@@ -83,6 +84,7 @@ def _declare(L):
     L.gc_plan_destroy.restype = None
     L.qsgd_global_maxnorm.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _vp,
                                       ctypes.POINTER(_sz), _vp]
+    L.qsgd_global_maxnorm_noalloc.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _vp]
     L.qsgd_maxnorm_quantize.argtypes = [_vp, _sz, _vp, _i, ctypes.c_uint64, ctypes.c_uint32,
                                         _vp, _vp]
     L.qsgd_dequant_sum.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _i, _vp, _vp, _vp, _sz,
@@ -97,7 +99,8 @@ def _declare(L):
     for name in ("compress_2bit", "decompress_2bit", "decompress_2bit_sum",
                  "compress_ternary", "decompress_ternary", "decompress_ternary_sum",
                  "gc_plan_2bit_multi_create", "gc_plan_block_offsets", "compress_2bit_multi",
-                 "qsgd_global_maxnorm", "qsgd_maxnorm_quantize", "qsgd_dequant_sum",
+                 "qsgd_global_maxnorm", "qsgd_global_maxnorm_noalloc",
+                 "qsgd_maxnorm_quantize", "qsgd_dequant_sum",
                  "qsgd_quantize_sum",
                  "grandk_indices", "gather_f32", "grandk_mn_step"):
         getattr(L, name).restype = _i
@@ -348,6 +351,20 @@ def qsgd_global_maxnorm(grads: Sequence, norm, ws, stream=None) -> None:
                                       _dev(norm, torch.float32, "norm"),
                                       _dev(ws, torch.uint8, "ws"), ctypes.byref(size),
                                       _stream(stream)))
+
+
+def qsgd_global_maxnorm_noalloc(grads: Sequence, norm, stream=None) -> None:
+    """qsgd_global_maxnorm without a workspace: the partial maxima go to the
+    library's fixed device array. Calls that overlap on one device race."""
+    torch = _torch()
+    n = grads[0].numel()
+    for g in grads:
+        if g.numel() != n:
+            raise ValueError("qsgd_global_maxnorm_noalloc: gradients differ in size")
+    _need_norm(norm, "qsgd_global_maxnorm_noalloc")
+    _check(load().qsgd_global_maxnorm_noalloc(_ptr_array(grads, torch.float32, "grads"),
+                                              len(grads), n, _dev(norm, torch.float32, "norm"),
+                                              _stream(stream)))
 
 
 def qsgd_maxnorm_quantize(grad, norm, s: int, seed: int, worker: int, levels,

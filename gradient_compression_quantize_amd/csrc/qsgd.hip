@@ -15,6 +15,8 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
+#include <string>
 
 namespace gcq {
 namespace {
@@ -1101,6 +1103,40 @@ size_t grid_for(size_t items)
 
 using namespace gcq;
 
+namespace gcq {
+namespace {
+
+// The two launches of the max-norm, with the partial maxima in `partials`
+// (mg.gx * W floats of device memory). Arguments are validated by the caller.
+int launch_maxnorm(const PtrTable<float>& tab, int W, size_t n, const MaxNormGrid& mg,
+                   float* partials, float* norm, hipStream_t stream)
+{
+    hipLaunchKernelGGL(maxabs_partial_kernel, dim3(mg.gx, unsigned(W)), dim3(kThreads), 0, stream,
+                       tab, n, mg.chunk4, partials);
+    if (int rc = check_launch("qsgd_global_maxnorm (partials)"))
+        return rc;
+    hipLaunchKernelGGL(max_final_kernel, dim3(1), dim3(kFinalThreads), 0, stream, partials,
+                       mg.gx * unsigned(W), norm);
+    return check_launch("qsgd_global_maxnorm (final)");
+}
+
+// Validates the gradient pointers and the output of a max-norm call.
+int maxnorm_table(const char* what, const float* const* grads, int W, size_t n, float* norm,
+                  PtrTable<float>& tab)
+{
+    if (!grads || !norm || !aligned4(norm))
+        return fail(GC_EINVAL, std::string(what) + ": NULL or misaligned pointer");
+    for (int w = 0; w < W; ++w) {
+        if ((n > 0 && !grads[w]) || !aligned4(grads[w]))
+            return fail(GC_EINVAL, std::string(what) + ": a gradient pointer is NULL or misaligned");
+        tab.p[w] = grads[w];
+    }
+    return GC_OK;
+}
+
+}  // namespace
+}  // namespace gcq
+
 GCQ_API int qsgd_global_maxnorm(const float* const* grads, int W, size_t n, float* norm, void* ws,
                                 size_t* ws_bytes, hipStream_t stream)
 {
@@ -1110,30 +1146,83 @@ GCQ_API int qsgd_global_maxnorm(const float* const* grads, int W, size_t n, floa
     if (!ws_bytes)
         return fail(GC_EINVAL, "qsgd_global_maxnorm: ws_bytes is NULL");
     const MaxNormGrid mg = maxnorm_grid(n);
-    const unsigned gx = mg.gx;
-    const size_t need = size_t(gx) * size_t(W) * sizeof(float);
+    const size_t need = size_t(mg.gx) * size_t(W) * sizeof(float);
     if (!ws) {
         *ws_bytes = need;
         return GC_OK;
     }
     if (*ws_bytes < need || !aligned4(ws))
         return fail(GC_EINVAL, "qsgd_global_maxnorm: workspace too small or misaligned");
-    if (!grads || !norm || !aligned4(norm))
-        return fail(GC_EINVAL, "qsgd_global_maxnorm: NULL or misaligned pointer");
     PtrTable<float> tab{};
-    for (int w = 0; w < W; ++w) {
-        if ((n > 0 && !grads[w]) || !aligned4(grads[w]))
-            return fail(GC_EINVAL, "qsgd_global_maxnorm: a gradient pointer is NULL or misaligned");
-        tab.p[w] = grads[w];
-    }
-    float* partials = static_cast<float*>(ws);
-    hipLaunchKernelGGL(maxabs_partial_kernel, dim3(gx, unsigned(W)), dim3(kThreads), 0, stream,
-                       tab, n, mg.chunk4, partials);
-    if (int rc = check_launch("qsgd_global_maxnorm (partials)"))
+    if (int rc = maxnorm_table("qsgd_global_maxnorm", grads, W, n, norm, tab))
         return rc;
-    hipLaunchKernelGGL(max_final_kernel, dim3(1), dim3(kFinalThreads), 0, stream, partials,
-                       gx * unsigned(W), norm);
-    return check_launch("qsgd_global_maxnorm (final)");
+    return launch_maxnorm(tab, W, n, mg, static_cast<float*>(ws), norm, stream);
+}
+
+// ---- the max-norm without a workspace ---------------------------------------
+//
+// For callers that cannot allocate (code under HIP graph capture, tight
+// loops): the partial maxima go to this file-scope device array instead of a
+// caller workspace. It holds the most partials any valid call makes:
+// kMaxPartialsPerWorker workgroups for each of GC_MAX_WORKERS workers, 1 MiB;
+// each device the library runs on keeps its own copy until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address on each device comes from hipGetSymbolAddress, once per
+// device, and only that address is passed to the kernels.
+constexpr size_t kScratchFloats = size_t(gcq::kMaxPartialsPerWorker) * GC_MAX_WORKERS;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+namespace gcq {
+namespace {
+
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kScratchMaxDevices] = {};
+
+// Device address of `scratch` on the current device: looked up on the first
+// call on that device (with that device current), then remembered.
+int scratch_on_current_device(float** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(GC_EHIP, std::string("qsgd_global_maxnorm_noalloc: hipGetDevice: ") +
+                                 hipGetErrorString(e));
+    if (dev < 0 || dev >= kScratchMaxDevices)
+        return fail(GC_EUNSUPPORTED, "qsgd_global_maxnorm_noalloc: device index above 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(GC_EHIP, std::string("qsgd_global_maxnorm_noalloc: hipGetSymbolAddress: ") +
+                                     hipGetErrorString(e));
+        g_scratch_dev[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_dev[dev];
+    return GC_OK;
+}
+
+}  // namespace
+}  // namespace gcq
+
+GCQ_API int qsgd_global_maxnorm_noalloc(const float* const* grads, int W, size_t n, float* norm,
+                                        hipStream_t stream)
+{
+    clear_error();
+    if (W < 1 || W > GC_MAX_WORKERS)
+        return fail(GC_EINVAL, "qsgd_global_maxnorm_noalloc: W must be in [1, 64]");
+    const MaxNormGrid mg = maxnorm_grid(n);
+    if (size_t(mg.gx) * size_t(W) > kScratchFloats)
+        return fail(GC_EUNSUPPORTED, "qsgd_global_maxnorm_noalloc: the partial maxima exceed "
+                                     "the fixed 1 MiB device array");
+    PtrTable<float> tab{};
+    if (int rc = maxnorm_table("qsgd_global_maxnorm_noalloc", grads, W, n, norm, tab))
+        return rc;
+    float* partials = nullptr;
+    if (int rc = scratch_on_current_device(&partials))
+        return rc;
+    return launch_maxnorm(tab, W, n, mg, partials, norm, stream);
 }
 
 GCQ_API int qsgd_maxnorm_quantize(const float* grad, size_t n, const float* norm, int s,

@@ -191,6 +191,22 @@ int qsgd_global_maxnorm(const float* const* grads, int W, size_t n,
                         float* norm, void* ws, size_t* ws_bytes,
                         hipStream_t stream);
 
+/* qsgd_global_maxnorm for callers that cannot allocate or hand in a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. Same result, same launches; the partial maxima
+ * live in a fixed device array of the library (1 MiB, one per device, held
+ * until the process ends) instead of `ws`. No device or host memory is
+ * allocated by the call (the array's device address is looked up once per
+ * device, on the first call there).
+ *   grads  HOST array of W device pointers, each [n] fp32;  W 1 .. 64
+ *   norm   device fp32 scalar (output)
+ * Every valid (W, n) fits the array; GC_EUNSUPPORTED would name a size
+ * beyond it. All calls on one device share that device's array: calls that
+ * overlap on one device (other streams, other host threads) race and must
+ * be serialized by the caller. */
+int qsgd_global_maxnorm_noalloc(const float* const* grads, int W, size_t n, float* norm,
+                                hipStream_t stream);
+
 /* levels[i] = sign(grad[i]) * floor(|grad[i]| / norm * s + u_i), with
  *   x = (|grad[i]| / norm) * s rounded to fp32 after each operation,
  *   the floor of x + u_i taken exactly (never rounding up to s + 1),
