@@ -80,8 +80,12 @@ PROFILE_COMMANDS = {
                  "--output-format csv -- python3 -u bench.py --calibrate-copy",
     "cal_write": "rocprofv3 --pmc WRITE_SIZE -T -d prof_out/pmc_cal_write -o cal "
                  "--output-format csv -- python3 -u bench.py --calibrate-copy",
+    "ceilings": "rocprofv3 --kernel-trace --stats -T -d prof_out/prof_ceilings -o ceil "
+                "--output-format csv -- python3 -u bench.py --calibrate-ceilings",
     "summary": "python3 bench.py --summarize-profiles prof_out",
 }
+PROFILE_CEILINGS = ROOT / "profiles" / "hbm_ceilings.md"
+CEILING_SOURCES = [ROOT / "gradient_compression_quantize_amd" / "csrc" / "hbm_ceilings.hip"]
 
 
 def log(msg: str) -> None:
@@ -116,14 +120,20 @@ def parse_args():
                     help="CPU time budget of the oracle baseline sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB (counter calibration)")
+    ap.add_argument("--calibrate-ceilings", action="store_true",
+                    help="only time the HBM ceiling kernels (plain streams with each hot-path "
+                         "kernel's access mix) and print their rates")
+    ap.add_argument("--skip-ceilings", action="store_true",
+                    help="do not time the HBM ceiling kernels (no frac_of_ceiling fields)")
+    ap.add_argument("--ceiling-steps", type=int, default=20)
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 output under DIR")
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (KERNEL_SOURCES if sources is None else sources):
         h.update(f.read_bytes())
     return h.hexdigest()
 
@@ -220,10 +230,78 @@ def summarize_valu(d: pathlib.Path) -> pathlib.Path | None:
     return PROFILE_VALU
 
 
+def ceiling_kernel_bytes() -> dict:
+    """Bytes per launch of each ceiling kernel at the sizes measure_ceilings
+    uses (the workloads rounded down to whole 16384-value quanta)."""
+    Q = 16384
+    n2, n3 = N_C2 // Q * Q, N_C3 // Q * Q
+    return {
+        "ceil_read_chunked_kernel": (4 * W_C3 * n3, "read, chunked (8 buffers per launch)"),
+        "ceil_read_tile_kernel": (4 * n3, "read, one tile per wave (1 buffer per launch)"),
+        "ceil_levelsum_mix_kernel": ((W_C3 + 8) * n3, "level-sum mix (W = 8)"),
+        "ceil_quantize_mix_kernel": (5 * n3, "quantize mix"),
+        "ceil_write_tile_kernel": (4 * n2, "write, one tile per wave"),
+        "ceil_write_stride_kernel": (4 * n2, "write, grid-stride"),
+        "ceil_compress_mix_kernel": (compress_bytes(n2), "compress mix"),
+        "ceil_dequant_tile_kernel": (dequant_sum_bytes(n2, W_C2), "dequantize-sum mix, the kernel's pattern"),
+        "ceil_dequant_wide_kernel": (dequant_sum_bytes(n2, W_C2), "dequantize-sum mix, wide reads"),
+        "ceil_dequant_burst_kernel": (dequant_sum_bytes(n2, W_C2), "dequantize-sum mix, workgroup bursts"),
+    }
+
+
+def summarize_ceilings(d: pathlib.Path) -> pathlib.Path | None:
+    """profiles/hbm_ceilings.md from the kernel trace of --calibrate-ceilings."""
+    import csv
+    files = list((d / "prof_ceilings").glob("*kernel_stats.csv")) if (d / "prof_ceilings").exists() else []
+    if not files:
+        return None
+    stats = {r["Name"]: r for r in csv.DictReader(open(files[0]))}
+    Q = 16384
+    lines = [
+        "# HBM ceilings of the hot path's access mixes (rocprofv3 kernel trace)",
+        "",
+        "Commands (repo root):",
+        "",
+        f"    {PROFILE_COMMANDS['ceilings']}",
+        f"    {PROFILE_COMMANDS['summary']}",
+        "",
+        "Plain streaming kernels (`gradient_compression_quantize_amd/csrc/hbm_ceilings.hip`, "
+        "built into `libgcq_ceilings.so`) that move exactly the bytes of one hot-path kernel in "
+        "its tile shapes, with trivial arithmetic in place of the quantization. Sizes: "
+        f"{N_C3 // Q * Q:,} values (VGG16, rounded down to a multiple of {Q}) for read, level sum "
+        f"and quantize; {N_C2 // Q * Q:,} (ResNet-50, rounded) for write, compress and the "
+        "dequantize-sum. Each launch rotates over buffer sets larger than the Infinity Cache. "
+        "`bench.py` times the same kernels live with events in every default run and reports "
+        "each hot-path kernel's rate over its mix's best rate as `frac_of_ceiling`.",
+        "",
+        "| kernel | mix | calls | average us | bytes per launch | GB/s | % of 8 TB/s |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    for k, (nb, what) in ceiling_kernel_bytes().items():
+        r = stats.get(k)
+        if not r:
+            continue
+        us = float(r["AverageNs"]) / 1e3
+        gbs = nb / (us * 1e-6) / 1e9
+        lines.append(f"| {k} | {what} | {r['Calls']} | {us:.2f} | {nb:,} | {gbs:,.0f} | "
+                     f"{100 * gbs / HBM_PEAK_GBS:.1f} |")
+    lines += ["", f"ceiling_source_sha256: {kernel_source_hash(CEILING_SOURCES)}", ""]
+    PROFILE_CEILINGS.write_text("\n".join(lines))
+    return PROFILE_CEILINGS
+
+
 def summarize_profiles(out_dir: str) -> None:
-    """Write the two profiles/ summaries from rocprofv3 CSV output."""
+    """Write the profiles/ summaries whose rocprofv3 CSV output is under
+    out_dir (each summary needs only its own runs)."""
     import csv
     d = pathlib.Path(out_dir)
+    wrote = []
+    c = summarize_ceilings(d)
+    if c:
+        wrote.append(c)
+    if not (d / "pmc_cal_fetch").exists():
+        print("wrote " + ", ".join(str(w) for w in wrote))
+        return
     n2, W2, n3, W3 = N_C2, W_C2, N_C3, W_C3
     algo = {
         "compress_2bit_vec_kernel": (8 * n2, 4 * n2 + 4 * (3 + (n2 + 15) // 16)),
@@ -329,7 +407,7 @@ def summarize_profiles(out_dir: str) -> None:
                   f"{HBM_PEAK_GBS:,.0f} GB/s."]
     lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
     PROFILE_STATS.write_text("\n".join(lines))
-    wrote = [PROFILE_TRAFFIC, PROFILE_STATS]
+    wrote += [PROFILE_TRAFFIC, PROFILE_STATS]
     extra = list((d / "prof_extra").glob("*kernel_stats.csv")) if (d / "prof_extra").exists() else []
     if extra:
         stats = list(csv.DictReader(open(extra[0])))
@@ -405,6 +483,97 @@ def calibrate_copy() -> None:
                       "bytes_written": 4 * n, "launches": 3}), flush=True)
 
 
+def measure_ceilings(torch, steps: int) -> dict:
+    """What this part's HBM gives each access mix of the hot path: the plain
+    streaming kernels of libgcq_ceilings.so, which move exactly a hot-path
+    kernel's bytes in its tile shapes with trivial arithmetic, timed with
+    events around `steps` back-to-back launches that rotate over buffer sets
+    (each mix's rotation is larger than the 256 MB Infinity Cache). Sizes
+    are the workloads' rounded down to whole 16384-value quanta. For each
+    mix: bytes per launch, ms per launch of every pattern, the best pattern
+    and its rate."""
+    from gradient_compression_quantize_amd import ceilings as cl
+    Q = cl.quantum()
+    n2, n3 = N_C2 // Q * Q, N_C3 // Q * Q
+    dev = "cuda"
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def zeros(count, dtype=torch.float32):
+        return torch.zeros(count, dtype=dtype, device=dev)
+
+    def timed(fns) -> float:
+        for _ in range(2):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        a, b = mk(), mk()
+        a.record()
+        for k in range(steps):
+            fns[k % len(fns)]()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    def entry(nbytes, ms_by_pattern, n):
+        best = min(ms_by_pattern, key=ms_by_pattern.get)
+        gbs = nbytes / (ms_by_pattern[best] / 1e3) / 1e9
+        return {"n": n, "bytes": nbytes, "ms": {k: round(v, 5) for k, v in ms_by_pattern.items()},
+                "best": best, "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+    out = {"workloads": f"read and level sum at n = {n3:,} (VGG16 size, W = {W_C3}); write, "
+                        f"compress and dequantize-sum at n = {n2:,} (ResNet-50 size, W = {W_C2})",
+           "steps": steps}
+    log("ceilings: read (the max-norm's stream)")
+    bufs = [zeros(n3) for _ in range(W_C3)]
+    sink = zeros(cl.read_sink_words(W_C3, n3), torch.int32)
+    out["read"] = entry(4 * W_C3 * n3, {
+        "chunked": timed([lambda: cl.read(bufs, n3, cl.READ_CHUNKED, sink)]),
+        "tile": timed([lambda: cl.read(bufs, n3, cl.READ_TILE, sink)])}, n3)
+    del bufs, sink
+    log("ceilings: level-sum mix")
+    lv = [zeros(n3 // 4, torch.int32) for _ in range(W_C3)]
+    sums, o3 = zeros(n3, torch.int32), zeros(n3)
+    out["levelsum_mix"] = entry((W_C3 + 8) * n3,
+                                {"tile": timed([lambda: cl.levelsum(lv, n3, sums, o3)])}, n3)
+    del lv, sums
+    log("ceilings: quantize mix")
+    src2, dst2 = [o3, zeros(n3)], [zeros(n3 // 4, torch.int32) for _ in range(2)]
+    out["quantize_mix"] = entry(5 * n3, {"tile": timed(
+        [lambda k=k: cl.quantize(src2[k], n3, dst2[k]) for k in range(2)])}, n3)
+    del src2, dst2, o3
+    torch.cuda.empty_cache()
+    log("ceilings: write")
+    dsts = [zeros(n2) for _ in range(8)]
+    out["write"] = entry(4 * n2, {
+        "tile": timed([lambda d=d: cl.write(d, n2, cl.WRITE_TILE) for d in dsts]),
+        "stride": timed([lambda d=d: cl.write(d, n2, cl.WRITE_STRIDE) for d in dsts])}, n2)
+    log("ceilings: compress mix")
+    bw = cl.block_words(n2)
+    sets = [(zeros(n2), zeros(n2), zeros(bw, torch.int32)) for _ in range(6)]
+    out["compress_mix"] = entry(compress_bytes(n2), {"tile": timed(
+        [lambda st=st: cl.compress(st[0], st[1], n2, st[2]) for st in sets])}, n2)
+    del sets
+    log("ceilings: dequantize-sum mix")
+    dsets = [[zeros(bw, torch.int32) for _ in range(W_C2)] for _ in range(8)]
+    out["dequant_mix"] = entry(dequant_sum_bytes(n2, W_C2), {
+        name: timed([lambda k=k, pat=pat: cl.dequant(dsets[k], n2, pat, dsts[k])
+                     for k in range(8)])
+        for name, pat in (("tile", cl.DEQ_TILE), ("wide", cl.DEQ_WIDE), ("burst", cl.DEQ_BURST))},
+        n2)
+    del dsets, dsts
+    torch.cuda.empty_cache()
+    return out
+
+
+def with_ceiling(roof: dict, gbs: float, ceil: dict | None, mix: str) -> dict:
+    """Adds to a roofline object the kernel's rate over its access mix's
+    measured ceiling (frac_of_ceiling) and that ceiling."""
+    if ceil and mix in ceil:
+        roof["ceiling"] = {"mix": mix, "gbs": ceil[mix]["gbs"], "pattern": ceil[mix]["best"]}
+        roof["frac_of_ceiling"] = round(gbs / ceil[mix]["gbs"], 4)
+    return roof
+
+
 def bench_2bit(gcq, torch, np, si, steps: int, warmup: int):
     return bench_threshold_step(gcq, torch, si, steps, warmup, "2-bit",
                                 gcq.gc_compressed_2bit_words, gcq.compress_2bit,
@@ -465,6 +634,23 @@ def bench_threshold_step(gcq, torch, si, steps: int, warmup: int, tag: str, word
     torch.cuda.synchronize()
     comp_ms = [evs[k][0].elapsed_time(evs[k][1]) / W for k in range(steps)]
     deq_ms = [evs[k][1].elapsed_time(evs[k][2]) for k in range(steps)]
+    # the dequantize-sum alone, timed like the ceiling kernels: K back-to-back
+    # launches between two events, rotating over 8 copies of the step's
+    # blocks and 8 outputs (1.2 GB, so the Infinity Cache cannot serve the
+    # reads); one event pair around a single launch adds its own latency
+    sets = [[c.clone() for c in comprs] for _ in range(8)]
+    outs = [torch.empty_like(out) for _ in range(8)]
+    for k in range(8):
+        dequant_sum(sets[k], n, outs[k])
+    torch.cuda.synchronize()
+    d0, d1 = mk(), mk()
+    d0.record()
+    for k in range(steps):
+        dequant_sum(sets[k % 8], n, outs[k % 8])
+    d1.record()
+    torch.cuda.synchronize()
+    deq_b2b_ms = d0.elapsed_time(d1) / steps
+    del sets, outs
     # the same step replayed from a HIP graph (no host launch cost)
     graph = graph_of(torch, step)
     g0, g1 = mk(), mk()
@@ -478,7 +664,7 @@ def bench_threshold_step(gcq, torch, si, steps: int, warmup: int, tag: str, word
     del grads, res, comprs, out
     torch.cuda.empty_cache()
     return {"ms_per_step": ms_step, "wall_s": wall, "compress_ms": comp_ms, "dequant_sum_ms": deq_ms,
-            "graph_ms_per_step": graph_ms}
+            "dequant_sum_b2b_ms": deq_b2b_ms, "graph_ms_per_step": graph_ms}
 
 
 def hbm_alu_roofline(name: str, kernel: str, nbytes: int, launch_s: float) -> dict:
@@ -578,6 +764,11 @@ def bench_qsgd(gcq, torch, np, si, steps: int):
     hbm = {"bound": "hbm", "kernel": "qsgd_global_maxnorm", "achieved": round(mx_gbs, 1),
            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(mx_gbs / HBM_PEAK_GBS, 4),
            "traffic": traffic_from_profile("maxabs_partial_kernel")}
+    ls_gbs = (W + 8) * n / (mean(ds) / 1e3) / 1e9
+    level_sum = {"bound": "hbm", "kernel": "qsgd_dequant_sum (dense level sum + dequantize)",
+                 "achieved": round(ls_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(ls_gbs / HBM_PEAK_GBS, 4),
+                 "traffic": traffic_from_profile("qsgd_dequant_sum_kernel")}
     fused = {
         "workload": "the same step with qsgd_quantize_sum (W quantizes + level sum + dequantize "
                     "in one pass; the int8 levels are not written)",
@@ -602,6 +793,7 @@ def bench_qsgd(gcq, torch, np, si, steps: int):
         "steps": steps,
         "roofline": quant,
         "roofline_maxnorm": hbm,
+        "roofline_level_sum": level_sum,
         "fused": fused,
     }
 
@@ -634,7 +826,7 @@ def bench_ternary(gcq, torch, np, si, steps: int):
     comp_b = 12 * n + 4 * ternary_words(n)
     deq_b = 4 * W * ternary_words(n) + 4 * n
     comp_ms = sum(r["compress_ms"]) / len(r["compress_ms"])
-    deq_ms = sum(r["dequant_sum_ms"]) / len(r["dequant_sum_ms"])
+    deq_ms = r["dequant_sum_b2b_ms"]
     step_b = W * comp_b + deq_b
     comp_gbs = comp_b / (comp_ms / 1e3) / 1e9
     return {"workload": "dense ternary packing (5 codes per byte): compress_ternary x 8 workers "
@@ -646,7 +838,10 @@ def bench_ternary(gcq, torch, np, si, steps: int):
             "compress_ternary": {"avg_ms": comp_ms, "algorithmic_bytes": comp_b,
                                  "gbs": comp_gbs},
             "decompress_ternary_sum": {"avg_ms": deq_ms, "algorithmic_bytes": deq_b,
-                                       "gbs": deq_b / (deq_ms / 1e3) / 1e9},
+                                       "gbs": deq_b / (deq_ms / 1e3) / 1e9,
+                                       "frac": round(deq_b / (deq_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                                       "timing": "back-to-back launches over 8 rotating block sets",
+                                       "in_step_avg_ms": sum(r["dequant_sum_ms"]) / len(r["dequant_sum_ms"])},
             "roofline": {"bound": "hbm", "kernel": "compress_ternary",
                          "achieved": round(comp_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(comp_gbs / HBM_PEAK_GBS, 4),
@@ -725,7 +920,9 @@ def bench_misaligned(gcq, torch, si, steps: int):
     out_buf = torch.empty(nq + 1, dtype=torch.float32, device=dev)
     qsteps = max(2, steps // 4)
     entry = {"workload": f"QSGD-MN, s={s}, W={W} x {nq:,} values; misaligned: gradients, sums "
-                         "and outputs at element offset 1, levels at byte offset 4"}
+                         "and outputs at element offset 1, levels at byte offset 4; "
+                         "levels_at_byte_offsets: worker w's int8 levels at byte offset "
+                         "1 + w % 3, everything else aligned"}
     for off, key in ((1, "misaligned"), (0, "aligned")):
         gv = [g[off:off + nq] for g in qgrads]
         lv = [b[4 * off:4 * off + nq] for b in lv_buf]
@@ -749,6 +946,25 @@ def bench_misaligned(gcq, torch, si, steps: int):
         b.record()
         torch.cuda.synchronize()
         entry[key]["quantize_sum_ms"] = round(a.elapsed_time(b) / qsteps, 5)
+    # int8 levels 1-3 bytes past a 4-byte boundary (worker w at 1 + w % 3),
+    # the gradients and outputs aligned: the quantize and the level sum
+    gv = [g[0:nq] for g in qgrads]
+    lv = [b[1 + w % 3:1 + w % 3 + nq] for w, b in enumerate(lv_buf)]
+    sm, o = sums_buf[0:nq], out_buf[0:nq]
+    gcq.qsgd_global_maxnorm(gv, norm, ws)
+    for w in range(W):
+        gcq.qsgd_maxnorm_quantize(gv[w], norm, s, seed, w, lv[w])
+    entry["levels_at_byte_offsets"] = {
+        "quantize_one_worker_ms": round(per_call(
+            lambda: gcq.qsgd_maxnorm_quantize(gv[1], norm, s, seed, 1, lv[1])), 5),
+        "dequant_sum_ms": round(per_call(lambda: gcq.qsgd_dequant_sum(lv, norm, s, o, sums=sm)), 5),
+    }
+    al = entry["aligned"]
+    entry["levels_at_byte_offsets"]["vs_aligned"] = {
+        "quantize": round(entry["levels_at_byte_offsets"]["quantize_one_worker_ms"]
+                          / al["quantize_one_worker_ms"], 3),
+        "dequant_sum": round(entry["levels_at_byte_offsets"]["dequant_sum_ms"]
+                             / al["dequant_sum_ms"], 3)}
     result["qsgd"] = entry
     del qgrads, lv_buf, sums_buf, out_buf, ws
     torch.cuda.empty_cache()
@@ -1025,6 +1241,12 @@ def main() -> int:
     if args.calibrate_copy:
         calibrate_copy()
         return 0
+    if args.calibrate_ceilings:
+        if not torch.cuda.is_available():
+            print("bench.py: no GPU visible", file=sys.stderr)
+            return 1
+        print(json.dumps({"hbm_ceilings": measure_ceilings(torch, args.ceiling_steps)}), flush=True)
+        return 0
 
     import gradient_compression_quantize_amd as gcq
     import synthetic_inputs as si
@@ -1048,6 +1270,8 @@ def main() -> int:
     comp_ms = sum(r2["compress_ms"]) / len(r2["compress_ms"])
     deq_ms = sum(r2["dequant_sum_ms"]) / len(r2["dequant_sum_ms"])
     comp_gbs = compress_bytes(N_C2) / (comp_ms / 1e3) / 1e9
+    deq_b2b_ms = r2["dequant_sum_b2b_ms"]
+    deq_gbs = dequant_sum_bytes(N_C2, W_C2) / (deq_b2b_ms / 1e3) / 1e9
     traffic = traffic_from_profile("compress_2bit_vec_kernel")
 
     result = {
@@ -1081,12 +1305,16 @@ def main() -> int:
                               "launches": W_C2 * len(r2["compress_ms"]),
                               "timing": "per step, the 8 back-to-back launches between two "
                                         "events, divided by 8"},
-            "decompress_2bit_sum": {"avg_ms": round(deq_ms, 5),
-                                    "median_ms": round(statistics.median(r2["dequant_sum_ms"]), 5),
-                                    "min_ms": round(min(r2["dequant_sum_ms"]), 5),
-                                    "gbs": round(dequant_sum_bytes(N_C2, W_C2) / (deq_ms / 1e3) / 1e9, 1),
+            "decompress_2bit_sum": {"avg_ms": round(deq_b2b_ms, 5),
+                                    "gbs": round(deq_gbs, 1),
+                                    "frac": round(deq_gbs / HBM_PEAK_GBS, 4),
+                                    "timing": f"{args.steps} back-to-back launches between two "
+                                              "events over 8 rotating block sets",
+                                    "in_step_avg_ms": round(deq_ms, 5),
+                                    "in_step_median_ms": round(statistics.median(r2["dequant_sum_ms"]), 5),
+                                    "in_step_timing": "one event pair around the launch in each step",
                                     "algorithmic_bytes": dequant_sum_bytes(N_C2, W_C2),
-                                    "launches": len(r2["dequant_sum_ms"])},
+                                    "launches": len(r2["dequant_sum_ms"]) + args.steps},
         },
         "roofline": {"bound": "hbm", "kernel": "compress_2bit",
                      "achieved": round(comp_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -1103,6 +1331,32 @@ def main() -> int:
         result["grandk_mn"] = bench_grandk(gcq, torch, np, si, args.extra_steps)
         result["ternary"] = bench_ternary(gcq, torch, np, si, args.extra_steps)
         result["misaligned"] = bench_misaligned(gcq, torch, si, args.extra_steps)
+
+    if not args.skip_ceilings:
+        ceil = measure_ceilings(torch, args.ceiling_steps)
+        result["hbm_ceilings"] = ceil
+        with_ceiling(result["roofline"], comp_gbs, ceil, "compress_mix")
+        dk = result["kernels"]["decompress_2bit_sum"]
+        with_ceiling(dk, dk["gbs"], ceil, "dequant_mix")
+        if "qsgd_mn" in result:
+            q = result["qsgd_mn"]
+            with_ceiling(q["roofline"], q["roofline"]["achieved"], ceil, "quantize_mix")
+            with_ceiling(q["roofline_maxnorm"], q["roofline_maxnorm"]["achieved"], ceil, "read")
+            with_ceiling(q["roofline_level_sum"], q["roofline_level_sum"]["achieved"], ceil,
+                         "levelsum_mix")
+        if "multi_tensor" in result:
+            m = result["multi_tensor"]
+            with_ceiling(m["roofline"], m["gbs"], ceil, "compress_mix")
+        if "ternary" in result:
+            t = result["ternary"]
+            with_ceiling(t["roofline"], t["compress_ternary"]["gbs"], ceil, "compress_mix")
+            # the 2-bit dequantize-sum's mix (2 B read : 4 B written per
+            # value) stands in for the ternary one (1.6 B : 4 B)
+            td = t["decompress_ternary_sum"]
+            with_ceiling(td, td["gbs"], ceil, "dequant_mix")
+        if "grandk_mn" in result:
+            g = result["grandk_mn"]
+            with_ceiling(g["roofline"], g["roofline"]["achieved"], ceil, "write")
 
     if not args.skip_cpu_baseline:
         workloads = set()

@@ -314,12 +314,54 @@ __device__ __forceinline__ void load_slots(const float* __restrict__ g, size_t t
     wave_lds_sync();  // these reads precede the next tile's writes
 }
 
+// Stores a full tile's packed level words when the levels sit sh = 1..3
+// bytes past a 4-byte boundary. Slot q's four levels (packed[u] of the lane
+// holding q) start at byte sh of aligned word q (counted from levels - sh),
+// so aligned word q holds the last sh levels of slot q - 1 and the first
+// 4 - sh of slot q: v_alignbyte of the two packed words, the previous slot's
+// coming from the lane before (lane 63 of the previous u for lane 0). Inside
+// the tile every such word is stored whole; the tile's first aligned word
+// and the word after its last (shared with the neighbouring tiles) get only
+// this tile's bytes, as byte stores.
+template <int U>
+__device__ __forceinline__ void store_levels_shifted(int8_t* __restrict__ levels, uint32_t sh,
+                                                     size_t q0, int lane, const uint32_t (&packed)[U])
+{
+    uint32_t* a = reinterpret_cast<uint32_t*>(levels - sh);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        uint32_t prev = static_cast<uint32_t>(__shfl_up(static_cast<int>(packed[u]), 1));
+        if (u > 0) {
+            const uint32_t last = __builtin_amdgcn_readlane(packed[u - 1], kWave - 1);
+            if (lane == 0)
+                prev = last;
+        }
+        const uint32_t word = __builtin_amdgcn_alignbyte(packed[u], prev, 4u - sh);
+        if (u > 0 || lane > 0)
+            __builtin_nontemporal_store(word, a + q0 + size_t(u) * kWave);
+    }
+    if (lane == 0) {
+        // the first 4 - sh levels of the tile's first slot
+        for (uint32_t k = 0; k < 4u - sh; ++k)
+            levels[q0 * 4 + k] = int8_t(packed[0] >> (8 * k));
+    }
+    if (lane == kWave - 1) {
+        // the last sh levels of the tile's last slot
+        const size_t ql = q0 + size_t(U - 1) * kWave;
+        for (uint32_t k = 4u - sh; k < 4u; ++k)
+            levels[ql * 4 + k] = int8_t(packed[U - 1] >> (8 * k));
+    }
+}
+
 // kDword: grad 4- but not 16-byte aligned (loads through load_slots).
-template <bool kLoop, bool kDword>
+// kLvShift: levels 1-3 bytes past a 4-byte boundary (lv_shift bytes); full
+// tiles store words through store_levels_shifted.
+template <bool kLoop, bool kDword, bool kLvShift>
 __device__ __forceinline__ void qsgd_quantize_body(const float* __restrict__ grad, size_t n,
                                                    const float* __restrict__ norm_ptr, float s24,
                                                    uint32_t k0, uint32_t k1, uint32_t worker,
-                                                   int8_t* __restrict__ levels, int vec)
+                                                   int8_t* __restrict__ levels, int vec,
+                                                   uint32_t lv_shift)
 {
     __shared__ float stage[kDword ? kThreads / kWave : 1][kDword ? 4 * kQTile : 1];
     const bool gvec = vec && !kDword;  // grad itself 16-byte aligned
@@ -353,10 +395,14 @@ __device__ __forceinline__ void qsgd_quantize_body(const float* __restrict__ gra
                     packed[u] = pack_levels4(t);
                 }
             }
+            if (kLvShift) {
+                store_levels_shifted<kQUnroll>(levels, lv_shift, q0, lane, packed);
+            } else {
 #pragma unroll
-            for (int u = 0; u < kQUnroll; ++u)
-                __builtin_nontemporal_store(packed[u], reinterpret_cast<uint32_t*>(levels) + q0 +
-                                                           size_t(u) * kWave);
+                for (int u = 0; u < kQUnroll; ++u)
+                    __builtin_nontemporal_store(packed[u], reinterpret_cast<uint32_t*>(levels) +
+                                                               q0 + size_t(u) * kWave);
+            }
         } else {
             // the partial tile, or levels without 4-byte alignment. Whole
             // float4 slots are still one load (16-byte-aligned gradient)
@@ -382,7 +428,8 @@ __device__ __forceinline__ void qsgd_quantize_body(const float* __restrict__ gra
                 const size_t q = q0 + size_t(u) * kWave;
                 if (q >= nslots)
                     continue;
-                const bool whole = vec && q < nfull;  // the slot's levels as one word
+                // the slot's levels as one word (levels 4-byte aligned)
+                const bool whole = !kLvShift && vec && q < nfull;
                 if (!(gvec && q < nfull)) {
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
@@ -411,13 +458,15 @@ __device__ __forceinline__ void qsgd_quantize_body(const float* __restrict__ gra
 }
 
 // Entry kernels of the body above, named apart so that profiles keep the
-// aligned and the 4-byte-aligned gradients separate.
+// aligned and the 4-byte-aligned gradients, and levels at byte offsets,
+// separate.
 template <bool kLoop>
 __global__ __launch_bounds__(kThreads) void qsgd_quantize_kernel(
     const float* __restrict__ grad, size_t n, const float* __restrict__ norm_ptr, float s24,
     uint32_t k0, uint32_t k1, uint32_t worker, int8_t* __restrict__ levels, int vec)
 {
-    qsgd_quantize_body<kLoop, false>(grad, n, norm_ptr, s24, k0, k1, worker, levels, vec);
+    qsgd_quantize_body<kLoop, false, false>(grad, n, norm_ptr, s24, k0, k1, worker, levels, vec,
+                                            0u);
 }
 
 template <bool kLoop>
@@ -425,7 +474,19 @@ __global__ __launch_bounds__(kThreads) void qsgd_quantize_dword_kernel(
     const float* __restrict__ grad, size_t n, const float* __restrict__ norm_ptr, float s24,
     uint32_t k0, uint32_t k1, uint32_t worker, int8_t* __restrict__ levels, int vec)
 {
-    qsgd_quantize_body<kLoop, true>(grad, n, norm_ptr, s24, k0, k1, worker, levels, vec);
+    qsgd_quantize_body<kLoop, true, false>(grad, n, norm_ptr, s24, k0, k1, worker, levels, vec,
+                                           0u);
+}
+
+// Levels 1-3 bytes past a 4-byte boundary (lv_shift); kDword: the gradient
+// 4- but not 16-byte aligned.
+template <bool kLoop, bool kDword>
+__global__ __launch_bounds__(kThreads) void qsgd_quantize_bytes_kernel(
+    const float* __restrict__ grad, size_t n, const float* __restrict__ norm_ptr, float s24,
+    uint32_t k0, uint32_t k1, uint32_t worker, int8_t* __restrict__ levels, uint32_t lv_shift)
+{
+    qsgd_quantize_body<kLoop, kDword, true>(grad, n, norm_ptr, s24, k0, k1, worker, levels, 1,
+                                            lv_shift);
 }
 
 // ---- level sum + dequantize ------------------------------------------------
@@ -459,11 +520,53 @@ __device__ __forceinline__ void dequant_store(float norm, float s_f, i32x4 S, in
     __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(out) + q);
 }
 
-// kDword: sums and out 4- but not 16-byte aligned (levels 4-byte aligned):
-// a full tile's sums and values pass through the wave's LDS stage and leave
-// as lane-contiguous 4-byte stores.
-template <int WC, bool kDword>
-__device__ __forceinline__ void qsgd_dequant_sum_body(const PtrTable<int8_t>& tab, int W_rt,
+// Byte offset (0..3) of each worker's levels past the 4-byte-aligned address
+// the kernel is given for them, two bits per worker.
+struct LevelShifts {
+    uint32_t s[GC_MAX_WORKERS / 16];
+};
+
+__device__ __forceinline__ uint32_t level_shift(const LevelShifts& ls, int w)
+{
+    return (ls.s[w >> 4] >> (2 * (w & 15))) & 3u;
+}
+
+// Levels of worker w at byte offset sh (1..3) past the aligned word array a:
+// the four int8 levels of slot q are bytes sh .. sh+3 of the word pair
+// (a[q], a[q+1]), i.e. v_alignbyte of the two. words[u] holds a[q + 64 u]
+// for this lane's slots q; a[q + 1 + 64 u] is the next lane's word, lane 0's
+// word of the next u for lane 63, and for lane 63 at the last u one more
+// load. That word holds the tile's last level bytes, so it lies inside the
+// buffer (a word holding at least one of its bytes).
+template <int U>
+__device__ __forceinline__ void align_level_words(const uint32_t* __restrict__ a, size_t q,
+                                                  uint32_t sh, int lane, uint32_t (&words)[U])
+{
+    uint32_t hi[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        hi[u] = static_cast<uint32_t>(__shfl_down(static_cast<int>(words[u]), 1));
+#pragma unroll
+    for (int u = 0; u + 1 < U; ++u) {
+        const uint32_t next0 = __builtin_amdgcn_readfirstlane(words[u + 1]);
+        if (lane == kWave - 1)
+            hi[u] = next0;
+    }
+    if (lane == kWave - 1)
+        hi[U - 1] = a[q + size_t(U - 1) * kWave + 1];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        words[u] = __builtin_amdgcn_alignbyte(hi[u], words[u], sh);
+}
+
+// kDword: sums and out 4- but not 16-byte aligned: a full tile's sums and
+// values pass through the wave's LDS stage and leave as lane-contiguous
+// 4-byte stores. kLvAny: tab holds each worker's levels rounded down to 4-byte
+// alignment, `shifts` the byte offsets past them; full tiles still load
+// words (align_level_words), and the partial tile reads bytes at the offset.
+template <int WC, bool kDword, bool kLvAny>
+__device__ __forceinline__ void qsgd_dequant_sum_body(const PtrTable<int8_t>& tab,
+                                                      const LevelShifts& shifts, int W_rt,
                                                       size_t n, const float* __restrict__ norm_ptr,
                                                       float s_f, int32_t* __restrict__ sums,
                                                       float* __restrict__ out, int vec)
@@ -497,6 +600,18 @@ __device__ __forceinline__ void qsgd_dequant_sum_body(const PtrTable<int8_t>& ta
                                            : __builtin_nontemporal_load(
                                                  reinterpret_cast<const uint32_t*>(tab.p[w0 + dw]) +
                                                  q0 + size_t(u) * kWave);
+                if (kLvAny) {
+#pragma unroll
+                    for (int dw = 0; dw < kGroup; ++dw) {
+                        if (WC == 0 && w0 + dw >= W)
+                            break;
+                        const uint32_t sh = level_shift(shifts, w0 + dw);  // uniform
+                        if (sh)
+                            align_level_words<kDqUnroll>(
+                                reinterpret_cast<const uint32_t*>(tab.p[w0 + dw]), q0, sh, lane,
+                                words[dw]);
+                    }
+                }
 #pragma unroll
                 for (int dw = 0; dw < kGroup; ++dw)
 #pragma unroll
@@ -543,7 +658,7 @@ __device__ __forceinline__ void qsgd_dequant_sum_body(const PtrTable<int8_t>& ta
                     int S = 0;
 #pragma unroll 1
                     for (int w = 0; w < W; ++w)
-                        S += int(tab.p[w][i]);
+                        S += int(tab.p[w][i + (kLvAny ? level_shift(shifts, w) : 0u)]);
                     if (sums)
                         sums[i] = S;
                     out[i] = dequant(norm, S, s_f);
@@ -554,13 +669,15 @@ __device__ __forceinline__ void qsgd_dequant_sum_body(const PtrTable<int8_t>& ta
 }
 
 // Entry kernels of the body above, named apart so that profiles keep the
-// aligned and the 4-byte-aligned outputs separate.
+// aligned and the 4-byte-aligned outputs, and the levels at byte offsets,
+// separate.
 template <int WC>
 __global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_kernel(
     PtrTable<int8_t> tab, int W, size_t n, const float* __restrict__ norm_ptr, float s_f,
     int32_t* __restrict__ sums, float* __restrict__ out, int vec)
 {
-    qsgd_dequant_sum_body<WC, false>(tab, W, n, norm_ptr, s_f, sums, out, vec);
+    qsgd_dequant_sum_body<WC, false, false>(tab, LevelShifts{}, W, n, norm_ptr, s_f, sums, out,
+                                            vec);
 }
 
 template <int WC>
@@ -568,7 +685,17 @@ __global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_dword_kernel(
     PtrTable<int8_t> tab, int W, size_t n, const float* __restrict__ norm_ptr, float s_f,
     int32_t* __restrict__ sums, float* __restrict__ out, int vec)
 {
-    qsgd_dequant_sum_body<WC, true>(tab, W, n, norm_ptr, s_f, sums, out, vec);
+    qsgd_dequant_sum_body<WC, true, false>(tab, LevelShifts{}, W, n, norm_ptr, s_f, sums, out,
+                                           vec);
+}
+
+// Levels of some worker 1-3 bytes off 4-byte alignment; kDword as above.
+template <int WC, bool kDword>
+__global__ __launch_bounds__(kThreads) void qsgd_dequant_sum_bytes_kernel(
+    PtrTable<int8_t> tab, LevelShifts shifts, int W, size_t n, const float* __restrict__ norm_ptr,
+    float s_f, int32_t* __restrict__ sums, float* __restrict__ out)
+{
+    qsgd_dequant_sum_body<WC, kDword, true>(tab, shifts, W, n, norm_ptr, s_f, sums, out, 1);
 }
 
 // ---- fused quantize + level sum + dequantize --------------------------------
@@ -1240,19 +1367,38 @@ GCQ_API int qsgd_maxnorm_quantize(const float* grad, size_t n, const float* norm
         return fail(GC_EINVAL, "qsgd_maxnorm_quantize: grad must be 4-byte aligned");
     if (n == 0)
         return GC_OK;
-    // vec: whole slots of levels as words (levels 4-byte aligned); the
-    // gradient's loads are float4 when it is 16-byte aligned, else staged
-    const int vec = aligned4(levels) ? 1 : 0;
-    const bool dword = vec && !aligned16(grad);
     const size_t ntiles = ceil_div(ceil_div(n, 4), kQTile);
     const size_t want = ceil_div(ntiles, kThreads / kWave);
     const dim3 grid(std::min(want, max_grid_blocks())), block(kThreads);
     const float s24 = float(s) * 16777216.0f;  // exact: s <= 127
-    const int vec_kernel = (vec && aligned16(grad)) ? 1 : 0;
+    const bool loop = want > max_grid_blocks();
+    if (!aligned4(levels)) {
+        // levels 1-3 bytes past a 4-byte boundary: full tiles still store
+        // words (realigned in registers), the gradient float4 or staged
+        const uint32_t sh = uint32_t(reinterpret_cast<uintptr_t>(levels) & 3u);
+        const bool g16 = aligned16(grad);
+#define GCQ_QB_LAUNCH(L, D)                                                                     \
+    hipLaunchKernelGGL((qsgd_quantize_bytes_kernel<L, D>), grid, block, 0, stream, grad, n, norm, \
+                       s24, uint32_t(seed), uint32_t(seed >> 32), worker, levels, sh)
+        if (loop && g16)
+            GCQ_QB_LAUNCH(true, false);
+        else if (loop)
+            GCQ_QB_LAUNCH(true, true);
+        else if (g16)
+            GCQ_QB_LAUNCH(false, false);
+        else
+            GCQ_QB_LAUNCH(false, true);
+#undef GCQ_QB_LAUNCH
+        return check_launch("qsgd_maxnorm_quantize");
+    }
+    // levels 4-byte aligned: whole slots of levels as words; the gradient's
+    // loads are float4 when it is 16-byte aligned, else staged
+    const int vec = 1;
+    const bool dword = !aligned16(grad);
+    const int vec_kernel = aligned16(grad) ? 1 : 0;
 #define GCQ_Q_LAUNCH(K, L, V)                                                                 \
     hipLaunchKernelGGL((K<L>), grid, block, 0, stream, grad, n, norm, s24, uint32_t(seed),   \
                        uint32_t(seed >> 32), worker, levels, V)
-    const bool loop = want > max_grid_blocks();
     if (dword && loop)
         GCQ_Q_LAUNCH(qsgd_quantize_dword_kernel, true, vec);
     else if (dword)
@@ -1296,6 +1442,36 @@ GCQ_API int qsgd_dequant_sum(const int8_t* const* levels, int W, size_t n, const
         if (n == 0)
             return GC_OK;
         const bool out_aligned = aligned16(out) && (!sums || aligned16(sums));
+        if (!lv_aligned) {
+            // levels 1-3 bytes off 4-byte alignment: word loads from each
+            // worker's levels rounded down to 4 bytes, realigned in registers
+            PtrTable<int8_t> base{};
+            LevelShifts sh{};
+            for (int w = 0; w < W; ++w) {
+                const uint32_t b = uint32_t(reinterpret_cast<uintptr_t>(levels[w]) & 3u);
+                base.p[w] = levels[w] - b;
+                sh.s[w >> 4] |= b << (2 * (w & 15));
+            }
+            const size_t ntiles = ceil_div(ceil_div(n, 4), kDqTile);
+            const dim3 grid(std::max<size_t>(1, std::min(ceil_div(ntiles, kThreads / kWave),
+                                                         max_grid_blocks()))),
+                block(kThreads);
+#define GCQ_DQB_LAUNCH(k)                                                                      \
+    do {                                                                                       \
+        if (out_aligned)                                                                       \
+            hipLaunchKernelGGL((qsgd_dequant_sum_bytes_kernel<k, false>), grid, block, 0,      \
+                               stream, base, sh, W, n, norm, s_f, sums, out);                  \
+        else                                                                                   \
+            hipLaunchKernelGGL((qsgd_dequant_sum_bytes_kernel<k, true>), grid, block, 0,       \
+                               stream, base, sh, W, n, norm, s_f, sums, out);                  \
+    } while (0)
+            if (W == 8)
+                GCQ_DQB_LAUNCH(8);
+            else
+                GCQ_DQB_LAUNCH(0);
+#undef GCQ_DQB_LAUNCH
+            return check_launch("qsgd_dequant_sum");
+        }
         // levels 4-byte aligned: word loads; outputs staged when not 16-byte aligned
         const bool dword = lv_aligned && !out_aligned;
         const int vec = lv_aligned ? 1 : 0;

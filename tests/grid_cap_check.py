@@ -164,6 +164,28 @@ def main():
     d_or = oracle.qsgd_dequantize(s_or, norm_or, s)
     check(np.array_equal(gu.host(out_m), d_or) and np.array_equal(gu.host(fout_m), d_or),
           "qsgd misaligned dequantized")
+    # int8 levels 1-3 bytes past a 4-byte boundary (a different offset per
+    # worker), gradients aligned and 4 bytes off: the word paths that
+    # realign levels in registers, striding over many tiles
+    for gmis in (False, True):
+        print(f"[case] capped qsgd, levels at byte offsets, misaligned gradients={gmis}",
+              flush=True)
+        gb_dev = [gu.dev(g, gmis) for g in gs]
+        bufs = [torch.full((n + 8,), 99, dtype=torch.int8, device=gu.DEV) for _ in range(W)]
+        lvb = [bufs[w][1 + w % 3:1 + w % 3 + n] for w in range(W)]
+        for w in range(W):
+            gcq.qsgd_maxnorm_quantize(gb_dev[w], norm, s, seed, w, lvb[w])
+        sums_b = gu.empty(n, torch.int32, fill=-7)
+        out_b = gu.empty(n, torch.float32, fill=float("nan"))
+        gcq.qsgd_dequant_sum(lvb, norm, s, out_b, sums=sums_b)
+        gu.sync()
+        for w in range(W):
+            check(np.array_equal(gu.host(lvb[w]), lv_or[w]), f"qsgd byte-offset levels worker {w}")
+            hb = gu.host(bufs[w])
+            check(np.all(hb[:1 + w % 3] == 99) and np.all(hb[1 + w % 3 + n:] == 99),
+                  f"qsgd byte-offset levels: bytes outside the view, worker {w}")
+        check(np.array_equal(gu.host(sums_b), s_or), "qsgd byte-offset level sums")
+        check(np.array_equal(gu.host(out_b), d_or), "qsgd byte-offset dequantized")
     idx = oracle.randk_indices(n, 5000, 3)
     gk = gu.empty(5000, torch.float32)
     gcq.gather_f32(g_dev[0], gu.dev(idx), gk)

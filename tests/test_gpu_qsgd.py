@@ -54,8 +54,9 @@ def check_deq(got, expect):
 
 @pytest.mark.parametrize("byte_off", [1, 2, 3])
 def test_levels_at_odd_byte_offsets(gcq, byte_off):
-    """int8 levels 1-3 bytes off 4-byte alignment take the element-by-element
-    quantize and level sum; gradients at a 4-byte offset, outputs aligned."""
+    """int8 levels 1-3 bytes off 4-byte alignment (the word paths that
+    realign them in registers); gradients at a 4-byte offset, outputs
+    aligned."""
     n, W, s, seed = 70_001, 3, 127, 19
     announce(f"qsgd levels at byte offset {byte_off}")
     grads = [si.heavy_tailed_f32(si.grad_seed(w, 13), n, 0.02) for w in range(W)]
@@ -83,6 +84,88 @@ def test_levels_at_odd_byte_offsets(gcq, byte_off):
     S = oracle.level_sum(lv_or)
     np.testing.assert_array_equal(gu.host(sums), S)
     check_deq(gu.host(out), oracle.qsgd_dequantize(S, norm_or, s))
+
+
+@pytest.mark.parametrize("gmis", [False, True])
+@pytest.mark.parametrize("W,n", [(8, 70_001), (5, 300_007), (8, 1024 * 256 * 3 + 257),
+                                 (2, 1031), (13, 9_999)])
+def test_levels_at_mixed_byte_offsets(gcq, W, n, gmis):
+    """Each worker's int8 levels at its own offset 0-3 past a 4-byte boundary
+    (the word paths that realign levels in registers; W = 8 known at compile
+    time, other W read at run time), gradients aligned or 4 bytes off, sizes
+    over several tiles with a ragged tail: levels, sums and values against
+    the oracle, and no byte written outside any view."""
+    seed = 0xB17E5 + n + W
+    announce(f"qsgd levels at mixed byte offsets W={W} n={n} gmis={gmis}")
+    grads = [si.heavy_tailed_f32(si.grad_seed(w, 14), n, 0.02) for w in range(W)]
+    g_dev = [gu.dev(g, gmis) for g in grads]
+    norm = torch.empty(1, dtype=torch.float32, device=gu.DEV)
+    ws = torch.empty(gcq.qsgd_maxnorm_ws_bytes(W, n), dtype=torch.uint8, device=gu.DEV)
+    gcq.qsgd_global_maxnorm(g_dev, norm, ws)
+    offs = [(3 * w + 1) % 4 for w in range(W)]
+    bufs = [torch.full((n + 8,), 99, dtype=torch.int8, device=gu.DEV) for _ in range(W)]
+    levels = [bufs[w][offs[w]:offs[w] + n] for w in range(W)]
+    for w in range(W):
+        gcq.qsgd_maxnorm_quantize(g_dev[w], norm, 127, seed, w, levels[w])
+    sums = gu.empty(n, torch.int32, fill=-7)
+    out = gu.empty(n, torch.float32, fill=float("nan"))
+    gcq.qsgd_dequant_sum(levels, norm, 127, out, sums=sums)
+    gu.sync()
+    norm_or = oracle.maxnorm(grads)
+    assert np.float32(gu.host(norm)[0]) == norm_or
+    lv_or = [oracle.qsgd_quantize(g, norm_or, 127, seed, w) for w, g in enumerate(grads)]
+    for w in range(W):
+        np.testing.assert_array_equal(gu.host(levels[w]), lv_or[w], err_msg=f"worker {w}")
+        hb = gu.host(bufs[w])
+        assert np.all(hb[:offs[w]] == 99) and np.all(hb[offs[w] + n:] == 99), f"worker {w}"
+    S = oracle.level_sum(lv_or)
+    np.testing.assert_array_equal(gu.host(sums), S)
+    check_deq(gu.host(out), oracle.qsgd_dequantize(S, norm_or, 127))
+    # the level sum alone on arbitrary int8 bytes at those offsets, the
+    # outputs 4 bytes off 16-byte alignment (staged stores)
+    rng = np.random.default_rng(n + W)
+    anyq = [rng.integers(-128, 128, n, dtype=np.int64).astype(np.int8) for _ in range(W)]
+    for w in range(W):
+        levels[w].copy_(torch.from_numpy(anyq[w]))
+    sums_m = gu.empty(n, torch.int32, misalign=True, fill=-7)
+    out_m = gu.empty(n, torch.float32, misalign=True, fill=float("nan"))
+    gcq.qsgd_dequant_sum(levels, norm, 127, out_m, sums=sums_m)
+    gu.sync()
+    S_any = oracle.level_sum(anyq)
+    np.testing.assert_array_equal(gu.host(sums_m), S_any)
+    check_deq(gu.host(out_m), oracle.qsgd_dequantize(S_any, norm_or, 127))
+
+
+@pytest.mark.slow
+def test_levels_at_byte_offsets_vgg16_full_size(gcq):
+    """The VGG16-sized step with worker w's levels at byte offset 1 + w % 3:
+    every level, sum and value against the oracle's run over all elements."""
+    import vgg16_case as vc
+    announce("qsgd full size, levels at byte offsets: generating inputs")
+    grads = vc.grads()
+    g_dev = [gu.dev(g) for g in grads]
+    norm = torch.empty(1, dtype=torch.float32, device=gu.DEV)
+    ws = torch.empty(gcq.qsgd_maxnorm_ws_bytes(vc.W, vc.N), dtype=torch.uint8, device=gu.DEV)
+    announce("qsgd full size, levels at byte offsets: device step")
+    gcq.qsgd_global_maxnorm(g_dev, norm, ws)
+    bufs = [torch.empty(vc.N + 4, dtype=torch.int8, device=gu.DEV) for _ in range(vc.W)]
+    levels = [bufs[w][1 + w % 3:1 + w % 3 + vc.N] for w in range(vc.W)]
+    for w in range(vc.W):
+        gcq.qsgd_maxnorm_quantize(g_dev[w], norm, vc.S, vc.SEED, w, levels[w])
+    del g_dev
+    sums = gu.empty(vc.N, torch.int32, fill=-7)
+    out = gu.empty(vc.N, torch.float32, fill=float("nan"))
+    gcq.qsgd_dequant_sum(levels, norm, vc.S, out, sums=sums)
+    gu.sync()
+    announce("qsgd full size, levels at byte offsets: oracle over every element")
+    norm_or, lv_or, s_or, d_or = vc.oracle_step()
+    assert np.float32(gu.host(norm)[0]) == norm_or
+    for w in range(vc.W):
+        np.testing.assert_array_equal(gu.host(levels[w]), lv_or[w], err_msg=f"worker {w}")
+    np.testing.assert_array_equal(gu.host(sums), s_or)
+    check_deq(gu.host(out), d_or)
+    del bufs, levels, sums, out
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("misalign", [False, True])
