@@ -235,6 +235,7 @@ def ceiling_kernel_bytes() -> dict:
     uses (the workloads rounded down to whole 16384-value quanta)."""
     Q = 16384
     n2, n3 = N_C2 // Q * Q, N_C3 // Q * Q
+    nt = N_C2 // 81920 * 81920
     return {
         "ceil_read_chunked_kernel": (4 * W_C3 * n3, "read, chunked (8 buffers per launch)"),
         "ceil_read_tile_kernel": (4 * n3, "read, one tile per wave (1 buffer per launch)"),
@@ -246,6 +247,8 @@ def ceiling_kernel_bytes() -> dict:
         "ceil_dequant_tile_kernel": (dequant_sum_bytes(n2, W_C2), "dequantize-sum mix, the kernel's pattern"),
         "ceil_dequant_wide_kernel": (dequant_sum_bytes(n2, W_C2), "dequantize-sum mix, wide reads"),
         "ceil_dequant_burst_kernel": (dequant_sum_bytes(n2, W_C2), "dequantize-sum mix, workgroup bursts"),
+        "ceil_dequant_ternary_kernel": (4 * W_C2 * (3 + nt // 20) + 4 * nt,
+                                        "ternary dequantize-sum mix (at n = %d)" % nt),
     }
 
 
@@ -560,7 +563,13 @@ def measure_ceilings(torch, steps: int) -> dict:
                      for k in range(8)])
         for name, pat in (("tile", cl.DEQ_TILE), ("wide", cl.DEQ_WIDE), ("burst", cl.DEQ_BURST))},
         n2)
-    del dsets, dsts
+    log("ceilings: ternary dequantize-sum mix")
+    nt = N_C2 // cl.ternary_quantum() * cl.ternary_quantum()
+    tsets = [[zeros(3 + nt // 20, torch.int32) for _ in range(W_C2)] for _ in range(8)]
+    out["dequant_ternary_mix"] = entry(4 * W_C2 * (3 + nt // 20) + 4 * nt, {
+        "tile": timed([lambda k=k: cl.dequant_ternary(tsets[k], nt, dsts[k]) for k in range(8)])},
+        nt)
+    del dsets, dsts, tsets
     torch.cuda.empty_cache()
     return out
 
@@ -1350,10 +1359,8 @@ def main() -> int:
         if "ternary" in result:
             t = result["ternary"]
             with_ceiling(t["roofline"], t["compress_ternary"]["gbs"], ceil, "compress_mix")
-            # the 2-bit dequantize-sum's mix (2 B read : 4 B written per
-            # value) stands in for the ternary one (1.6 B : 4 B)
             td = t["decompress_ternary_sum"]
-            with_ceiling(td, td["gbs"], ceil, "dequant_mix")
+            with_ceiling(td, td["gbs"], ceil, "dequant_ternary_mix")
         if "grandk_mn" in result:
             g = result["grandk_mn"]
             with_ceiling(g["roofline"], g["roofline"]["achieved"], ceil, "write")

@@ -41,9 +41,12 @@ def load() -> ctypes.CDLL:
         L.gcq_ceiling_compress.argtypes = [_vp, _vp, _sz, _vp, _sz, _vp]
         L.gcq_ceiling_dequant.argtypes = [ctypes.POINTER(_vp), _i, _sz, _sz, _i, _vp, _vp]
         L.gcq_ceiling_quantize.argtypes = [_vp, _sz, _vp, _vp]
+        L.gcq_ceiling_ternary_quantum.restype = _sz
+        L.gcq_ceiling_dequant_ternary.argtypes = [ctypes.POINTER(_vp), _i, _sz, _sz, _vp, _vp]
         L.gcq_ceiling_levelsum.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _vp, _vp]
         for f in ("gcq_ceiling_read", "gcq_ceiling_write", "gcq_ceiling_compress",
-                  "gcq_ceiling_dequant", "gcq_ceiling_quantize", "gcq_ceiling_levelsum"):
+                  "gcq_ceiling_dequant", "gcq_ceiling_dequant_ternary", "gcq_ceiling_quantize",
+                  "gcq_ceiling_levelsum"):
             getattr(L, f).restype = _i
         _lib = L
     return _lib
@@ -116,6 +119,17 @@ def dequant(blocks: Sequence, n: int, pattern: int, out, stream=None) -> None:
     cap = min(b.numel() for b in blocks)
     _check(load().gcq_ceiling_dequant(_arr(blocks), len(blocks), n, cap, pattern, _p(out),
                                       _stream(stream)))
+
+
+def ternary_quantum() -> int:
+    return int(load().gcq_ceiling_ternary_quantum())
+
+
+def dequant_ternary(blocks: Sequence, n: int, out, stream=None) -> None:
+    _need(out, n, "out")
+    cap = min(b.numel() for b in blocks)
+    _check(load().gcq_ceiling_dequant_ternary(_arr(blocks), len(blocks), n, cap, _p(out),
+                                              _stream(stream)))
 
 
 def quantize(src, n: int, dst, stream=None) -> None:

@@ -18,6 +18,8 @@
 //             wave, one 512 B load per block) and workgroup bursts (a
 //             1024-thread workgroup stages 16 tiles' words of every block in
 //             LDS with 16-byte loads, then writes 64 KB)
+//   ternary   the same for the ternary dequantize-sum: one 4-byte element per
+//             20 values from each of W blocks, 4 B written per value
 //   quantize  4 B read + 1 B written per value
 //   levelsum  W B read + 8 B written per value (an int32 sum and an fp32)
 // A hot-path kernel's rate over its mix's rate here is how close it runs to
@@ -274,6 +276,31 @@ __global__ __launch_bounds__(kBurstThreads) void ceil_dequant_burst_kernel(Ptrs<
         __builtin_nontemporal_store(spread(x, u), o + u * kWave);
 }
 
+// The ternary dequantize-sum's pattern: a wave tile is 64 elements (1280
+// values); lane L loads element L of the tile from each block (256 B per
+// load, 12 bytes into the block), then writes the tile's 5 KB as 5
+// lane-contiguous float4 stores.
+constexpr size_t kTernTileVals = 1280;
+
+__global__ __launch_bounds__(kThreads) void ceil_dequant_ternary_kernel(Ptrs<uint32_t> blk,
+                                                                        float* __restrict__ out)
+{
+    const size_t tile = size_t(blockIdx.x) * kWaves + threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t w[kDeqW];
+#pragma unroll
+    for (int k = 0; k < kDeqW; ++k)
+        w[k] = __builtin_nontemporal_load(blk.p[k] + 3 + tile * kWave + lane);
+    uint32_t x = 0;
+#pragma unroll
+    for (int k = 0; k < kDeqW; ++k)
+        x ^= w[k];
+    f32x4* o = reinterpret_cast<f32x4*>(out) + tile * (kTernTileVals / 4) + lane;
+#pragma unroll
+    for (int u = 0; u < 5; ++u)
+        __builtin_nontemporal_store(spread(x, u & 3), o + u * kWave);
+}
+
 // ---- the quantize mix --------------------------------------------------------
 
 // Per wave tile: 4 float4 read per lane, one 4-byte word per float4 written
@@ -333,6 +360,27 @@ GCQ_CEIL_API const char* gcq_ceiling_last_error(void) { return g_err.c_str(); }
 GCQ_CEIL_API size_t gcq_ceiling_quantum(void) { return kQuantum; }
 
 GCQ_CEIL_API size_t gcq_ceiling_block_words(size_t n) { return 3 + n / 16 + 4; }
+
+GCQ_CEIL_API size_t gcq_ceiling_ternary_quantum(void) { return 81920; }
+
+GCQ_CEIL_API int gcq_ceiling_dequant_ternary(const uint32_t* const* blocks, int W, size_t n,
+                                             size_t block_cap_words, float* out,
+                                             hipStream_t stream)
+{
+    // whole workgroups of 4 tiles of 1280 values; n / 20 elements per block
+    if (n == 0 || n % gcq_ceiling_ternary_quantum() || W != kDeqW || !blocks || !aligned16(out) ||
+        block_cap_words < 3 + n / 20)
+        return fail("gcq_ceiling_dequant_ternary: bad arguments (W must be 8)");
+    Ptrs<uint32_t> tab{};
+    for (int k = 0; k < W; ++k) {
+        if (!aligned16(blocks[k]))
+            return fail("gcq_ceiling_dequant_ternary: blocks must be 16-byte aligned");
+        tab.p[k] = blocks[k];
+    }
+    hipLaunchKernelGGL(ceil_dequant_ternary_kernel, dim3(unsigned(n / kTernTileVals / kWaves)),
+                       dim3(kThreads), 0, stream, tab, out);
+    return launched("gcq_ceiling_dequant_ternary");
+}
 
 GCQ_CEIL_API size_t gcq_ceiling_read_sink_words(int nbufs, size_t n)
 {

@@ -324,10 +324,13 @@ __device__ __forceinline__ void decode_element(uint32_t word, const float2* t,
 // run time, in groups of four. `stage` is this wave's kTileF4-float4 buffer.
 // kDword: out without 16-byte alignment; the staged tile leaves as
 // lane-contiguous 4-byte stores.
+// pre: this lane's W elements, already loaded (WC > 0), or NULL to load them
+// here.
 template <int WC, bool kAcc, bool kDword>
 __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& tab, int W_rt,
                                                      const float2* lut, float* __restrict__ out,
-                                                     size_t q0, int lane, f32x4* stage)
+                                                     size_t q0, int lane, f32x4* stage,
+                                                     const uint32_t* pre = nullptr)
 {
     const int W = WC > 0 ? WC : W_rt;
     const size_t j = q0 / kSlots + lane;
@@ -339,7 +342,8 @@ __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& t
         for (int dw = 0; dw < kGroup; ++dw) {
             mine[dw] = (WC == 0 && w0 + dw >= W)
                            ? 0u
-                           : __builtin_nontemporal_load(tab.p[w0 + dw] + 3 + j);
+                           : (pre ? pre[w0 + dw]
+                                  : __builtin_nontemporal_load(tab.p[w0 + dw] + 3 + j));
         }
 #pragma unroll
         for (int dw = 0; dw < kGroup; ++dw) {
@@ -416,9 +420,28 @@ __device__ __forceinline__ void decompress_ternary_body(const PtrTable<uint32_t>
 {
     __shared__ float2 lut[16 * (WC > 0 ? WC : GC_MAX_WORKERS)];
     __shared__ f32x4 stage[kWavesPerBlock][kTileF4];
-    build_pair_table(lut, tab, WC > 0 ? WC : W);
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    if (!kLoop && WC > 0) {
+        // One tile per wave, W known: the tile's element loads go out before
+        // the table is built, as in the 2-bit kernel.
+        const size_t t = xcd_contiguous(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+        const size_t q0 = t < ntiles ? (ntiles - 1 - t) * kTileF4 : 0;
+        const bool full = t < ntiles && q0 + kTileF4 <= (n >> 2);
+        uint32_t pre[WC > 0 ? WC : 1];
+        if (full) {
+#pragma unroll
+            for (int w = 0; w < (WC > 0 ? WC : 1); ++w)
+                pre[w] = __builtin_nontemporal_load(tab.p[w] + 3 + q0 / kSlots + lane);
+        }
+        build_pair_table(lut, tab, WC);
+        if (full)
+            decompress_full_tile<WC, kAcc, kDword>(tab, W, lut, out, q0, lane, stage[wave], pre);
+        else if (t < ntiles)
+            decompress_tail_tile(tab, WC, lut, n, out, kAcc ? 1 : 0, q0, lane);
+        return;
+    }
+    build_pair_table(lut, tab, WC > 0 ? WC : W);
     const size_t stride = size_t(gridDim.x) * kWavesPerBlock;
     const size_t blk = kLoop ? blockIdx.x : xcd_contiguous(blockIdx.x, gridDim.x);
     for (size_t t = blk * kWavesPerBlock + wave; t < ntiles; t += stride) {

@@ -289,11 +289,13 @@ __global__ __launch_bounds__(kThreads) void compress_2bit_dword_kernel(
 // before any is decoded; WC == 0: W read at run time, in groups of four.
 // kDword: out without 16-byte alignment. The tile's float4 slots go to the
 // wave's LDS stage and leave as lane-contiguous 4-byte stores.
+// pre: this lane's W words, already loaded (WC > 0), or NULL to load them here.
 template <int WC, bool kAcc, bool kDword>
 __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& tab, int W_rt,
                                                      const float2* lut,
                                                      float* __restrict__ out, size_t q0,
-                                                     int lane, f32x4* stage)
+                                                     int lane, f32x4* stage,
+                                                     const uint32_t* pre = nullptr)
 {
     const int W = WC > 0 ? WC : W_rt;
     const size_t jmine = (q0 >> 2) + lane;  // the word this lane fetches
@@ -307,7 +309,8 @@ __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& t
         for (int dw = 0; dw < kGroup; ++dw) {
             mine[dw] = (WC == 0 && w0 + dw >= W)
                            ? 0u
-                           : __builtin_nontemporal_load(tab.p[w0 + dw] + 3 + jmine);
+                           : (pre ? pre[w0 + dw]
+                                  : __builtin_nontemporal_load(tab.p[w0 + dw] + 3 + jmine));
         }
 #pragma unroll
         for (int dw = 0; dw < kGroup; ++dw) {
@@ -393,8 +396,29 @@ __device__ __forceinline__ void decompress_2bit_body(const PtrTable<uint32_t>& t
 {
     __shared__ float2 lut[16 * GC_MAX_WORKERS];
     __shared__ f32x4 stage[kDword ? kWavesPerBlock : 1][kDword ? kTileF4 : 1];
-    build_nibble_table(lut, tab, WC > 0 ? WC : W);
     const int lane = threadIdx.x & (kWave - 1);
+    if (!kLoop && WC > 0) {
+        // One tile per wave, W known: the tile's word loads go out before
+        // the table is built, so they are in flight during the header loads
+        // and the barrier (measured ~2% faster at W = 8 than loading after).
+        const size_t t = xcd_contiguous(blockIdx.x, gridDim.x) * kWavesPerBlock + threadIdx.x / kWave;
+        const size_t q0 = t < ntiles ? (ntiles - 1 - t) * kTileF4 : 0;
+        const bool full = t < ntiles && q0 + kTileF4 <= (n >> 2);
+        uint32_t pre[WC > 0 ? WC : 1];
+        if (full) {
+#pragma unroll
+            for (int w = 0; w < (WC > 0 ? WC : 1); ++w)
+                pre[w] = __builtin_nontemporal_load(tab.p[w] + 3 + (q0 >> 2) + lane);
+        }
+        build_nibble_table(lut, tab, WC);
+        if (full)
+            decompress_full_tile<WC, kAcc, kDword>(tab, W, lut, out, q0, lane,
+                                                   stage[kDword ? threadIdx.x / kWave : 0], pre);
+        else if (t < ntiles)
+            decompress_tail_tile(tab, WC, lut, n, out, kAcc ? 1 : 0, q0, lane);
+        return;
+    }
+    build_nibble_table(lut, tab, WC > 0 ? WC : W);
     const size_t stride = size_t(gridDim.x) * kWavesPerBlock;
     // Last tile first: the partial tile's scalar path reads all W blocks
     // word by word, so it starts with the first wave. XCD-contiguous: a

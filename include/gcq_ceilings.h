@@ -72,6 +72,13 @@ int gcq_ceiling_compress(const float* a, float* b, size_t n, uint32_t* words, si
 int gcq_ceiling_dequant(const uint32_t* const* blocks, int W, size_t n, size_t block_cap_words,
                         int pattern, float* out, hipStream_t stream);
 
+/* The ternary dequantize-sum's mix, W = 8: read n/20 elements 12 bytes into
+ * each block (block_cap_words >= 3 + n/20), write out[n]: W n/5 + 4 n bytes.
+ * n must be a multiple of gcq_ceiling_ternary_quantum() (81920). */
+size_t gcq_ceiling_ternary_quantum(void);
+int gcq_ceiling_dequant_ternary(const uint32_t* const* blocks, int W, size_t n,
+                                size_t block_cap_words, float* out, hipStream_t stream);
+
 /* The quantize's mix: read src[n] fp32, write dst[n/4] words: 5 n bytes. */
 int gcq_ceiling_quantize(const float* src, size_t n, uint32_t* dst, hipStream_t stream);
 

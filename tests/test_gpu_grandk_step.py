@@ -62,8 +62,8 @@ def check(got, expect):
                                      (100_003, 10_000, 8, 7), (65_536, 16_384, 4, 15),
                                      (70_001, 16_385, 5, 7), (300_007, 40_000, 9, 127),
                                      (20_000, 5_003, 64, 3), (5_000, 4_001, 2, 1),
-                                     # n above ~1900 K: the dense fill is split between the
-                                     # draw's launch and the gathers' launch
+                                     # n much larger than K: most of the dense fill runs
+                                     # beside the draw, gathers and scatter
                                      (2_000_003, 100, 8, 7), (10_001, 0, 3, 7), (5_000, 1, 2, 7),
                                      (4_000_000, 2_000, 4, 127)])
 def test_grandk_mn_step_small(gcq, n, K, W, s):
@@ -82,6 +82,55 @@ def test_grandk_mn_step_misaligned_dense_without_sums(gcq, misalign, n, K):
     idx, S, dense, norm = run_step(gcq, grads, K, s, seed, misalign=misalign, with_sums=False)
     assert S is None
     check((idx, None, dense, norm), oracle_step(grads, K, s, seed))
+
+
+@pytest.mark.parametrize("off", [1, 2, 3])
+@pytest.mark.parametrize("n,K", [(7, 7), (13, 13), (4_099, 4_099), (16_387, 16_384),
+                                 (100_003, 5_000), (2_000_005, 3_000)])
+def test_grandk_mn_step_dense_head_and_tail(gcq, off, n, K):
+    """dense as a view `off` floats into its buffer (so 4 - off values before
+    its first 16-byte boundary) with n % 4 values after its last whole float4,
+    every position drawn in the small cases: the fill's head, tail, regions
+    and drawn-position bitmap against the oracle, and nothing written
+    outside the view."""
+    announce(f"grandk_mn_step dense view at +{off}, n={n} K={K}")
+    W, s, seed = 3, 7, 0x51DE + n + off
+    grads = [si.normal_f32(si.grad_seed(w, 9), n, 0.01) for w in range(W)]
+    g_dev = [gu.dev(g) for g in grads]
+    buf = torch.full((n + 8,), 7.0, dtype=torch.float32, device=gu.DEV)
+    dense = buf[off:off + n]
+    idx = gu.empty(K, torch.int32, fill=-1)
+    sums = gu.empty(K, torch.int32, fill=-7)
+    norm = torch.empty(1, dtype=torch.float32, device=gu.DEV)
+    ws = torch.empty(gcq.grandk_mn_step_ws_bytes(W, n, K), dtype=torch.uint8, device=gu.DEV)
+    gcq.grandk_mn_step(g_dev, K, seed, s, idx, dense, ws, sums=sums, norm=norm)
+    gu.sync()
+    check((gu.host(idx, np.uint32), gu.host(sums), gu.host(dense), np.float32(gu.host(norm)[0])),
+          oracle_step(grads, K, s, seed))
+    hb = gu.host(buf)
+    assert np.all(hb[:off] == 7.0) and np.all(hb[off + n:] == 7.0)
+
+
+def test_grandk_mn_step_workspace_reused_across_sizes(gcq):
+    """One workspace, sized for the largest call, serves calls of other sizes
+    in turn: whatever a call leaves in it (fill progress, flags, marks of
+    drawn positions) must not reach the next."""
+    W, s = 4, 7
+    cases = [(1_000_003, 10_000, 1), (5_001, 4_000, 2), (1_000_003, 9_000, 3), (60_000, 16_384, 4)]
+    ws = torch.empty(max(gcq.grandk_mn_step_ws_bytes(W, n, K) for n, K, _ in cases),
+                     dtype=torch.uint8, device=gu.DEV)
+    for n, K, seed in cases:
+        announce(f"grandk_mn_step reused workspace n={n} K={K}")
+        grads = [si.normal_f32(si.grad_seed(w, 10 + seed), n, 0.01) for w in range(W)]
+        g_dev = [gu.dev(g) for g in grads]
+        idx = gu.empty(K, torch.int32, fill=-1)
+        sums = gu.empty(K, torch.int32, fill=-7)
+        dense = gu.empty(n, torch.float32, fill=float("nan"))
+        norm = torch.empty(1, dtype=torch.float32, device=gu.DEV)
+        gcq.grandk_mn_step(g_dev, K, seed, s, idx, dense, ws, sums=sums, norm=norm)
+        gu.sync()
+        check((gu.host(idx, np.uint32), gu.host(sums), gu.host(dense),
+               np.float32(gu.host(norm)[0])), oracle_step(grads, K, s, seed))
 
 
 def test_grandk_mn_step_zero_gradients(gcq):
