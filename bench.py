@@ -293,6 +293,111 @@ def summarize_ceilings(d: pathlib.Path) -> pathlib.Path | None:
     return PROFILE_CEILINGS
 
 
+PROFILE_GRANDK = ROOT / "profiles" / "grandk_step_critical_path.md"
+
+
+def summarize_grandk_path(d: pathlib.Path) -> pathlib.Path | None:
+    """profiles/grandk_step_critical_path.md: the launches of the one-call
+    GlobalRandK-MN step, and each of its stages run alone, from the kernel
+    trace of the extras run."""
+    import csv
+    files = list((d / "prof_extra").glob("*kernel_trace.csv")) if (d / "prof_extra").exists() else []
+    if not files:
+        return None
+    rows = sorted(csv.DictReader(open(files[0])), key=lambda r: int(r["Start_Timestamp"]))
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # noqa: E731
+    med = lambda v: statistics.median(v) if v else float("nan")  # noqa: E731
+    steps = []
+    for i in range(len(rows) - 2):
+        a, b, c = rows[i], rows[i + 1], rows[i + 2]
+        if (a["Kernel_Name"].startswith("grandk_draw_fill_kernel")
+                and b["Kernel_Name"].startswith("grandk_gather_fill_kernel")
+                and c["Kernel_Name"].startswith("grandk_quantize_scatter_kernel")):
+            steps.append((a, b, c))
+    if not steps:
+        return None
+    by = lambda name: [dur(r) for r in rows if r["Kernel_Name"].startswith(name)]  # noqa: E731
+    l1, l2, l3 = ([dur(t[j]) for t in steps] for j in range(3))
+    g12 = [(int(t[1]["Start_Timestamp"]) - int(t[0]["End_Timestamp"])) / 1e3 for t in steps]
+    g23 = [(int(t[2]["Start_Timestamp"]) - int(t[1]["End_Timestamp"])) / 1e3 for t in steps]
+    n, K, W = N_C2, 10_000, W_C2
+    draw = by("grandk_indices_lds_kernel")
+    fill = by("fill_zero_kernel")
+    gather = by("gather_kernel")
+    # the separate-call step's quantizes are the smallest qsgd_quantize launches
+    qrows = [r for r in rows if r["Kernel_Name"].startswith("qsgd_quantize")
+             and "sum" not in r["Kernel_Name"]]
+    gmin = min((int(r["Grid_Size_X"]) for r in qrows), default=0)
+    quant = [dur(r) for r in qrows if int(r["Grid_Size_X"]) == gmin]
+    scatter = by("qsgd_dequant_scatter_kernel")
+    ceil_gbs = None
+    if PROFILE_CEILINGS.exists():
+        import re as _re
+        m = _re.search(r"^\| ceil_write_tile_kernel \|.*?\| ([0-9.]+) \| ([0-9,]+) \| ([0-9,]+) \|",
+                       PROFILE_CEILINGS.read_text(), _re.M)
+        if m:
+            ceil_gbs = float(m.group(3).replace(",", ""))
+    fill_floor = 4 * n / (ceil_gbs * 1e3) if ceil_gbs else None  # us
+    lines = [
+        "# GlobalRandK-MN step: per-launch critical path (rocprofv3 kernel trace)",
+        "",
+        "Commands (repo root):",
+        "",
+        f"    {PROFILE_COMMANDS['trace_extra']}",
+        f"    {PROFILE_COMMANDS['summary']}",
+        "",
+        f"Workload: n = {n:,}, K = {K}, W = {W}, s = 7. `grandk_mn_step` is three launches on "
+        "one stream; the same run also times the step as separate calls, whose kernels give "
+        "each stage's cost alone. Durations are medians over the trace's launches. The "
+        "profiler adds its own latency between launches, so the gaps below are wider than "
+        "in the untraced benchmark (`grandk_mn.ms_per_step` in the bench line).",
+        "",
+        "| launch of grandk_mn_step | what runs | median us |",
+        "|---|---|---|",
+        f"| 1 `grandk_draw_fill_kernel` | the K-index draw in one workgroup (Philox targets + "
+        f"LDS resolve), beside the first share of the dense zero fill | {med(l1):.2f} |",
+        f"| gap | | {med(g12):.2f} |",
+        f"| 2 `grandk_gather_fill_kernel` | W x K gathers and partial maxima, beside the rest of "
+        f"the fill | {med(l2):.2f} |",
+        f"| gap | | {med(g23):.2f} |",
+        f"| 3 `grandk_quantize_scatter_kernel` | norm, levels, sums, dequantize, scatter (after "
+        f"the whole fill) | {med(l3):.2f} |",
+        f"| whole step, first launch's start to last launch's end | | "
+        f"{med([(int(t[2]['End_Timestamp']) - int(t[0]['Start_Timestamp'])) / 1e3 for t in steps]):.2f} |",
+        f"| steps traced | | {len(steps)} |",
+        "",
+        "| stage alone (separate-call step) | kernel | median us |",
+        "|---|---|---|",
+        f"| the draw | `grandk_indices_lds_kernel` | {med(draw):.2f} |",
+        f"| the dense zero fill, {4 * n:,} B | `fill_zero_kernel` | {med(fill):.2f} |",
+        f"| one worker's gather of K values | `gather_kernel` | {med(gather):.2f} |",
+        f"| one worker's quantize of K values | `qsgd_quantize*` (K-sized launches) | "
+        f"{med(quant):.2f} |",
+        f"| level sum, dequantize, scatter | `qsgd_dequant_scatter_kernel` | {med(scatter):.2f} |",
+        "",
+    ]
+    if fill_floor:
+        lines += [f"Fill floor: {4 * n:,} B at the measured write ceiling "
+                  f"({ceil_gbs:,.0f} GB/s, `profiles/hbm_ceilings.md`) = {fill_floor:.1f} us."]
+    lines += [
+        "",
+        "Why the step cannot get much shorter on this part:",
+        "",
+        "- The scatter must follow the whole fill, so launch 3 comes after the fill: the step "
+        "costs at least the fill floor plus launch 3 plus one launch gap.",
+        "- The draw is the only stage that overlaps the fill at full speed: it touches no "
+        "global memory until it writes the indices. Stages that load from memory (the "
+        "gathers, the quantize, any flag a workgroup polls) run several times slower while "
+        "the fill's writes drain, so they cannot hide under the fill.",
+        "- Launch 1 therefore holds the draw and as much fill as drains in the draw's time; "
+        "launch 2 holds the gathers and the rest of the fill; launch 3 the quantize and "
+        "scatter.",
+        "",
+    ]
+    PROFILE_GRANDK.write_text("\n".join(lines))
+    return PROFILE_GRANDK
+
+
 def summarize_profiles(out_dir: str) -> None:
     """Write the profiles/ summaries whose rocprofv3 CSV output is under
     out_dir (each summary needs only its own runs)."""
@@ -302,6 +407,9 @@ def summarize_profiles(out_dir: str) -> None:
     c = summarize_ceilings(d)
     if c:
         wrote.append(c)
+    gk = summarize_grandk_path(d)
+    if gk:
+        wrote.append(gk)
     if not (d / "pmc_cal_fetch").exists():
         print("wrote " + ", ".join(str(w) for w in wrote))
         return
