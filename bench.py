@@ -298,28 +298,38 @@ PROFILE_GRANDK = ROOT / "profiles" / "grandk_step_critical_path.md"
 
 def summarize_grandk_path(d: pathlib.Path) -> pathlib.Path | None:
     """profiles/grandk_step_critical_path.md: the launches of the one-call
-    GlobalRandK-MN step, and each of its stages run alone, from the kernel
-    trace of the extras run."""
+    GlobalRandK-MN step at the ResNet-50 size and at n = 2^20 (the chain with
+    almost no fill), and each stage run alone, from the kernel trace of the
+    extras run."""
     import csv
     files = list((d / "prof_extra").glob("*kernel_trace.csv")) if (d / "prof_extra").exists() else []
     if not files:
         return None
     rows = sorted(csv.DictReader(open(files[0])), key=lambda r: int(r["Start_Timestamp"]))
-    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # noqa: E731
+    ts = lambda r, k: int(r[k + "_Timestamp"])  # noqa: E731
+    dur = lambda r: (ts(r, "End") - ts(r, "Start")) / 1e3  # noqa: E731
     med = lambda v: statistics.median(v) if v else float("nan")  # noqa: E731
-    steps = []
-    for i in range(len(rows) - 2):
-        a, b, c = rows[i], rows[i + 1], rows[i + 2]
-        if (a["Kernel_Name"].startswith("grandk_draw_fill_kernel")
-                and b["Kernel_Name"].startswith("grandk_gather_fill_kernel")
-                and c["Kernel_Name"].startswith("grandk_quantize_scatter_kernel")):
-            steps.append((a, b, c))
+    names = ("grandk_draw_fill_kernel", "grandk_gather_fill_kernel",
+             "grandk_quantize_scatter_kernel")
+    steps = [rows[i:i + 3] for i in range(len(rows) - 2)
+             if all(rows[i + j]["Kernel_Name"].startswith(names[j]) for j in range(3))]
     if not steps:
         return None
+    # the full-size steps have the larger launch-1 grid (more fill workgroups)
+    grids = sorted({int(t[0]["Grid_Size_X"]) for t in steps})
+    big = [t for t in steps if int(t[0]["Grid_Size_X"]) == grids[-1]]
+    small = [t for t in steps if int(t[0]["Grid_Size_X"]) == grids[0]] if len(grids) > 1 else []
+
+    def launch_rows(group):
+        l1, l2, l3 = ([dur(t[j]) for t in group] for j in range(3))
+        g12 = [(ts(t[1], "Start") - ts(t[0], "End")) / 1e3 for t in group]
+        g23 = [(ts(t[2], "Start") - ts(t[1], "End")) / 1e3 for t in group]
+        whole = [(ts(t[2], "End") - ts(t[0], "Start")) / 1e3 for t in group]
+        nxt = [(ts(group[i + 1][0], "Start") - ts(group[i][0], "Start")) / 1e3
+               for i in range(len(group) - 1)]
+        return [med(l1), med(g12), med(l2), med(g23), med(l3), med(whole), med(nxt), len(group)]
+
     by = lambda name: [dur(r) for r in rows if r["Kernel_Name"].startswith(name)]  # noqa: E731
-    l1, l2, l3 = ([dur(t[j]) for t in steps] for j in range(3))
-    g12 = [(int(t[1]["Start_Timestamp"]) - int(t[0]["End_Timestamp"])) / 1e3 for t in steps]
-    g23 = [(int(t[2]["Start_Timestamp"]) - int(t[1]["End_Timestamp"])) / 1e3 for t in steps]
     n, K, W = N_C2, 10_000, W_C2
     draw = by("grandk_indices_lds_kernel")
     fill = by("fill_zero_kernel")
@@ -332,12 +342,20 @@ def summarize_grandk_path(d: pathlib.Path) -> pathlib.Path | None:
     scatter = by("qsgd_dequant_scatter_kernel")
     ceil_gbs = None
     if PROFILE_CEILINGS.exists():
-        import re as _re
-        m = _re.search(r"^\| ceil_write_tile_kernel \|.*?\| ([0-9.]+) \| ([0-9,]+) \| ([0-9,]+) \|",
-                       PROFILE_CEILINGS.read_text(), _re.M)
+        m = re.search(r"^\| ceil_write_tile_kernel \|.*?\| ([0-9.]+) \| ([0-9,]+) \| ([0-9,]+) \|",
+                      PROFILE_CEILINGS.read_text(), re.M)
         if m:
             ceil_gbs = float(m.group(3).replace(",", ""))
     fill_floor = 4 * n / (ceil_gbs * 1e3) if ceil_gbs else None  # us
+    B = launch_rows(big)
+    S = launch_rows(small) if small else [float("nan")] * 8
+    what = ["1 `grandk_draw_fill_kernel`: the K-index draw in one workgroup (Philox targets, "
+            "LDS chains), beside the first share of the dense zero fill",
+            "gap", "2 `grandk_gather_fill_kernel`: W x K gathers and partial maxima, beside the "
+            "rest of the fill", "gap",
+            "3 `grandk_quantize_scatter_kernel`: norm, levels, sums, dequantize, scatter",
+            "first launch's start to last launch's end",
+            "one step's start to the next step's start", "steps traced"]
     lines = [
         "# GlobalRandK-MN step: per-launch critical path (rocprofv3 kernel trace)",
         "",
@@ -346,27 +364,22 @@ def summarize_grandk_path(d: pathlib.Path) -> pathlib.Path | None:
         f"    {PROFILE_COMMANDS['trace_extra']}",
         f"    {PROFILE_COMMANDS['summary']}",
         "",
-        f"Workload: n = {n:,}, K = {K}, W = {W}, s = 7. `grandk_mn_step` is three launches on "
-        "one stream; the same run also times the step as separate calls, whose kernels give "
-        "each stage's cost alone. Durations are medians over the trace's launches. The "
-        "profiler adds its own latency between launches, so the gaps below are wider than "
-        "in the untraced benchmark (`grandk_mn.ms_per_step` in the bench line).",
+        f"Workload: K = {K}, W = {W}, s = 7, at n = {n:,} (ResNet-50) and at n = 1,048,576 "
+        "(the same chain of draw, gathers, norm, quantize and scatter with a 4 MB fill instead "
+        "of a 102 MB one). `grandk_mn_step` is three launches on one stream. Durations are "
+        "medians over the trace's launches (eager calls and graph replays together); the "
+        "profiler adds latency of its own between launches, so the spans are longer than the "
+        "graph-timed `grandk_mn.ms_per_step` and `chain_ms_per_step` of the bench line.",
         "",
-        "| launch of grandk_mn_step | what runs | median us |",
+        f"| grandk_mn_step | n = {n:,}, us | n = 1,048,576, us |",
         "|---|---|---|",
-        f"| 1 `grandk_draw_fill_kernel` | the K-index draw in one workgroup (Philox targets + "
-        f"LDS resolve), beside the first share of the dense zero fill | {med(l1):.2f} |",
-        f"| gap | | {med(g12):.2f} |",
-        f"| 2 `grandk_gather_fill_kernel` | W x K gathers and partial maxima, beside the rest of "
-        f"the fill | {med(l2):.2f} |",
-        f"| gap | | {med(g23):.2f} |",
-        f"| 3 `grandk_quantize_scatter_kernel` | norm, levels, sums, dequantize, scatter (after "
-        f"the whole fill) | {med(l3):.2f} |",
-        f"| whole step, first launch's start to last launch's end | | "
-        f"{med([(int(t[2]['End_Timestamp']) - int(t[0]['Start_Timestamp'])) / 1e3 for t in steps]):.2f} |",
-        f"| steps traced | | {len(steps)} |",
+    ]
+    for k in range(7):
+        lines.append(f"| {what[k]} | {B[k]:.2f} | {S[k]:.2f} |")
+    lines.append(f"| {what[7]} | {B[7]} | {S[7]} |")
+    lines += [
         "",
-        "| stage alone (separate-call step) | kernel | median us |",
+        "| stage alone (the separate-call step at the full size) | kernel | median us |",
         "|---|---|---|",
         f"| the draw | `grandk_indices_lds_kernel` | {med(draw):.2f} |",
         f"| the dense zero fill, {4 * n:,} B | `fill_zero_kernel` | {med(fill):.2f} |",
@@ -378,20 +391,19 @@ def summarize_grandk_path(d: pathlib.Path) -> pathlib.Path | None:
     ]
     if fill_floor:
         lines += [f"Fill floor: {4 * n:,} B at the measured write ceiling "
-                  f"({ceil_gbs:,.0f} GB/s, `profiles/hbm_ceilings.md`) = {fill_floor:.1f} us."]
+                  f"({ceil_gbs:,.0f} GB/s, `profiles/hbm_ceilings.md`) = {fill_floor:.1f} us.", ""]
     lines += [
+        "Reading:",
         "",
-        "Why the step cannot get much shorter on this part:",
-        "",
-        "- The scatter must follow the whole fill, so launch 3 comes after the fill: the step "
-        "costs at least the fill floor plus launch 3 plus one launch gap.",
-        "- The draw is the only stage that overlaps the fill at full speed: it touches no "
-        "global memory until it writes the indices. Stages that load from memory (the "
-        "gathers, the quantize, any flag a workgroup polls) run several times slower while "
-        "the fill's writes drain, so they cannot hide under the fill.",
-        "- Launch 1 therefore holds the draw and as much fill as drains in the draw's time; "
-        "launch 2 holds the gathers and the rest of the fill; launch 3 the quantize and "
-        "scatter.",
+        "- At n = 1,048,576 the fill is negligible, so that column is the chain itself: the "
+        "draw in launch 1, then the gathers, then norm -> quantize -> scatter, with two launch "
+        "gaps between them. The full-size step costs that chain plus the part of the fill that "
+        "does not hide beside it.",
+        "- Launch 1 lasts about as long as the draw run alone: the draw only touches LDS, so "
+        "the fill beside it runs at full speed and costs the step nothing extra.",
+        "- Launch 2 is where the fill and the gathers meet: the gathers' scattered reads slow "
+        "while the fill's writes drain, and the fill slows beside them.",
+        "- Launch 3 must follow the whole fill (its scatter lands anywhere in dense).",
         "",
     ]
     PROFILE_GRANDK.write_text("\n".join(lines))
@@ -1194,35 +1206,36 @@ def bench_grandk(gcq, torch, np, si, steps: int):
     def one_call(seed):
         gcq.grandk_mn_step(grads, K, seed, s, idx, dense, sws, sums=sums, norm=norm)
 
-    for k in range(3):
-        one_call(k)
-    torch.cuda.synchronize()
-    t0, t1 = mk(), mk()
-    t0.record()
-    for k in range(steps):
-        one_call(k)
-    t1.record()
-    torch.cuda.synchronize()
-    one_eager = t0.elapsed_time(t1) / steps
-    graph = graph_of(torch, lambda: one_call(0))
-    t0, t1 = mk(), mk()
-    t0.record()
-    for _ in range(steps):
-        graph.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    tot = t0.elapsed_time(t1) / steps
-    del graph, grads, dense, sws
+    gpu_ms, eager_ms, host_us = time_grandk_calls(torch, one_call, steps)
+    # the latency chain alone: the same step on n = 2^20 values, whose fill
+    # is ~0.7 us
+    nc = 1 << 20
+    cgrads = [g[:nc] for g in grads]
+    cdense = torch.empty(nc, dtype=torch.float32, device=dev)
+    cws = torch.empty(gcq.grandk_mn_step_ws_bytes(W, nc, K), dtype=torch.uint8, device=dev)
+    chain_ms, _, _ = time_grandk_calls(
+        torch, lambda seed: gcq.grandk_mn_step(cgrads, K, seed, s, idx, cdense, cws, sums=sums,
+                                               norm=norm), steps)
+    del grads, dense, sws, cgrads, cdense, cws
     torch.cuda.empty_cache()
     del host
     dense_gbs = 4 * n / (fill / 1e3) / 1e9
-    step_gbs = 4 * n / (one_eager / 1e3) / 1e9
+    step_gbs = 4 * n / (gpu_ms / 1e3) / 1e9
     return {"workload": f"GRandK-MN: n={n:,}, K={K}, W={W}, s={s}: shared index draw, gather, "
                         "max-norm, quantize, level sum, scatter into a dense fp32 buffer",
-            "ms_per_step": one_eager, "values_per_s": K * W / (one_eager / 1e3),
-            "timing": "grandk_mn_step (three launches), K steps back to back between two "
-                      "events; graph_ms_per_step replays it from a HIP graph",
-            "graph_ms_per_step": tot,
+            "ms_per_step": gpu_ms, "values_per_s": K * W / (gpu_ms / 1e3),
+            "timing": f"grandk_mn_step (three launches): a HIP graph of {GK_GRAPH_STEPS} steps "
+                      "replayed back to back, so the GPU never waits for the host",
+            "eager_ms_per_step": eager_ms,
+            "host_us_per_call": round(host_us, 2),
+            "eager_timing": "the same calls issued one by one from Python between two events; "
+                            "host_us_per_call is the binding's host time per call (argument "
+                            "checks, marshalling, three kernel launches): where it exceeds the "
+                            "GPU's time, eager_ms_per_step measures the host",
+            "chain_ms_per_step": chain_ms,
+            "chain_timing": f"the same step at n = {nc:,} (a 4 MB fill), graph-timed: the "
+                            "draw -> gather -> norm -> quantize -> scatter chain and its launch "
+                            "gaps without the bulk of the fill",
             "separate_calls": {
                 "timing": "the 20 separate calls (draw, W gathers, max-norm, W quantizes, "
                           "dequantize-scatter): HIP graph replay; stages from an eager pass",
@@ -1237,6 +1250,47 @@ def bench_grandk(gcq, torch, np, si, steps: int):
                          "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
             "oracle_ms_per_step": None, "steps": steps}
+
+
+GK_GRAPH_STEPS = 20
+
+
+def time_grandk_calls(torch, call, steps: int):
+    """(GPU ms per step, eager ms per step, host us per call) of call(seed):
+    the GPU time from a HIP graph of GK_GRAPH_STEPS calls replayed back to
+    back; the eager time from `steps` calls issued one by one; the host time
+    from the wall clock around those calls."""
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    for k in range(3):
+        call(k)
+    torch.cuda.synchronize()
+    t0, t1 = mk(), mk()
+    h0 = time.perf_counter()
+    t0.record()
+    for k in range(steps):
+        call(k)
+    h1 = time.perf_counter()
+    t1.record()
+    torch.cuda.synchronize()
+    eager = t0.elapsed_time(t1) / steps
+    host_us = (h1 - h0) / steps * 1e6
+
+    def many():
+        for k in range(GK_GRAPH_STEPS):
+            call(k)
+
+    graph = graph_of(torch, many)
+    reps = max(3, steps // GK_GRAPH_STEPS)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(reps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    gpu = t0.elapsed_time(t1) / (reps * GK_GRAPH_STEPS)
+    del graph
+    return gpu, eager, host_us
 
 
 def cpu_baseline(np, si, budget_s: float, workloads=()):

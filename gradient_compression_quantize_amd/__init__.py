@@ -124,22 +124,38 @@ def _torch():
 
 
 _gpu_present = None
+_get_device = None
+_raw_stream = None
 
 
 def _current_device():
     """Index of torch's current device, or None when torch sees no GPU (then
     there is nothing to compare against: every call fails validation or its
-    device-tensor checks first)."""
-    global _gpu_present
-    torch = _torch()
+    device-tensor checks first). Once torch's device state is set up, this
+    reads the device straight from torch's C layer (every call of the
+    binding asks once per tensor, so it is worth a few microseconds a call)."""
+    global _gpu_present, _get_device, _raw_stream
     if _gpu_present is None:
-        _gpu_present = bool(torch.cuda.is_available())
-    return torch.cuda.current_device() if _gpu_present else None
+        torch = _torch()
+        present = bool(torch.cuda.is_available())
+        if present:
+            torch.cuda.current_device()  # sets up torch's device state
+            _get_device = getattr(torch._C, "_cuda_getDevice", torch.cuda.current_device)
+            _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _gpu_present = present
+    if not _gpu_present:
+        return None
+    return _get_device() if _get_device is not None else _torch().cuda.current_device()
 
 
 def _stream(stream) -> ctypes.c_void_p:
     torch = _torch()
     if stream is None:
+        cur = _current_device()
+        if cur is not None and _raw_stream is not None:
+            # the same handle as torch.cuda.current_stream().cuda_stream,
+            # without building a Stream object
+            return _vp(_raw_stream(cur))
         s = torch.cuda.current_stream()
     else:
         s = stream
@@ -151,22 +167,33 @@ def _stream(stream) -> ctypes.c_void_p:
     return _vp(s.cuda_stream)
 
 
-def _dev(t, dtype, what: str) -> ctypes.c_void_p:
-    """Device pointer of a contiguous tensor of the given dtype on the current
-    device (the device the library launches on)."""
-    if t is None:
-        return _vp(None)
+def _refuse(t, dtype, what: str, cur) -> None:
     if not t.is_cuda:
         raise TypeError(f"{what}: expected a device tensor")
     if t.dtype != dtype:
         raise TypeError(f"{what}: expected {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise TypeError(f"{what}: expected a contiguous tensor")
-    cur = _current_device()
-    if cur is not None and t.get_device() != cur:
-        raise ValueError(f"{what}: on cuda:{t.get_device()} but the current device is "
-                         f"cuda:{cur}; the library launches on the current device")
-    return _vp(t.data_ptr())
+    raise ValueError(f"{what}: on cuda:{t.get_device()} but the current device is "
+                     f"cuda:{cur}; the library launches on the current device")
+
+
+def _ptr(t, dtype, what: str, cur, k=None) -> int:
+    """Device address of a contiguous tensor of the given dtype on device
+    `cur` (the current device, which the library launches on; None when
+    torch sees no GPU). The error names `what`, or `what[k]`."""
+    if (not t.is_cuda or t.dtype != dtype or not t.is_contiguous()
+            or (cur is not None and t.get_device() != cur)):
+        _refuse(t, dtype, what if k is None else f"{what}[{k}]", cur)
+    return t.data_ptr()
+
+
+def _dev(t, dtype, what: str) -> ctypes.c_void_p:
+    """Device pointer of a contiguous tensor of the given dtype on the current
+    device (the device the library launches on)."""
+    if t is None:
+        return _vp(None)
+    return _vp(_ptr(t, dtype, what, _current_device()))
 
 
 def _need_norm(norm, what: str) -> None:
@@ -178,8 +205,9 @@ def _need_norm(norm, what: str) -> None:
 
 def _ptr_array(ts, dtype, what: str):
     arr = (_vp * len(ts))()
+    cur = _current_device()
     for k, t in enumerate(ts):
-        arr[k] = _dev(t, dtype, f"{what}[{k}]").value
+        arr[k] = None if t is None else _ptr(t, dtype, what, cur, k)
     return arr
 
 
