@@ -14,6 +14,7 @@
 #include "gcq_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <mutex>
 #include <string>
@@ -1095,17 +1096,41 @@ __global__ __launch_bounds__(kRandKThreads) void grandk_draw_fill_kernel(
 // rest runs beside the gathers in launch 2 (the scatter in launch 3 comes
 // after both). Launch 1 lasts about max(draw, its fill), launch 2 about
 // max(gathers, the rest of the fill), so the split puts about as much fill
-// beside the draw as the draw takes. Measured on MI355X: the draw costs
-// about 1.24 ns per index (12.4 us at K = 10000), the fill about 0.70 ps per
-// value (18 us for 25.6M), a ratio of ~1770; the factor used is a little
-// above it, so that the fill (the longer job) stays on the critical path.
+// beside the draw as the draw takes. The draw is bound by one CU's ALU, so
+// its time follows the device's core clock: measured on MI355X, about 2980
+// cycles per index (1.24 ns at 2.4 GHz). The fill zeroes about 1.43 values
+// per ns at this part's write rate. The split takes their product for the
+// device's reported clock, 6% over, so that the fill (the longer job) stays
+// on the critical path. Only the speed depends on it, never the results.
 // Returns n, or a multiple of 4 below n, so that launch 2's part keeps
 // dense's float4 alignment.
-constexpr double kDrawPerFillValue = 1900.0;
+constexpr double kDrawCyclesPerIndex = 2980.0;
+constexpr double kFillValuesPerNs = 1.43;
+constexpr double kFillSplitMargin = 1.06;
+
+// Core clock of the current device in GHz (2.4 if the runtime cannot say),
+// queried once per device.
+double core_clock_ghz()
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> khz[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 2.4;
+    int v = dev >= 0 && dev < kMaxDevices ? khz[dev].load(std::memory_order_relaxed) : 0;
+    if (v == 0) {
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeClockRate, dev) != hipSuccess || v <= 0)
+            v = 2400000;
+        if (dev >= 0 && dev < kMaxDevices)
+            khz[dev].store(v, std::memory_order_relaxed);
+    }
+    return double(v) * 1e-6;
+}
 
 size_t grandk_fill_split(size_t n, uint32_t K)
 {
-    const double share = kDrawPerFillValue * double(K) / double(n);
+    const double draw_ns = kDrawCyclesPerIndex / core_clock_ghz() * double(K);
+    const double share = kFillSplitMargin * kFillValuesPerNs * draw_ns / double(n);
     if (share >= 1.0)
         return n;
     return size_t(share * double(n)) & ~size_t(3);
