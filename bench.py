@@ -240,6 +240,7 @@ def ceiling_kernel_bytes() -> dict:
         "ceil_read_chunked_kernel": (4 * W_C3 * n3, "read, chunked (8 buffers per launch)"),
         "ceil_read_tile_kernel": (4 * n3, "read, one tile per wave (1 buffer per launch)"),
         "ceil_levelsum_mix_kernel": ((W_C3 + 8) * n3, "level-sum mix (W = 8)"),
+        "ceil_quantize_sum_mix_kernel": ((4 * W_C3 + 8) * n3, "fused quantize-sum mix (W = 8)"),
         "ceil_quantize_mix_kernel": (5 * n3, "quantize mix"),
         "ceil_write_tile_kernel": (4 * n2, "write, one tile per wave"),
         "ceil_write_stride_kernel": (4 * n2, "write, grid-stride"),
@@ -658,7 +659,12 @@ def measure_ceilings(torch, steps: int) -> dict:
     sums, o3 = zeros(n3, torch.int32), zeros(n3)
     out["levelsum_mix"] = entry((W_C3 + 8) * n3,
                                 {"tile": timed([lambda: cl.levelsum(lv, n3, sums, o3)])}, n3)
-    del lv, sums
+    del lv
+    log("ceilings: fused quantize-sum mix")
+    grads = [zeros(n3) for _ in range(W_C3)]
+    out["quantize_sum_mix"] = entry((4 * W_C3 + 8) * n3, {
+        "tile": timed([lambda: cl.quantize_sum(grads, n3, sums, o3)])}, n3)
+    del grads, sums
     log("ceilings: quantize mix")
     src2, dst2 = [o3, zeros(n3)], [zeros(n3 // 4, torch.int32) for _ in range(2)]
     out["quantize_mix"] = entry(5 * n3, {"tile": timed(
@@ -1515,6 +1521,9 @@ def main() -> int:
             with_ceiling(q["roofline_maxnorm"], q["roofline_maxnorm"]["achieved"], ceil, "read")
             with_ceiling(q["roofline_level_sum"], q["roofline_level_sum"]["achieved"], ceil,
                          "levelsum_mix")
+            if "fused" in q:
+                with_ceiling(q["fused"]["roofline"], q["fused"]["roofline"]["achieved"], ceil,
+                             "quantize_sum_mix")
         if "multi_tensor" in result:
             m = result["multi_tensor"]
             with_ceiling(m["roofline"], m["gbs"], ceil, "compress_mix")

@@ -44,9 +44,10 @@ def load() -> ctypes.CDLL:
         L.gcq_ceiling_ternary_quantum.restype = _sz
         L.gcq_ceiling_dequant_ternary.argtypes = [ctypes.POINTER(_vp), _i, _sz, _sz, _vp, _vp]
         L.gcq_ceiling_levelsum.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _vp, _vp]
+        L.gcq_ceiling_quantize_sum.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _vp, _vp]
         for f in ("gcq_ceiling_read", "gcq_ceiling_write", "gcq_ceiling_compress",
                   "gcq_ceiling_dequant", "gcq_ceiling_dequant_ternary", "gcq_ceiling_quantize",
-                  "gcq_ceiling_levelsum"):
+                  "gcq_ceiling_levelsum", "gcq_ceiling_quantize_sum"):
             getattr(L, f).restype = _i
         _lib = L
     return _lib
@@ -145,3 +146,12 @@ def levelsum(levels: Sequence, n: int, sums, out, stream=None) -> None:
     _need(out, n, "out")
     _check(load().gcq_ceiling_levelsum(_arr(levels), len(levels), n, _p(sums), _p(out),
                                        _stream(stream)))
+
+
+def quantize_sum(grads: Sequence, n: int, sums, out, stream=None) -> None:
+    for g in grads:
+        _need(g, n, "gradient")
+    _need(sums, n, "sums")
+    _need(out, n, "out")
+    _check(load().gcq_ceiling_quantize_sum(_arr(grads), len(grads), n, _p(sums), _p(out),
+                                           _stream(stream)))

@@ -351,6 +351,42 @@ __global__ __launch_bounds__(kThreads) void ceil_levelsum_mix_kernel(Ptrs<uint32
     }
 }
 
+// ---- the fused quantize-sum mix -------------------------------------------------
+
+// Per wave tile of 4 x 64 slots of 4 values: the workers in turn, each one's
+// 4 float4 per lane loaded together (the fused kernel's worker loop), then an
+// int4 and a float4 written per slot.
+__global__ __launch_bounds__(kThreads) void ceil_quantize_sum_mix_kernel(Ptrs<float> g,
+                                                                         int32_t* __restrict__ sums,
+                                                                         float* __restrict__ out)
+{
+    const size_t tile = size_t(blockIdx.x) * kWaves + threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const size_t q0 = tile * kTileF4 + lane;
+    i32x4 S[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        S[u] = i32x4{0, 0, 0, 0};
+#pragma unroll 1
+    for (int k = 0; k < kDeqW; ++k) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(g.p[k]) + q0;
+        f32x4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            x[u] = __builtin_nontemporal_load(src + u * kWave);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            S[u] += i32x4{int(fbits(x[u].x) & 1u), int(fbits(x[u].y) & 1u),
+                          int(fbits(x[u].z) & 1u), int(fbits(x[u].w) & 1u)};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        __builtin_nontemporal_store(S[u], reinterpret_cast<i32x4*>(sums) + q0 + u * kWave);
+        const f32x4 v = {float(S[u].x), float(S[u].y), float(S[u].z), float(S[u].w)};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out) + q0 + u * kWave);
+    }
+}
+
 bool whole(size_t n) { return n > 0 && n % kQuantum == 0; }
 
 }  // namespace
@@ -506,4 +542,20 @@ GCQ_CEIL_API int gcq_ceiling_levelsum(const uint32_t* const* levels, int W, size
     hipLaunchKernelGGL(ceil_levelsum_mix_kernel, dim3(unsigned(n / 512 / kWaves)),
                        dim3(kThreads), 0, stream, tab, sums, out);
     return launched("gcq_ceiling_levelsum");
+}
+
+GCQ_CEIL_API int gcq_ceiling_quantize_sum(const float* const* grads, int W, size_t n,
+                                          int32_t* sums, float* out, hipStream_t stream)
+{
+    if (!whole(n) || W != kDeqW || !grads || !aligned16(sums) || !aligned16(out))
+        return fail("gcq_ceiling_quantize_sum: bad arguments (W must be 8)");
+    Ptrs<float> tab{};
+    for (int k = 0; k < W; ++k) {
+        if (!aligned16(grads[k]))
+            return fail("gcq_ceiling_quantize_sum: gradients must be 16-byte aligned");
+        tab.p[k] = grads[k];
+    }
+    hipLaunchKernelGGL(ceil_quantize_sum_mix_kernel, dim3(unsigned(n / kTileVals / kWaves)),
+                       dim3(kThreads), 0, stream, tab, sums, out);
+    return launched("gcq_ceiling_quantize_sum");
 }

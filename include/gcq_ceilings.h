@@ -88,6 +88,12 @@ int gcq_ceiling_quantize(const float* src, size_t n, uint32_t* dst, hipStream_t 
 int gcq_ceiling_levelsum(const uint32_t* const* levels, int W, size_t n, int32_t* sums,
                          float* out, hipStream_t stream);
 
+/* The fused quantize-sum's mix, W = 8: read n fp32 from each of W
+ * gradients (HOST array of device pointers), the workers in turn per tile,
+ * write sums[n] int32 and out[n] fp32: (4 W + 8) n bytes. */
+int gcq_ceiling_quantize_sum(const float* const* grads, int W, size_t n, int32_t* sums,
+                             float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
