@@ -60,3 +60,57 @@ def test_roofline_names_the_higher_fraction(monkeypatch):
     insts = int(0.3 * bench.VALU_PEAK_T_LANE_INSTS * 1e12 * 1e-3 / 64)
     monkeypatch.setattr(bench, "valu_insts_from_profile", lambda k: insts)
     assert bench.hbm_alu_roofline("k", "k_kernel", 4_000_000_000, 1e-3)["bound"] == "hbm"
+
+
+def _write_trace(path: pathlib.Path, rows) -> None:
+    import csv
+    path.parent.mkdir(parents=True, exist_ok=True)
+    fields = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X",
+              "Workgroup_Size_X", "LDS_Block_Size"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for name, start, end, grid in rows:
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": start, "End_Timestamp": end,
+                        "Grid_Size_X": grid, "Workgroup_Size_X": 256, "LDS_Block_Size": 0})
+
+
+def test_grandk_critical_path_summary_from_a_trace(tmp_path, monkeypatch):
+    """The GlobalRandK summary finds the step's three launches in a kernel
+    trace, tells the full-size steps from the n = 2^20 ones by launch 1's
+    grid, and reports each launch's median duration and the gaps (ns
+    timestamps in, us out)."""
+    sys.path.insert(0, str(ROOT))
+    import bench
+    rows, t = [], 0
+
+    def step(grid, d1, d2, d3, gap):
+        nonlocal t
+        for name, d, g in (("grandk_draw_fill_kernel", d1, grid),
+                           ("grandk_gather_fill_kernel", d2, 9000),
+                           ("grandk_quantize_scatter_kernel", d3, 8000)):
+            rows.append((name, t, t + d, g))
+            t += d + gap
+
+    for _ in range(3):
+        step(1_188_864, 14_000, 8_000, 4_500, 1_000)
+    for _ in range(3):
+        step(64_512, 12_500, 4_500, 4_500, 2_000)
+    rows.append(("fill_zero_kernel", t, t + 17_800, 4096))
+    _write_trace(tmp_path / "prof_extra" / "extra_kernel_trace.csv", rows)
+    out = tmp_path / "gk.md"
+    monkeypatch.setattr(bench, "PROFILE_GRANDK", out)
+    monkeypatch.setattr(bench, "PROFILE_CEILINGS", tmp_path / "no_ceilings.md")
+    assert bench.summarize_grandk_path(tmp_path) == out
+    text = out.read_text()
+    assert "| 14.00 | 12.50 |" in text  # launch 1, full size | n = 2^20
+    assert "| 8.00 | 4.50 |" in text    # launch 2
+    assert "| 1.00 | 2.00 |" in text    # gaps
+    assert "| 28.50 | 25.50 |" in text  # first start to last end
+    assert "17.80" in text              # the fill run alone
+
+
+def test_grandk_summary_needs_the_trace(tmp_path):
+    sys.path.insert(0, str(ROOT))
+    import bench
+    assert bench.summarize_grandk_path(tmp_path) is None
