@@ -178,6 +178,21 @@ def _read_counters(path: pathlib.Path):
     return per
 
 
+def copy_calibration(d: pathlib.Path):
+    """(FETCH scale, WRITE scale, copy kernel, FETCH KiB, WRITE KiB) from the
+    1 GiB device copy of --calibrate-copy: bytes = counter KiB x 1024 x
+    scale. None without the two calibration passes."""
+    if not (d / "pmc_cal_fetch").exists() or not (d / "pmc_cal_write").exists():
+        return None
+    cal_f = _read_counters(next((d / "pmc_cal_fetch").glob("*counter_collection.csv")))
+    cal_w = _read_counters(next((d / "pmc_cal_write").glob("*counter_collection.csv")))
+    copy_name = max(cal_w, key=lambda k: sum(cal_w[k]))
+    copy_bytes = 4 << 28
+    f_kib = sum(cal_f[copy_name]) / len(cal_f[copy_name])
+    w_kib = sum(cal_w[copy_name]) / len(cal_w[copy_name])
+    return copy_bytes / (f_kib * 1024), copy_bytes / (w_kib * 1024), copy_name, f_kib, w_kib
+
+
 def _read_counters_by_name(path: pathlib.Path):
     """{kernel: {counter: [value per dispatch]}} from a rocprofv3 counter CSV."""
     import csv
@@ -393,6 +408,7 @@ def summarize_grandk_path(d: pathlib.Path) -> pathlib.Path | None:
     if fill_floor:
         lines += [f"Fill floor: {4 * n:,} B at the measured write ceiling "
                   f"({ceil_gbs:,.0f} GB/s, `profiles/hbm_ceilings.md`) = {fill_floor:.1f} us.", ""]
+    lines += grandk_traffic_lines(d, names, n)
     lines += [
         "Reading:",
         "",
@@ -409,6 +425,55 @@ def summarize_grandk_path(d: pathlib.Path) -> pathlib.Path | None:
     ]
     PROFILE_GRANDK.write_text("\n".join(lines))
     return PROFILE_GRANDK
+
+
+def grandk_traffic_lines(d: pathlib.Path, names, n: int) -> list:
+    """HBM bytes of each launch of the full-size GlobalRandK step from the
+    FETCH_SIZE and WRITE_SIZE passes over the extras run, calibrated on the
+    device copy; [] without those passes."""
+    import csv
+    cal = copy_calibration(d)
+    if cal is None or not (d / "pmc_fetch_extra").exists() or not (d / "pmc_write_extra").exists():
+        return []
+    f_scale, w_scale = cal[0], cal[1]
+
+    def per_launch(sub, scale):
+        rows = sorted(csv.DictReader(open(next((d / sub).glob("*counter_collection.csv")))),
+                      key=lambda r: int(r["Dispatch_Id"]))
+        rows = [r for r in rows if r["Kernel_Name"].startswith(names)]
+        steps = [rows[i:i + 3] for i in range(len(rows) - 2)
+                 if all(rows[i + j]["Kernel_Name"].startswith(names[j]) for j in range(3))]
+        if not steps:
+            return None
+        big = max(int(t[0]["Grid_Size"]) for t in steps)
+        steps = [t for t in steps if int(t[0]["Grid_Size"]) == big]
+        return [statistics.median(float(t[j]["Counter_Value"]) for t in steps) * 1024 * scale
+                for j in range(3)], len(steps)
+
+    f, w = per_launch("pmc_fetch_extra", f_scale), per_launch("pmc_write_extra", w_scale)
+    if not f or not w:
+        return []
+    (fb, nf), (wb, nw) = f, w
+    tot = sum(fb) + sum(wb)
+    out = [
+        f"HBM bytes of the full-size step (medians over {min(nf, nw)} steps; one counter per "
+        "run, calibrated on a 1 GiB device copy):",
+        "",
+        f"    {PROFILE_COMMANDS['fetch_extra']}",
+        f"    {PROFILE_COMMANDS['write_extra']}",
+        "",
+        "| launch | read (FETCH_SIZE) | written (WRITE_SIZE) |",
+        "|---|---|---|",
+    ]
+    for j in range(3):
+        out.append(f"| {j + 1} `{names[j]}` | {fb[j]:,.0f} B | {wb[j]:,.0f} B |")
+    K, W = 10_000, W_C2
+    out += [f"| step | {sum(fb):,.0f} B | {sum(wb):,.0f} B |", "",
+            f"The step moves {tot:,.0f} B, {tot / (4 * n):.3f}x its {4 * n:,} B of dense "
+            f"output. Nearly all the reads are launch 2's gathers: W x K = {W * K:,} random "
+            f"4-byte values, each costing a 128-byte line ({W * K * 128:,} B). The writes "
+            "are the dense output, the gathered values and the scattered lines.", ""]
+    return out
 
 
 def summarize_profiles(out_dir: str) -> None:
@@ -435,14 +500,8 @@ def summarize_profiles(out_dir: str) -> None:
         "qsgd_dequant_sum_kernel": (W3 * n3, 8 * n3),
         "qsgd_quantize_sum_kernel": (4 * W3 * n3, 8 * n3),
     }
-    cal_f = _read_counters(next((d / "pmc_cal_fetch").glob("*counter_collection.csv")))
-    cal_w = _read_counters(next((d / "pmc_cal_write").glob("*counter_collection.csv")))
-    copy_name = max(cal_w, key=lambda k: sum(cal_w[k]))
+    f_scale, w_scale, copy_name, f_kib, w_kib = copy_calibration(d)
     copy_bytes = 4 << 28
-    f_kib = sum(cal_f[copy_name]) / len(cal_f[copy_name])
-    w_kib = sum(cal_w[copy_name]) / len(cal_w[copy_name])
-    f_scale = copy_bytes / (f_kib * 1024)
-    w_scale = copy_bytes / (w_kib * 1024)
     fetch = _read_counters(next((d / "pmc_fetch").glob("*counter_collection.csv")))
     write = _read_counters(next((d / "pmc_write").glob("*counter_collection.csv")))
     sizes = [int(v) for v in __import__("synthetic_inputs").bert_base_sizes()]
