@@ -138,14 +138,16 @@ def kernel_source_hash(sources=None) -> str:
     return h.hexdigest()
 
 
-def traffic_from_profile(kernel: str) -> int | None:
+def traffic_from_profile(kernel: str, profile: pathlib.Path | None = None,
+                         key: str = "traffic_bytes_per_launch") -> int | None:
     """HBM bytes per launch of `kernel` measured with rocprofv3 counters, if
     the committed measurement was taken on the current kernel sources."""
-    if not PROFILE_TRAFFIC.exists():
+    profile = profile or PROFILE_TRAFFIC
+    if not profile.exists():
         return None
-    text = PROFILE_TRAFFIC.read_text()
+    text = profile.read_text()
     m_h = re.search(r"^kernel_source_sha256:\s*([0-9a-f]+)", text, re.M)
-    m_b = re.search(rf"^traffic_bytes_per_launch\[{kernel}\]:\s*([0-9]+)", text, re.M)
+    m_b = re.search(rf"^{key}\[{kernel}\]:\s*([0-9]+)", text, re.M)
     if not (m_b and m_h) or m_h.group(1) != kernel_source_hash():
         return None
     return int(m_b.group(1))
@@ -472,7 +474,10 @@ def grandk_traffic_lines(d: pathlib.Path, names, n: int) -> list:
             f"The step moves {tot:,.0f} B, {tot / (4 * n):.3f}x its {4 * n:,} B of dense "
             f"output. Nearly all the reads are launch 2's gathers: W x K = {W * K:,} random "
             f"4-byte values, each costing a 128-byte line ({W * K * 128:,} B). The writes "
-            "are the dense output, the gathered values and the scattered lines.", ""]
+            "are the dense output, the gathered values and the scattered lines.", "",
+            "Machine-readable (bench.py reads this while the kernel sources are unchanged):", "",
+            f"kernel_source_sha256: {kernel_source_hash()}",
+            f"traffic_bytes_per_step[grandk_mn_step]: {int(round(tot))}", ""]
     return out
 
 
@@ -1313,7 +1318,9 @@ def bench_grandk(gcq, torch, np, si, steps: int):
             "roofline": {"bound": "hbm",
                          "kernel": "grandk_mn_step, whole step (dense output written once)",
                          "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+                         "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_from_profile("grandk_mn_step", PROFILE_GRANDK,
+                                                         "traffic_bytes_per_step")},
             "oracle_ms_per_step": None, "steps": steps}
 
 
