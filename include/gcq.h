@@ -50,7 +50,7 @@ typedef enum gc_status {
     GC_OK = 0,
     GC_EINVAL = -1,       /* bad argument; nothing enqueued */
     GC_EHIP = -2,         /* a HIP call or kernel launch failed */
-    GC_EUNSUPPORTED = -3  /* valid request outside what this build supports */
+    GC_EUNSUPPORTED = -3  /* valid request outside what the library supports */
 } gc_status;
 
 /* Largest number of simulated workers a single call combines. */
