@@ -269,3 +269,22 @@ def test_error_message_is_per_thread(lib):
     size = ctypes.c_size_t(0)
     assert lib.grandk_indices(100, 10, 0, NULL, NULL, ctypes.byref(size), None) == gcq.GC_OK
     assert lib.gc_last_error() == b""
+
+
+def test_abi_client_finds_its_libraries_relative_to_itself():
+    """tests/_bin/abi_client (the C-ABI client the GPU suite runs) needs
+    libgcq.so and liboracle.so by name and finds them through a RUNPATH
+    relative to its own location, so the built tree can move to another
+    machine."""
+    import abi_client_build as acb
+    if not acb.BIN.exists():
+        pytest.fail(f"{acb.BIN} is not built: run python tests/abi_client_build.py (or build())")
+    out = subprocess.run(["readelf", "-d", str(acb.BIN)], capture_output=True, text=True,
+                         check=True).stdout
+    needed = set(re.findall(r"\(NEEDED\)\s+Shared library: \[([^\]]+)\]", out))
+    assert {"libgcq.so", "liboracle.so"} <= needed
+    runpath = re.search(r"\((?:RUNPATH|RPATH)\)\s+Library (?:runpath|rpath): \[([^\]]+)\]", out)
+    assert runpath, out
+    parts = runpath.group(1).split(":")
+    assert "$ORIGIN/../../gradient_compression_quantize_amd" in parts
+    assert "$ORIGIN/../../oracle" in parts
