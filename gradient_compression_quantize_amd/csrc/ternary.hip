@@ -321,7 +321,8 @@ __device__ __forceinline__ void decode_element(uint32_t word, const float2* t,
 
 // One full wave tile of the W-block dequantize-and-sum. WC > 0: W == WC at
 // compile time, every worker's element in flight at once; WC == 0: W read at
-// run time, in groups of four. `stage` is this wave's kTileF4-float4 buffer.
+// run time, in groups of eight, the next group's loads ahead of this one's
+// decode. `stage` is this wave's kTileF4-float4 buffer.
 // kDword: out without 16-byte alignment; the staged tile leaves as
 // lane-contiguous 4-byte stores.
 // pre: this lane's W elements, already loaded (WC > 0), or NULL to load them
@@ -335,22 +336,38 @@ __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& t
     const int W = WC > 0 ? WC : W_rt;
     const size_t j = q0 / kSlots + lane;
     float acc[kWordValues];
-    constexpr int kGroup = WC > 0 ? WC : 4;
-    for (int w0 = 0; w0 < W; w0 += kGroup) {
-        uint32_t mine[kGroup];
+    if constexpr (WC > 0) {
+        // every worker's element in flight together
+        uint32_t mine[WC];
 #pragma unroll
-        for (int dw = 0; dw < kGroup; ++dw) {
-            mine[dw] = (WC == 0 && w0 + dw >= W)
-                           ? 0u
-                           : (pre ? pre[w0 + dw]
-                                  : __builtin_nontemporal_load(tab.p[w0 + dw] + 3 + j));
-        }
+        for (int w = 0; w < WC; ++w)
+            mine[w] = pre ? pre[w] : __builtin_nontemporal_load(tab.p[w] + 3 + j);
 #pragma unroll
-        for (int dw = 0; dw < kGroup; ++dw) {
-            const int w = w0 + dw;
-            if (WC == 0 && w >= W)
-                break;
-            decode_element(mine[dw], lut + 16 * w, acc, w == 0);
+        for (int w = 0; w < WC; ++w)
+            decode_element(mine[w], lut + 16 * w, acc, w == 0);
+    } else {
+        // W at run time: groups of kGroup workers, the next group's elements
+        // loaded before this group is decoded (two groups in flight)
+        constexpr int kGroup = 8;
+        auto load = [&](uint32_t(&dst)[kGroup], int w0) {
+#pragma unroll
+            for (int dw = 0; dw < kGroup; ++dw)
+                dst[dw] = w0 + dw < W ? __builtin_nontemporal_load(tab.p[w0 + dw] + 3 + j) : 0u;
+        };
+        uint32_t cur[kGroup], nxt[kGroup];
+        load(cur, 0);
+        for (int w0 = 0; w0 < W; w0 += kGroup) {
+            if (w0 + kGroup < W)
+                load(nxt, w0 + kGroup);
+#pragma unroll
+            for (int dw = 0; dw < kGroup; ++dw) {
+                if (w0 + dw >= W)
+                    break;
+                decode_element(cur[dw], lut + 16 * (w0 + dw), acc, w0 + dw == 0);
+            }
+#pragma unroll
+            for (int dw = 0; dw < kGroup; ++dw)
+                cur[dw] = nxt[dw];
         }
     }
     // lane L holds values 20L .. 20L+19 of the tile = float4 slots 5L .. 5L+4

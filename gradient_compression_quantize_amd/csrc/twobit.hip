@@ -286,7 +286,8 @@ __global__ __launch_bounds__(kThreads) void compress_2bit_dword_kernel(
 // lane the word of its float4 slot (word 16u + L/4 for slot u), so no word
 // is fetched from memory twice. Decoding goes through the LDS nibble table.
 // WC > 0: W == WC is known at compile time, so every worker's word is loaded
-// before any is decoded; WC == 0: W read at run time, in groups of four.
+// before any is decoded; WC == 0: W read at run time, in groups of eight,
+// the next group's loads ahead of this one's decode.
 // kDword: out without 16-byte alignment. The tile's float4 slots go to the
 // wave's LDS stage and leave as lane-contiguous 4-byte stores.
 // pre: this lane's W words, already loaded (WC > 0), or NULL to load them here.
@@ -302,18 +303,10 @@ __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& t
     const uint32_t shift = 24u - 8u * uint32_t(lane & 3);
     f32x4* o4 = reinterpret_cast<f32x4*>(out);
     f32x4 acc[kUnroll];
-    constexpr int kGroup = WC > 0 ? WC : 4;  // workers whose words are in flight together
-    for (int w0 = 0; w0 < W; w0 += kGroup) {
-        uint32_t mine[kGroup];
+    // Adds workers w0 .. w0 + G - 1 (those below W) of `words` into acc.
+    auto decode = [&](const uint32_t* words, int w0, int G) {
 #pragma unroll
-        for (int dw = 0; dw < kGroup; ++dw) {
-            mine[dw] = (WC == 0 && w0 + dw >= W)
-                           ? 0u
-                           : (pre ? pre[w0 + dw]
-                                  : __builtin_nontemporal_load(tab.p[w0 + dw] + 3 + jmine));
-        }
-#pragma unroll
-        for (int dw = 0; dw < kGroup; ++dw) {
+        for (int dw = 0; dw < G; ++dw) {
             const int w = w0 + dw;
             if (WC == 0 && w >= W)
                 break;
@@ -322,13 +315,40 @@ __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& t
             for (int u = 0; u < kUnroll; ++u) {
                 // all 64 lanes take part: lane 16u + L/4 holds this slot's word
                 const uint32_t word = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(
-                    (16 * u + (lane >> 2)) * 4, static_cast<int>(mine[dw])));
+                    (16 * u + (lane >> 2)) * 4, static_cast<int>(words[dw])));
                 const uint32_t byte = (word >> shift) & 0xFFu;
                 const float2 hi = t[byte >> 4];
                 const float2 lo = t[byte & 15u];
                 const f32x4 d = {hi.x, hi.y, lo.x, lo.y};
                 acc[u] = (w == 0) ? d : acc[u] + d;
             }
+        }
+    };
+    if constexpr (WC > 0) {
+        // every worker's word in flight together
+        uint32_t mine[WC];
+#pragma unroll
+        for (int w = 0; w < WC; ++w)
+            mine[w] = pre ? pre[w] : __builtin_nontemporal_load(tab.p[w] + 3 + jmine);
+        decode(mine, 0, WC);
+    } else {
+        // W at run time: groups of kGroup workers, the next group's words
+        // loaded before this group is decoded (two groups in flight)
+        constexpr int kGroup = 8;
+        auto load = [&](uint32_t(&dst)[kGroup], int w0) {
+#pragma unroll
+            for (int dw = 0; dw < kGroup; ++dw)
+                dst[dw] = w0 + dw < W ? __builtin_nontemporal_load(tab.p[w0 + dw] + 3 + jmine) : 0u;
+        };
+        uint32_t cur[kGroup], nxt[kGroup];
+        load(cur, 0);
+        for (int w0 = 0; w0 < W; w0 += kGroup) {
+            if (w0 + kGroup < W)
+                load(nxt, w0 + kGroup);
+            decode(cur, w0, kGroup);
+#pragma unroll
+            for (int dw = 0; dw < kGroup; ++dw)
+                cur[dw] = nxt[dw];
         }
     }
     if (kDword) {
