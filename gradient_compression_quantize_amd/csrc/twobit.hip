@@ -286,8 +286,8 @@ __global__ __launch_bounds__(kThreads) void compress_2bit_dword_kernel(
 // lane the word of its float4 slot (word 16u + L/4 for slot u), so no word
 // is fetched from memory twice. Decoding goes through the LDS nibble table.
 // WC > 0: W == WC is known at compile time, so every worker's word is loaded
-// before any is decoded; WC == 0: W read at run time, in groups of eight,
-// the next group's loads ahead of this one's decode.
+// before any is decoded; WC == 0: W read at run time, each lane decoding its
+// own word (see the branch below).
 // kDword: out without 16-byte alignment. The tile's float4 slots go to the
 // wave's LDS stage and leave as lane-contiguous 4-byte stores.
 // pre: this lane's W words, already loaded (WC > 0), or NULL to load them here.
@@ -332,24 +332,54 @@ __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& t
             mine[w] = pre ? pre[w] : __builtin_nontemporal_load(tab.p[w] + 3 + jmine);
         decode(mine, 0, WC);
     } else {
-        // W at run time: groups of kGroup workers, the next group's words
-        // loaded before this group is decoded (two groups in flight)
+        // W at run time. Every lane decodes its own word of each worker (16
+        // values, float4 slots 4L .. 4L+3 of the tile): no ds_bpermute per
+        // worker, which at large W costs more than the table reads. Workers
+        // go in groups of kGroup, the next group's words loaded before this
+        // group is decoded; the tile then leaves through the wave's LDS
+        // stage as lane-contiguous stores.
         constexpr int kGroup = 8;
         auto load = [&](uint32_t(&dst)[kGroup], int w0) {
 #pragma unroll
             for (int dw = 0; dw < kGroup; ++dw)
                 dst[dw] = w0 + dw < W ? __builtin_nontemporal_load(tab.p[w0 + dw] + 3 + jmine) : 0u;
         };
+        float v16[16];
         uint32_t cur[kGroup], nxt[kGroup];
         load(cur, 0);
         for (int w0 = 0; w0 < W; w0 += kGroup) {
             if (w0 + kGroup < W)
                 load(nxt, w0 + kGroup);
-            decode(cur, w0, kGroup);
+#pragma unroll
+            for (int dw = 0; dw < kGroup; ++dw) {
+                const int w = w0 + dw;
+                if (w >= W)
+                    break;
+                const float2* t = lut + 16 * w;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t byte = (cur[dw] >> (24 - 8 * b)) & 0xFFu;
+                    const float2 hi = t[byte >> 4];
+                    const float2 lo = t[byte & 15u];
+                    const float d[4] = {hi.x, hi.y, lo.x, lo.y};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        v16[4 * b + k] = (w == 0) ? d[k] : v16[4 * b + k] + d[k];
+                }
+            }
 #pragma unroll
             for (int dw = 0; dw < kGroup; ++dw)
                 cur[dw] = nxt[dw];
         }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            stage[4 * lane + k] = f32x4{v16[4 * k], v16[4 * k + 1], v16[4 * k + 2], v16[4 * k + 3]};
+        wave_lds_sync();
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            acc[u] = stage[u * kWave + lane];
+        if (kDword)
+            wave_lds_sync();  // the staged reads below start from these same slots
     }
     if (kDword) {
 #pragma unroll
@@ -415,7 +445,10 @@ __device__ __forceinline__ void decompress_2bit_body(const PtrTable<uint32_t>& t
                                                      float* __restrict__ out, size_t ntiles)
 {
     __shared__ float2 lut[16 * GC_MAX_WORKERS];
-    __shared__ f32x4 stage[kDword ? kWavesPerBlock : 1][kDword ? kTileF4 : 1];
+    // the wave's stage: output transposes for 4-byte-aligned out, and the
+    // run-time-W decode's hand-over from word order to store order
+    constexpr bool kStage = kDword || WC == 0;
+    __shared__ f32x4 stage[kStage ? kWavesPerBlock : 1][kStage ? kTileF4 : 1];
     const int lane = threadIdx.x & (kWave - 1);
     if (!kLoop && WC > 0) {
         // One tile per wave, W known: the tile's word loads go out before
@@ -433,7 +466,7 @@ __device__ __forceinline__ void decompress_2bit_body(const PtrTable<uint32_t>& t
         build_nibble_table(lut, tab, WC);
         if (full)
             decompress_full_tile<WC, kAcc, kDword>(tab, W, lut, out, q0, lane,
-                                                   stage[kDword ? threadIdx.x / kWave : 0], pre);
+                                                   stage[kStage ? threadIdx.x / kWave : 0], pre);
         else if (t < ntiles)
             decompress_tail_tile(tab, WC, lut, n, out, kAcc ? 1 : 0, q0, lane);
         return;
@@ -451,7 +484,7 @@ __device__ __forceinline__ void decompress_2bit_body(const PtrTable<uint32_t>& t
         const size_t q0 = (ntiles - 1 - t) * kTileF4;
         if (q0 + kTileF4 <= (n >> 2))
             decompress_full_tile<WC, kAcc, kDword>(tab, W, lut, out, q0, lane,
-                                                   stage[kDword ? threadIdx.x / kWave : 0]);
+                                                   stage[kStage ? threadIdx.x / kWave : 0]);
         else
             decompress_tail_tile(tab, WC > 0 ? WC : W, lut, n, out, kAcc ? 1 : 0, q0, lane);
         if (!kLoop)
