@@ -185,7 +185,7 @@ def test_workers_on_concurrent_streams(gcq):
     np.testing.assert_array_equal(gu.host(out), oracle.dequantize_2bit_sum(c_or, n))
 
 
-@pytest.mark.parametrize("W", [1, 2, 3, 8, 64])
+@pytest.mark.parametrize("W", [1, 2, 3, 8, 9, 13, 16, 17, 33, 64])
 @pytest.mark.parametrize("n", [1, 17, 1000, 4097, 100_003])
 def test_dequantize_sum(gcq, W, n):
     announce(f"2-bit dequantize-sum W={W} n={n}")

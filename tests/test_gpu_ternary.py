@@ -141,7 +141,7 @@ def test_every_byte_value_decodes_like_the_oracle(gcq):
         np.testing.assert_array_equal(gu.host(out), expect)
 
 
-@pytest.mark.parametrize("W", [1, 2, 3, 8, 9, 64])
+@pytest.mark.parametrize("W", [1, 2, 3, 8, 9, 13, 16, 17, 33, 64])
 @pytest.mark.parametrize("n", [1, 17, 1000, 1281, 5121, 100_003])
 def test_dequantize_sum(gcq, W, n):
     announce(f"ternary dequantize-sum W={W} n={n}")
