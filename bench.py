@@ -1050,6 +1050,54 @@ def bench_ternary(gcq, torch, np, si, steps: int):
             "oracle_ms": None, "steps": steps}
 
 
+def bench_many_workers(gcq, torch, steps: int):
+    """The W-block dequantize-sums at the ResNet-50 size for W above the
+    compile-time range (16 and 64 workers: the run-time-W kernels), on
+    random-bit blocks with thresholds +-0.5, rotating over block sets of at
+    least 1 GB."""
+    n = N_C2
+    out = {"workload": f"decompress_2bit_sum and decompress_ternary_sum, n = {n:,}, random "
+                       "payload bits, W = 16 and 64",
+           "steps": steps}
+    mk = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    for tag, words_of, fn in (("2bit", gcq.gc_compressed_2bit_words, gcq.decompress_2bit_sum),
+                              ("ternary", gcq.gc_compressed_ternary_words,
+                               gcq.decompress_ternary_sum)):
+        for W in (16, 64):
+            log(f"many workers: {tag} W={W}")
+            nw = words_of(n)
+            R = max(2, -(-(1 << 30) // (W * nw * 4)))
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(7 * W)
+            sets = []
+            for _ in range(R):
+                bl = []
+                for _ in range(W):
+                    b = torch.randint(-2 ** 31, 2 ** 31 - 1, (nw,), dtype=torch.int32,
+                                      device="cuda", generator=gen)
+                    b[0], b[1], b[2] = -0x41000000, 0x3F000000, 0  # -0.5, 0.5 as fp32 bits
+                    bl.append(b)
+                sets.append(bl)
+            dst = [torch.empty(n, device="cuda") for _ in range(2)]
+            for r in range(R):
+                fn(sets[r], n, dst[r % 2])
+            torch.cuda.synchronize()
+            reps = max(steps, 2 * R)
+            a, b = mk(), mk()
+            a.record()
+            for k in range(reps):
+                fn(sets[k % R], n, dst[k % 2])
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / reps
+            nbytes = W * 4 * nw + 4 * n
+            out[f"{tag}_w{W}"] = {"ms": round(ms, 5), "bytes": nbytes,
+                                  "gbs": round(nbytes / (ms / 1e3) / 1e9, 1)}
+            del sets, dst
+            torch.cuda.empty_cache()
+    return out
+
+
 def bench_misaligned(gcq, torch, si, steps: int):
     """The 2-bit and ternary kernels on buffers 4 bytes off 16-byte alignment
     (views at element offset 1, as inside a flat bucket of odd-sized
@@ -1502,7 +1550,8 @@ def main() -> int:
         print(json.dumps({"multi_tensor": bench_multi(gcq, torch, np, si, args.extra_steps),
                           "grandk_mn": bench_grandk(gcq, torch, np, si, args.extra_steps),
                           "ternary": bench_ternary(gcq, torch, np, si, args.extra_steps),
-                          "misaligned": bench_misaligned(gcq, torch, si, args.extra_steps)}),
+                          "misaligned": bench_misaligned(gcq, torch, si, args.extra_steps),
+                          "many_workers": bench_many_workers(gcq, torch, args.extra_steps)}),
               flush=True)
         return 0
 
@@ -1574,6 +1623,7 @@ def main() -> int:
         result["grandk_mn"] = bench_grandk(gcq, torch, np, si, args.extra_steps)
         result["ternary"] = bench_ternary(gcq, torch, np, si, args.extra_steps)
         result["misaligned"] = bench_misaligned(gcq, torch, si, args.extra_steps)
+        result["many_workers"] = bench_many_workers(gcq, torch, args.extra_steps)
 
     if not args.skip_ceilings:
         ceil = measure_ceilings(torch, args.ceiling_steps)
