@@ -601,7 +601,7 @@ def summarize_profiles(out_dir: str) -> None:
         stats = list(csv.DictReader(open(extra[0])))
         lines = [
             "# Kernel durations from rocprofv3: many-tensor compress, GlobalRandK, ternary, "
-            "misaligned buffers",
+            "misaligned buffers, many workers",
             "",
             "Command (repo root):",
             "",
@@ -617,7 +617,11 @@ def summarize_profiles(out_dir: str) -> None:
             "buffers: the 2-bit and ternary compress and W = 8 dequantize-sum at the "
             "ResNet-50 size, and the QSGD-MN max-norm, quantize, level sum and fused "
             "quantize-sum at the VGG16 size, each on buffers 4 bytes off 16-byte alignment "
-            "(the *_dword_kernel rows) and on aligned buffers.",
+            "(the *_dword_kernel rows) and on aligned buffers. Many workers: the 2-bit and "
+            "ternary dequantize-sums at W = 16 and 64 (the run-time-W kernels) at the "
+            "ResNet-50 size. GlobalRandK also runs at n = 1,048,576 (the chain alone), and "
+            "the W = 8 dequantize-sum rows mix the workloads above, so their averages are "
+            "not one workload's.",
             "",
             "| kernel | calls | average us | min us | max us | share of GPU time |",
             "|---|---|---|---|---|---|",
