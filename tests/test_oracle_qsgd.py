@@ -251,6 +251,25 @@ def test_randk_prefix_property():
     np.testing.assert_array_equal(a, b[:500])
 
 
+@pytest.mark.parametrize("n,K,seed", [(1, 1, 0), (2, 2, 5), (7, 7, 11), (50, 13, 12345),
+                                      (300, 300, 2 ** 40 + 7), (1000, 37, 2 ** 63 + 1)])
+def test_randk_matches_an_explicit_fisher_yates(n, K, seed):
+    """Brute force on a materialised permutation: step i draws
+    j = i + floor(R (n - i) / 2^64) from Philox words (w0, w1) of counter
+    (i, 0, 0, 1), swaps positions i and j of a plain list, and takes the
+    value now at position i. The oracle tracks only displaced entries; this
+    walks the whole list."""
+    perm = list(range(n))
+    key = [seed & 0xFFFFFFFF, seed >> 32]
+    for i in range(K):
+        w = oracle.philox4x32_10([i, 0, 0, 1], key)
+        R = (int(w[1]) << 32) | int(w[0])
+        j = i + ((R * (n - i)) >> 64)
+        perm[i], perm[j] = perm[j], perm[i]
+    np.testing.assert_array_equal(oracle.randk_indices(n, K, seed),
+                                  np.array(perm[:K], dtype=np.uint32))
+
+
 def test_randk_rejects_k_above_n():
     with pytest.raises(ValueError):
         oracle.randk_indices(10, 11, 0)
