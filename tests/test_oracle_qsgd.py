@@ -213,6 +213,58 @@ def test_dequantize_within_two_roundings(s):
         assert err <= abs(exact) * Fraction(1, 2 ** 23), (k, int(S[k]))
 
 
+def _round_f32(x: Fraction) -> Fraction:
+    """x rounded to the nearest binary32 value, ties to even (normal range
+    and zero; the values below stay far from overflow and underflow)."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    assert Fraction(2) ** e <= a < Fraction(2) ** (e + 1)
+    ulp = Fraction(2) ** (e - 23)
+    m = a / ulp                      # in [2^23, 2^24)
+    q, r = divmod(m.numerator, m.denominator)
+    twice = 2 * r
+    if twice > m.denominator or (twice == m.denominator and q % 2 == 1):
+        q += 1
+    return sign * q * ulp
+
+
+def test_round_f32_helper_matches_numpy_on_doubles():
+    """The rounding helper agrees with numpy's (correctly rounded) float64 ->
+    float32 conversion, halfway cases included."""
+    rng = np.random.default_rng(61)
+    xs = list(rng.standard_normal(2000) * 10.0 ** rng.integers(-20, 20, 2000))
+    # exact halfway points between neighbouring binary32 values, both parities
+    for m in (1, 2, 3, 1 << 22, (1 << 23) - 1):
+        xs += [(2 ** 23 + m + 0.5) * 2.0 ** -23, -(2 ** 23 + m + 0.5) * 2.0 ** -30]
+    for x in xs:
+        assert _round_f32(Fraction(x)) == Fraction(float(np.float32(x))), x
+
+
+@pytest.mark.parametrize("s", [7, 127])
+def test_dequantize_is_the_product_rounded_then_the_quotient_rounded(s):
+    """out = fl(fl(norm * S) / s), from exact rationals: each step rounded
+    once to binary32 in that order. The other order, fl(norm * fl(S / s)),
+    differs on some of these inputs, so the check tells the two apart."""
+    rng = np.random.default_rng(60 + s)
+    S = rng.integers(-8 * s, 8 * s + 1, 3000).astype(np.int32)
+    norms = [np.float32(v) for v in (0.8234567, 3.0e-3, 17.25, 1.1e-7)]
+    other_order_differs = False
+    for norm in norms:
+        out = oracle.qsgd_dequantize(S, norm, s)
+        fn = Fraction(float(norm))
+        for k in range(S.size):
+            want = _round_f32(_round_f32(fn * int(S[k])) / s)
+            assert Fraction(float(out[k])) == want, (float(norm), int(S[k]))
+            alt = _round_f32(fn * _round_f32(Fraction(int(S[k]), s)))
+            other_order_differs |= alt != want
+    assert other_order_differs
+
+
 # ----------------------------------------------------------- rand-K ----
 
 def test_randk_tiny_uniform_over_ordered_pairs():
