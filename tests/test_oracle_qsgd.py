@@ -306,11 +306,12 @@ def test_randk_prefix_property():
 @pytest.mark.parametrize("n,K,seed", [(1, 1, 0), (2, 2, 5), (7, 7, 11), (50, 13, 12345),
                                       (300, 300, 2 ** 40 + 7), (1000, 37, 2 ** 63 + 1)])
 def test_randk_matches_an_explicit_fisher_yates(n, K, seed):
-    """Brute force on a materialised permutation: step i draws
-    j = i + floor(R (n - i) / 2^64) from Philox words (w0, w1) of counter
-    (i, 0, 0, 1), swaps positions i and j of a plain list, and takes the
-    value now at position i. The oracle tracks only displaced entries; this
-    walks the whole list."""
+    """The draw's definition restated with Python integers and a list:
+    step i draws j = i + floor(R (n - i) / 2^64) from Philox words (w0, w1)
+    of counter (i, 0, 0, 1), swaps positions i and j, and takes the value now
+    at position i. A consistency check of the C arithmetic (the 128-bit
+    product, 32-bit counters, 64-bit seeds split into the key), not an
+    independent pin: the uniformity tests above are those."""
     perm = list(range(n))
     key = [seed & 0xFFFFFFFF, seed >> 32]
     for i in range(K):
