@@ -73,6 +73,10 @@ MUTANTS = [
     ("sum_drops_term", "for (int w = 0; w < W; ++w)\n            acc += (int32_t)levels[w][i];",
      "for (int w = 1; w < W; ++w)\n            acc += (int32_t)levels[w][i];", TQ),
     ("deq_times_s", "out[i] = t / (float)s;", "out[i] = t * (float)s;", TQ),
+    ("deq_other_order", "float t = norm * (float)sums[i];\n        out[i] = t / (float)s;",
+     "float t = (float)sums[i] / (float)s;\n        out[i] = norm * t;", TQ),
+    ("deq_in_fp64", "float t = norm * (float)sums[i];\n        out[i] = t / (float)s;",
+     "double t = (double)norm * (double)sums[i];\n        out[i] = (float)(t / (double)s);", TQ),
     ("randk_range_n", "uint64_t range = (uint64_t)(n - i);", "uint64_t range = (uint64_t)n;", TQ),
     ("randk_takes_j", "idx[i] = perm[i];", "idx[i] = perm[j];", TQ),
     ("randk_low_word_only", "uint64_t R = ((uint64_t)r[1] << 32) | (uint64_t)r[0];",
