@@ -319,6 +319,41 @@ __device__ __forceinline__ void decode_element(uint32_t word, const float2* t,
     }
 }
 
+// Byte offsets into a worker's pair table of the byte's two pairs and its
+// single digit, packed (8 p0 | 8 p1 << 8 | 24 c4 << 16): the digit split of
+// decode_element done once per byte value instead of once per byte read.
+__host__ __device__ constexpr uint32_t packed_digit_offsets(uint32_t x)
+{
+    const Digits d = split_byte(x);
+    return (8u * d.p0) | ((8u * d.p1) << 8) | ((24u * d.c4) << 16);
+}
+
+__device__ __forceinline__ void build_digit_table(uint32_t* offs)
+{
+    for (uint32_t x = threadIdx.x; x < 256u; x += blockDim.x)
+        offs[x] = packed_digit_offsets(x);
+}
+
+// decode_element with the digit split read from the table of
+// packed_digit_offsets.
+__device__ __forceinline__ void decode_element_tab(uint32_t word, const float2* t,
+                                                   const uint32_t* offs,
+                                                   float (&acc)[kWordValues], bool first)
+{
+    const char* tb = reinterpret_cast<const char*>(t);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t o = offs[(word >> (8 * b)) & 0xFFu];
+        const float2 q0 = *reinterpret_cast<const float2*>(tb + (o & 0xFFu));
+        const float2 q1 = *reinterpret_cast<const float2*>(tb + ((o >> 8) & 0xFFu));
+        const float s = *reinterpret_cast<const float*>(tb + (o >> 16));
+        const float v[5] = {q0.x, q0.y, q1.x, q1.y, s};
+#pragma unroll
+        for (int k = 0; k < 5; ++k)
+            acc[5 * b + k] = first ? v[k] : acc[5 * b + k] + v[k];
+    }
+}
+
 // One full wave tile of the W-block dequantize-and-sum. WC > 0: W == WC at
 // compile time, every worker's element in flight at once; WC == 0: W read at
 // run time, in groups of eight, the next group's loads ahead of this one's
@@ -331,7 +366,8 @@ template <int WC, bool kAcc, bool kDword>
 __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& tab, int W_rt,
                                                      const float2* lut, float* __restrict__ out,
                                                      size_t q0, int lane, f32x4* stage,
-                                                     const uint32_t* pre = nullptr)
+                                                     const uint32_t* pre = nullptr,
+                                                     const uint32_t* offs = nullptr)
 {
     const int W = WC > 0 ? WC : W_rt;
     const size_t j = q0 / kSlots + lane;
@@ -363,7 +399,7 @@ __device__ __forceinline__ void decompress_full_tile(const PtrTable<uint32_t>& t
             for (int dw = 0; dw < kGroup; ++dw) {
                 if (w0 + dw >= W)
                     break;
-                decode_element(cur[dw], lut + 16 * (w0 + dw), acc, w0 + dw == 0);
+                decode_element_tab(cur[dw], lut + 16 * (w0 + dw), offs, acc, w0 + dw == 0);
             }
 #pragma unroll
             for (int dw = 0; dw < kGroup; ++dw)
@@ -458,13 +494,17 @@ __device__ __forceinline__ void decompress_ternary_body(const PtrTable<uint32_t>
             decompress_tail_tile(tab, WC, lut, n, out, kAcc ? 1 : 0, q0, lane);
         return;
     }
+    __shared__ uint32_t offs[WC == 0 ? 256 : 1];
+    if (WC == 0)
+        build_digit_table(offs);  // the barrier in build_pair_table covers it
     build_pair_table(lut, tab, WC > 0 ? WC : W);
     const size_t stride = size_t(gridDim.x) * kWavesPerBlock;
     const size_t blk = kLoop ? blockIdx.x : xcd_contiguous(blockIdx.x, gridDim.x);
     for (size_t t = blk * kWavesPerBlock + wave; t < ntiles; t += stride) {
         const size_t q0 = (ntiles - 1 - t) * kTileF4;
         if (q0 + kTileF4 <= (n >> 2))
-            decompress_full_tile<WC, kAcc, kDword>(tab, W, lut, out, q0, lane, stage[wave]);
+            decompress_full_tile<WC, kAcc, kDword>(tab, W, lut, out, q0, lane, stage[wave],
+                                                   nullptr, offs);
         else
             decompress_tail_tile(tab, WC > 0 ? WC : W, lut, n, out, kAcc ? 1 : 0, q0, lane);
         if (!kLoop)
