@@ -589,18 +589,28 @@ __device__ __forceinline__ void qsgd_dequant_sum_body(const PtrTable<int8_t>& ta
 #pragma unroll
             for (int u = 0; u < kDqUnroll; ++u)
                 S[u] = i32x4{0, 0, 0, 0};
-            constexpr int kGroup = WC > 0 ? WC : 4;
-            for (int w0 = 0; w0 < W; w0 += kGroup) {
-                uint32_t words[kGroup][kDqUnroll];
+            // WC > 0: every worker's words in flight together. W at run
+            // time: groups of eight, the next group's words loaded before
+            // this group is summed.
+            constexpr int kGroup = WC > 0 ? WC : 8;
+            auto load_group = [&](uint32_t(&dst)[kGroup][kDqUnroll], int w0) {
 #pragma unroll
                 for (int dw = 0; dw < kGroup; ++dw)
 #pragma unroll
                     for (int u = 0; u < kDqUnroll; ++u)
-                        words[dw][u] = (WC == 0 && w0 + dw >= W)
-                                           ? 0u
-                                           : __builtin_nontemporal_load(
-                                                 reinterpret_cast<const uint32_t*>(tab.p[w0 + dw]) +
-                                                 q0 + size_t(u) * kWave);
+                        dst[dw][u] = (WC == 0 && w0 + dw >= W)
+                                         ? 0u
+                                         : __builtin_nontemporal_load(
+                                               reinterpret_cast<const uint32_t*>(tab.p[w0 + dw]) +
+                                               q0 + size_t(u) * kWave);
+            };
+            uint32_t words[kGroup][kDqUnroll], ahead[WC > 0 ? 1 : kGroup][kDqUnroll];
+            load_group(words, 0);
+            for (int w0 = 0; w0 < W; w0 += kGroup) {
+                if constexpr (WC == 0) {
+                    if (w0 + kGroup < W)
+                        load_group(ahead, w0 + kGroup);
+                }
                 if (kLvAny) {
 #pragma unroll
                     for (int dw = 0; dw < kGroup; ++dw) {
@@ -622,6 +632,13 @@ __device__ __forceinline__ void qsgd_dequant_sum_body(const PtrTable<int8_t>& ta
                         S[u].z += sbyte(words[dw][u], 2);
                         S[u].w += sbyte(words[dw][u], 3);
                     }
+                if constexpr (WC == 0) {
+#pragma unroll
+                    for (int dw = 0; dw < kGroup; ++dw)
+#pragma unroll
+                        for (int u = 0; u < kDqUnroll; ++u)
+                            words[dw][u] = ahead[dw][u];
+                }
             }
             if (kDword) {
                 const int wave = threadIdx.x / kWave;

@@ -187,7 +187,8 @@ def test_qsgd_step_small(gcq, W, n, s, misalign):
     check_deq(out, oracle.qsgd_dequantize(s_or, norm_or, s))
 
 
-@pytest.mark.parametrize("W,n", [(1, 1000), (3, 4097), (8, 100_003), (13, 777)])
+@pytest.mark.parametrize("W,n", [(1, 1000), (3, 4097), (8, 100_003), (13, 777), (17, 100_003),
+                                 (33, 65_537), (64, 20_011)])
 def test_level_sum_of_arbitrary_levels(gcq, W, n):
     """The level sum and dequantize take any int8 levels, -128 and 127
     included: the int32 sums are exact whatever the inputs."""
