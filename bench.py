@@ -50,8 +50,8 @@ PROFILE_STATS = ROOT / "profiles" / "kernel_stats_resnet50_vgg16.md"
 PROFILE_STATS_EXTRA = ROOT / "profiles" / "kernel_stats_bert_multitensor_grandk_ternary.md"
 PROFILE_VALU = ROOT / "profiles" / "valu_busy_all_workloads.md"
 KERNEL_SOURCES = [ROOT / "gradient_compression_quantize_amd" / "csrc" / f
-                  for f in ("gcq_internal.h", "threshold_codes.h", "twobit.hip", "ternary.hip",
-                            "qsgd.hip")]
+                  for f in ("gcq_internal.h", "occupancy.h", "threshold_codes.h", "twobit.hip",
+                            "ternary.hip", "qsgd.hip")]
 
 # The rocprofv3 runs the committed summaries come from (run from the repo
 # root; prof_out/ is scratch output, not kept in the repository).
@@ -85,7 +85,11 @@ PROFILE_COMMANDS = {
     "summary": "python3 bench.py --summarize-profiles prof_out",
 }
 PROFILE_CEILINGS = ROOT / "profiles" / "hbm_ceilings.md"
-CEILING_SOURCES = [ROOT / "gradient_compression_quantize_amd" / "csrc" / "hbm_ceilings.hip"]
+CEILING_SOURCES = [ROOT / "gradient_compression_quantize_amd" / "csrc" / f
+                   for f in ("hbm_ceilings.hip", "occupancy.h")]
+# Resident workgroups per CU each ceiling pattern is also timed at (0: what
+# the kernel's registers allow); a mix's ceiling is its best pattern and cap.
+CEILING_WG_PER_CU = (0, 3, 4, 5)
 
 
 def log(msg: str) -> None:
@@ -270,13 +274,33 @@ def ceiling_kernel_bytes() -> dict:
     }
 
 
+def wg_per_cu_of_lds(lds_bytes: int) -> int:
+    """Resident workgroups per CU that a dispatch's LDS allocation allows on
+    a 160 KB CU (0: no reservation, so the registers decide). Allocations
+    are whole 1280-byte units."""
+    if lds_bytes <= 256:
+        return 0
+    unit = 1280
+    return 163840 // ((lds_bytes + unit - 1) // unit * unit)
+
+
 def summarize_ceilings(d: pathlib.Path) -> pathlib.Path | None:
-    """profiles/hbm_ceilings.md from the kernel trace of --calibrate-ceilings."""
+    """profiles/hbm_ceilings.md from the kernel trace of --calibrate-ceilings:
+    the average duration of each ceiling kernel at each occupancy cap (the
+    dispatch's LDS reservation)."""
     import csv
-    files = list((d / "prof_ceilings").glob("*kernel_stats.csv")) if (d / "prof_ceilings").exists() else []
+    root = d / "prof_ceilings"
+    files = list(root.glob("*kernel_trace.csv")) if root.exists() else []
     if not files:
         return None
-    stats = {r["Name"]: r for r in csv.DictReader(open(files[0]))}
+    durs: dict = {}
+    for r in csv.DictReader(open(files[0])):
+        name = r["Kernel_Name"].split("(")[0].split("::")[-1].strip()
+        if not name.startswith("ceil_"):
+            continue
+        cap = wg_per_cu_of_lds(int(r.get("LDS_Block_Size") or 0))
+        durs.setdefault((name, cap), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     Q = 16384
     lines = [
         "# HBM ceilings of the hot path's access mixes (rocprofv3 kernel trace)",
@@ -292,20 +316,23 @@ def summarize_ceilings(d: pathlib.Path) -> pathlib.Path | None:
         f"{N_C3 // Q * Q:,} values (VGG16, rounded down to a multiple of {Q}) for read, level sum "
         f"and quantize; {N_C2 // Q * Q:,} (ResNet-50, rounded) for write, compress and the "
         "dequantize-sum. Each launch rotates over buffer sets larger than the Infinity Cache. "
-        "`bench.py` times the same kernels live with events in every default run and reports "
-        "each hot-path kernel's rate over its mix's best rate as `frac_of_ceiling`.",
+        "Every pattern runs with what its registers allow per CU (\"-\") and held by an LDS "
+        f"reservation to {', '.join(str(c) for c in CEILING_WG_PER_CU if c)} resident "
+        "workgroups per CU. `bench.py` times the same kernels live with events in every default "
+        "run and reports each hot-path kernel's rate over its mix's best rate as "
+        "`frac_of_ceiling`.",
         "",
-        "| kernel | mix | calls | average us | bytes per launch | GB/s | % of 8 TB/s |",
-        "|---|---|---|---|---|---|---|",
+        "| kernel | mix | workgroups per CU | calls | average us | bytes per launch | GB/s | "
+        "% of 8 TB/s |",
+        "|---|---|---|---|---|---|---|---|",
     ]
     for k, (nb, what) in ceiling_kernel_bytes().items():
-        r = stats.get(k)
-        if not r:
-            continue
-        us = float(r["AverageNs"]) / 1e3
-        gbs = nb / (us * 1e-6) / 1e9
-        lines.append(f"| {k} | {what} | {r['Calls']} | {us:.2f} | {nb:,} | {gbs:,.0f} | "
-                     f"{100 * gbs / HBM_PEAK_GBS:.1f} |")
+        for cap in sorted(c for (name, c) in durs if name == k):
+            v = durs[(k, cap)]
+            us = statistics.mean(v)
+            gbs = nb / (us * 1e-6) / 1e9
+            lines.append(f"| {k} | {what} | {cap or '-'} | {len(v)} | {us:.2f} | {nb:,} | "
+                         f"{gbs:,.0f} | {100 * gbs / HBM_PEAK_GBS:.1f} |")
     lines += ["", f"ceiling_source_sha256: {kernel_source_hash(CEILING_SOURCES)}", ""]
     PROFILE_CEILINGS.write_text("\n".join(lines))
     return PROFILE_CEILINGS
@@ -360,10 +387,12 @@ def summarize_grandk_path(d: pathlib.Path) -> pathlib.Path | None:
     scatter = by("qsgd_dequant_scatter_kernel")
     ceil_gbs = None
     if PROFILE_CEILINGS.exists():
-        m = re.search(r"^\| ceil_write_tile_kernel \|.*?\| ([0-9.]+) \| ([0-9,]+) \| ([0-9,]+) \|",
-                      PROFILE_CEILINGS.read_text(), re.M)
-        if m:
-            ceil_gbs = float(m.group(3).replace(",", ""))
+        # the best write-tile row over the occupancy caps
+        rates = [float(m.group(3).replace(",", "")) for m in re.finditer(
+            r"^\| ceil_write_tile_kernel \|.*?\| ([0-9.]+) \| ([0-9,]+) \| ([0-9,]+) \|",
+            PROFILE_CEILINGS.read_text(), re.M)]
+        if rates:
+            ceil_gbs = max(rates)
     fill_floor = 4 * n / (ceil_gbs * 1e3) if ceil_gbs else None  # us
     B = launch_rows(big)
     S = launch_rows(small) if small else [float("nan")] * 8
@@ -682,8 +711,9 @@ def measure_ceilings(torch, steps: int) -> dict:
     events around `steps` back-to-back launches that rotate over buffer sets
     (each mix's rotation is larger than the 256 MB Infinity Cache). Sizes
     are the workloads' rounded down to whole 16384-value quanta. For each
-    mix: bytes per launch, ms per launch of every pattern, the best pattern
-    and its rate."""
+    mix: bytes per launch, ms per launch of every pattern (each also held to
+    3, 4 and 5 resident workgroups per CU, "@k/CU"), the best one and its
+    rate."""
     from gradient_compression_quantize_amd import ceilings as cl
     Q = cl.quantum()
     n2, n3 = N_C2 // Q * Q, N_C3 // Q * Q
@@ -706,6 +736,21 @@ def measure_ceilings(torch, steps: int) -> dict:
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
 
+    def capped(patterns: dict) -> dict:
+        """{pattern: launches} -> {pattern[@k/CU]: ms}, each pattern at
+        every cap of CEILING_WG_PER_CU ("burst" runs 1024-thread workgroups
+        with LDS of their own and is timed uncapped only)."""
+        ms = {}
+        for cap in CEILING_WG_PER_CU:
+            cl.set_wg_per_cu(cap)
+            for name, fns in patterns.items():
+                if cap == 0:
+                    ms[name] = timed(fns)
+                elif name != "burst":
+                    ms[f"{name}@{cap}/CU"] = timed(fns)
+        cl.set_wg_per_cu(0)
+        return ms
+
     def entry(nbytes, ms_by_pattern, n):
         best = min(ms_by_pattern, key=ms_by_pattern.get)
         gbs = nbytes / (ms_by_pattern[best] / 1e3) / 1e9
@@ -718,50 +763,49 @@ def measure_ceilings(torch, steps: int) -> dict:
     log("ceilings: read (the max-norm's stream)")
     bufs = [zeros(n3) for _ in range(W_C3)]
     sink = zeros(cl.read_sink_words(W_C3, n3), torch.int32)
-    out["read"] = entry(4 * W_C3 * n3, {
-        "chunked": timed([lambda: cl.read(bufs, n3, cl.READ_CHUNKED, sink)]),
-        "tile": timed([lambda: cl.read(bufs, n3, cl.READ_TILE, sink)])}, n3)
+    out["read"] = entry(4 * W_C3 * n3, capped({
+        "chunked": [lambda: cl.read(bufs, n3, cl.READ_CHUNKED, sink)],
+        "tile": [lambda: cl.read(bufs, n3, cl.READ_TILE, sink)]}), n3)
     del bufs, sink
     log("ceilings: level-sum mix")
     lv = [zeros(n3 // 4, torch.int32) for _ in range(W_C3)]
     sums, o3 = zeros(n3, torch.int32), zeros(n3)
     out["levelsum_mix"] = entry((W_C3 + 8) * n3,
-                                {"tile": timed([lambda: cl.levelsum(lv, n3, sums, o3)])}, n3)
+                                capped({"tile": [lambda: cl.levelsum(lv, n3, sums, o3)]}), n3)
     del lv
     log("ceilings: fused quantize-sum mix")
     grads = [zeros(n3) for _ in range(W_C3)]
-    out["quantize_sum_mix"] = entry((4 * W_C3 + 8) * n3, {
-        "tile": timed([lambda: cl.quantize_sum(grads, n3, sums, o3)])}, n3)
+    out["quantize_sum_mix"] = entry((4 * W_C3 + 8) * n3, capped({
+        "tile": [lambda: cl.quantize_sum(grads, n3, sums, o3)]}), n3)
     del grads, sums
     log("ceilings: quantize mix")
     src2, dst2 = [o3, zeros(n3)], [zeros(n3 // 4, torch.int32) for _ in range(2)]
-    out["quantize_mix"] = entry(5 * n3, {"tile": timed(
-        [lambda k=k: cl.quantize(src2[k], n3, dst2[k]) for k in range(2)])}, n3)
+    out["quantize_mix"] = entry(5 * n3, capped({"tile": [
+        lambda k=k: cl.quantize(src2[k], n3, dst2[k]) for k in range(2)]}), n3)
     del src2, dst2, o3
     torch.cuda.empty_cache()
     log("ceilings: write")
     dsts = [zeros(n2) for _ in range(8)]
-    out["write"] = entry(4 * n2, {
-        "tile": timed([lambda d=d: cl.write(d, n2, cl.WRITE_TILE) for d in dsts]),
-        "stride": timed([lambda d=d: cl.write(d, n2, cl.WRITE_STRIDE) for d in dsts])}, n2)
+    out["write"] = entry(4 * n2, capped({
+        "tile": [lambda d=d: cl.write(d, n2, cl.WRITE_TILE) for d in dsts],
+        "stride": [lambda d=d: cl.write(d, n2, cl.WRITE_STRIDE) for d in dsts]}), n2)
     log("ceilings: compress mix")
     bw = cl.block_words(n2)
     sets = [(zeros(n2), zeros(n2), zeros(bw, torch.int32)) for _ in range(6)]
-    out["compress_mix"] = entry(compress_bytes(n2), {"tile": timed(
-        [lambda st=st: cl.compress(st[0], st[1], n2, st[2]) for st in sets])}, n2)
+    out["compress_mix"] = entry(compress_bytes(n2), capped({"tile": [
+        lambda st=st: cl.compress(st[0], st[1], n2, st[2]) for st in sets]}), n2)
     del sets
     log("ceilings: dequantize-sum mix")
     dsets = [[zeros(bw, torch.int32) for _ in range(W_C2)] for _ in range(8)]
-    out["dequant_mix"] = entry(dequant_sum_bytes(n2, W_C2), {
-        name: timed([lambda k=k, pat=pat: cl.dequant(dsets[k], n2, pat, dsts[k])
-                     for k in range(8)])
-        for name, pat in (("tile", cl.DEQ_TILE), ("wide", cl.DEQ_WIDE), ("burst", cl.DEQ_BURST))},
+    out["dequant_mix"] = entry(dequant_sum_bytes(n2, W_C2), capped({
+        name: [lambda k=k, pat=pat: cl.dequant(dsets[k], n2, pat, dsts[k]) for k in range(8)]
+        for name, pat in (("tile", cl.DEQ_TILE), ("wide", cl.DEQ_WIDE), ("burst", cl.DEQ_BURST))}),
         n2)
     log("ceilings: ternary dequantize-sum mix")
     nt = N_C2 // cl.ternary_quantum() * cl.ternary_quantum()
     tsets = [[zeros(3 + nt // 20, torch.int32) for _ in range(W_C2)] for _ in range(8)]
-    out["dequant_ternary_mix"] = entry(4 * W_C2 * (3 + nt // 20) + 4 * nt, {
-        "tile": timed([lambda k=k: cl.dequant_ternary(tsets[k], nt, dsts[k]) for k in range(8)])},
+    out["dequant_ternary_mix"] = entry(4 * W_C2 * (3 + nt // 20) + 4 * nt, capped({
+        "tile": [lambda k=k: cl.dequant_ternary(tsets[k], nt, dsts[k]) for k in range(8)]}),
         nt)
     del dsets, dsts, tsets
     torch.cuda.empty_cache()

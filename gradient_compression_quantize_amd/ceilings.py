@@ -45,7 +45,8 @@ def load() -> ctypes.CDLL:
         L.gcq_ceiling_dequant_ternary.argtypes = [ctypes.POINTER(_vp), _i, _sz, _sz, _vp, _vp]
         L.gcq_ceiling_levelsum.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _vp, _vp]
         L.gcq_ceiling_quantize_sum.argtypes = [ctypes.POINTER(_vp), _i, _sz, _vp, _vp, _vp]
-        for f in ("gcq_ceiling_read", "gcq_ceiling_write", "gcq_ceiling_compress",
+        L.gcq_ceiling_set_wg_per_cu.argtypes = [_i]
+        for f in ("gcq_ceiling_set_wg_per_cu", "gcq_ceiling_read", "gcq_ceiling_write", "gcq_ceiling_compress",
                   "gcq_ceiling_dequant", "gcq_ceiling_dequant_ternary", "gcq_ceiling_quantize",
                   "gcq_ceiling_levelsum", "gcq_ceiling_quantize_sum"):
             getattr(L, f).restype = _i
@@ -86,6 +87,12 @@ def _stream(stream):
 
 def quantum() -> int:
     return int(load().gcq_ceiling_quantum())
+
+
+def set_wg_per_cu(per_cu: int) -> None:
+    """Holds later launches (all but the dequantize burst pattern) to at most
+    per_cu resident workgroups per CU; 0 restores the default."""
+    _check(load().gcq_ceiling_set_wg_per_cu(int(per_cu)))
 
 
 def block_words(n: int) -> int:

@@ -9,6 +9,7 @@
 #include <string>
 
 #include "gcq.h"
+#include "occupancy.h"
 
 #define GCQ_API extern "C" __attribute__((visibility("default")))
 

@@ -29,11 +29,13 @@
 // every tile is whole and no access is conditional.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstddef>
 #include <cstdint>
 #include <string>
 
 #include "gcq_ceilings.h"
+#include "occupancy.h"
 
 #define GCQ_CEIL_API extern "C" __attribute__((visibility("default")))
 
@@ -61,6 +63,12 @@ struct Ptrs {
 };
 
 thread_local std::string g_err;
+
+// Workgroups per CU the 256-thread kernels are held to (0: what their
+// registers allow), through an LDS reservation they never touch.
+std::atomic<int> g_wg_per_cu{0};
+
+size_t cap_lds() { return gcq::lds_for_wg_per_cu(g_wg_per_cu.load(std::memory_order_relaxed)); }
 
 int fail(const std::string& m)
 {
@@ -395,6 +403,14 @@ GCQ_CEIL_API const char* gcq_ceiling_last_error(void) { return g_err.c_str(); }
 
 GCQ_CEIL_API size_t gcq_ceiling_quantum(void) { return kQuantum; }
 
+GCQ_CEIL_API int gcq_ceiling_set_wg_per_cu(int per_cu)
+{
+    if (per_cu < 0)
+        return fail("gcq_ceiling_set_wg_per_cu: per_cu must be >= 0");
+    g_wg_per_cu.store(per_cu, std::memory_order_relaxed);
+    return 0;
+}
+
 GCQ_CEIL_API size_t gcq_ceiling_block_words(size_t n) { return 3 + n / 16 + 4; }
 
 GCQ_CEIL_API size_t gcq_ceiling_ternary_quantum(void) { return 81920; }
@@ -414,7 +430,7 @@ GCQ_CEIL_API int gcq_ceiling_dequant_ternary(const uint32_t* const* blocks, int 
         tab.p[k] = blocks[k];
     }
     hipLaunchKernelGGL(ceil_dequant_ternary_kernel, dim3(unsigned(n / kTernTileVals / kWaves)),
-                       dim3(kThreads), 0, stream, tab, out);
+                       dim3(kThreads), cap_lds(), stream, tab, out);
     return launched("gcq_ceiling_dequant_ternary");
 }
 
@@ -442,14 +458,15 @@ GCQ_CEIL_API int gcq_ceiling_read(const float* const* bufs, int nbufs, size_t n,
         const size_t chunk4 = ((n4 + 4095) / 4096 + 511) / 512 * 512;
         const size_t gx = (n4 + chunk4 - 1) / chunk4;
         hipLaunchKernelGGL(ceil_read_chunked_kernel, dim3(unsigned(gx), unsigned(nbufs)),
-                           dim3(kThreads), 0, stream, tab, n4, chunk4, sink);
+                           dim3(kThreads), cap_lds(), stream, tab, n4, chunk4, sink);
         return launched("gcq_ceiling_read (chunked)");
     }
     if (pattern == GCQ_CEIL_READ_TILE) {
         const size_t tiles = n / kTileVals;
         for (int k = 0; k < nbufs; ++k) {
             hipLaunchKernelGGL(ceil_read_tile_kernel, dim3(unsigned(tiles / kWaves)),
-                               dim3(kThreads), 0, stream, bufs[k], sink + size_t(k) * tiles);
+                               dim3(kThreads), cap_lds(), stream, bufs[k],
+                               sink + size_t(k) * tiles);
             if (int rc = launched("gcq_ceiling_read (tile)"))
                 return rc;
         }
@@ -464,12 +481,12 @@ GCQ_CEIL_API int gcq_ceiling_write(float* dst, size_t n, int pattern, hipStream_
         return fail("gcq_ceiling_write: bad arguments");
     if (pattern == GCQ_CEIL_WRITE_TILE) {
         hipLaunchKernelGGL(ceil_write_tile_kernel, dim3(unsigned(n / kTileVals / kWaves)),
-                           dim3(kThreads), 0, stream, dst, 1.0f);
+                           dim3(kThreads), cap_lds(), stream, dst, 1.0f);
         return launched("gcq_ceiling_write (tile)");
     }
     if (pattern == GCQ_CEIL_WRITE_STRIDE) {
-        hipLaunchKernelGGL(ceil_write_stride_kernel, dim3(2048), dim3(kThreads), 0, stream, dst,
-                           n / 4, 1.0f);
+        hipLaunchKernelGGL(ceil_write_stride_kernel, dim3(2048), dim3(kThreads), cap_lds(), stream,
+                           dst, n / 4, 1.0f);
         return launched("gcq_ceiling_write (stride)");
     }
     return fail("gcq_ceiling_write: unknown pattern");
@@ -482,7 +499,7 @@ GCQ_CEIL_API int gcq_ceiling_compress(const float* a, float* b, size_t n, uint32
         words_cap < gcq_ceiling_block_words(n))
         return fail("gcq_ceiling_compress: bad arguments");
     hipLaunchKernelGGL(ceil_compress_mix_kernel, dim3(unsigned(n / kTileVals / kWaves)),
-                       dim3(kThreads), 0, stream, a, b, words);
+                       dim3(kThreads), cap_lds(), stream, a, b, words);
     return launched("gcq_ceiling_compress");
 }
 
@@ -503,11 +520,11 @@ GCQ_CEIL_API int gcq_ceiling_dequant(const uint32_t* const* blocks, int W, size_
     switch (pattern) {
     case GCQ_CEIL_DEQ_TILE:
         hipLaunchKernelGGL(ceil_dequant_tile_kernel, dim3(unsigned(tiles / kWaves)),
-                           dim3(kThreads), 0, stream, tab, out);
+                           dim3(kThreads), cap_lds(), stream, tab, out);
         return launched("gcq_ceiling_dequant (tile)");
     case GCQ_CEIL_DEQ_WIDE:
         hipLaunchKernelGGL(ceil_dequant_wide_kernel, dim3(unsigned(tiles / 2 / kWaves)),
-                           dim3(kThreads), 0, stream, tab, out);
+                           dim3(kThreads), cap_lds(), stream, tab, out);
         return launched("gcq_ceiling_dequant (wide)");
     case GCQ_CEIL_DEQ_BURST:
         hipLaunchKernelGGL(ceil_dequant_burst_kernel, dim3(unsigned(tiles / kBurstTiles)),
@@ -524,7 +541,7 @@ GCQ_CEIL_API int gcq_ceiling_quantize(const float* src, size_t n, uint32_t* dst,
     if (!whole(n) || !aligned16(src) || !aligned16(dst))
         return fail("gcq_ceiling_quantize: bad arguments");
     hipLaunchKernelGGL(ceil_quantize_mix_kernel, dim3(unsigned(n / kTileVals / kWaves)),
-                       dim3(kThreads), 0, stream, src, dst);
+                       dim3(kThreads), cap_lds(), stream, src, dst);
     return launched("gcq_ceiling_quantize");
 }
 
@@ -540,7 +557,7 @@ GCQ_CEIL_API int gcq_ceiling_levelsum(const uint32_t* const* levels, int W, size
         tab.p[k] = levels[k];
     }
     hipLaunchKernelGGL(ceil_levelsum_mix_kernel, dim3(unsigned(n / 512 / kWaves)),
-                       dim3(kThreads), 0, stream, tab, sums, out);
+                       dim3(kThreads), cap_lds(), stream, tab, sums, out);
     return launched("gcq_ceiling_levelsum");
 }
 
@@ -556,6 +573,6 @@ GCQ_CEIL_API int gcq_ceiling_quantize_sum(const float* const* grads, int W, size
         tab.p[k] = grads[k];
     }
     hipLaunchKernelGGL(ceil_quantize_sum_mix_kernel, dim3(unsigned(n / kTileVals / kWaves)),
-                       dim3(kThreads), 0, stream, tab, sums, out);
+                       dim3(kThreads), cap_lds(), stream, tab, sums, out);
     return launched("gcq_ceiling_quantize_sum");
 }

@@ -90,6 +90,9 @@ constexpr unsigned kMaxPartialsPerWorker = 4096;
 constexpr int kMaxAbsUnroll = 2;
 constexpr size_t kMaxAbsMinChunk = 2048;  // float4 slots per workgroup, at least
 constexpr size_t kMaxAbsChunkAlign = 32;  // float4 slots: chunks start on 512 B
+// At most 3 workgroups per CU (an LDS reservation; the registers allow 8):
+// 647 against 658 us for 8 x 138M values; 4 per CU gave 653.
+constexpr int kMaxAbsWgPerCu = 3;
 
 struct MaxNormGrid {
     unsigned gx;    // workgroups per worker = partial maxima per worker
@@ -282,6 +285,10 @@ __device__ __forceinline__ uint32_t pack_levels4(const int32_t t[4])
 // (the usual case).
 constexpr int kQUnroll = 4;
 constexpr size_t kQTile = size_t(kWave) * kQUnroll;
+// The aligned quantize runs at most 5 workgroups per CU, held there by an
+// LDS reservation: 106 against 116 us per 138M values with the 8 its
+// registers allow (7 and 6 per CU: 115-116 us; 4: 107 us; 3: 121 us).
+constexpr int kQuantizeWgPerCu = 5;
 
 // Float4 slots tb + u kWave + lane (u < U) of g, one per lane per u. kDword:
 // g is only 4-byte aligned, so the tile's 4 U kWave values come in as
@@ -510,6 +517,10 @@ __device__ __forceinline__ int sbyte(uint32_t w, int k)
 // of four).
 constexpr int kDqUnroll = 2;
 constexpr size_t kDqTile = size_t(kWave) * kDqUnroll;
+// At most 5 workgroups per CU (an LDS reservation; the registers allow 8).
+// Over 138M values: W = 8, 359-360 against 366 us (4 per CU: 358; 3: 359-363);
+// W = 2, 219-220 against 224-228 us (4 per CU: 227; 3: 257).
+constexpr int kLevelSumWgPerCu = 5;
 
 __device__ __forceinline__ void dequant_store(float norm, float s_f, i32x4 S, int32_t* sums,
                                               float* out, size_t q)
@@ -1280,8 +1291,9 @@ namespace {
 int launch_maxnorm(const PtrTable<float>& tab, int W, size_t n, const MaxNormGrid& mg,
                    float* partials, float* norm, hipStream_t stream)
 {
-    hipLaunchKernelGGL(maxabs_partial_kernel, dim3(mg.gx, unsigned(W)), dim3(kThreads), 0, stream,
-                       tab, n, mg.chunk4, partials);
+    hipLaunchKernelGGL(maxabs_partial_kernel, dim3(mg.gx, unsigned(W)), dim3(kThreads),
+                       lds_cap(maxabs_partial_kernel, kMaxAbsWgPerCu), stream, tab, n, mg.chunk4,
+                       partials);
     if (int rc = check_launch("qsgd_global_maxnorm (partials)"))
         return rc;
     hipLaunchKernelGGL(max_final_kernel, dim3(1), dim3(kFinalThreads), 0, stream, partials,
@@ -1438,17 +1450,19 @@ GCQ_API int qsgd_maxnorm_quantize(const float* grad, size_t n, const float* norm
     const int vec = 1;
     const bool dword = !aligned16(grad);
     const int vec_kernel = aligned16(grad) ? 1 : 0;
-#define GCQ_Q_LAUNCH(K, L, V)                                                                 \
-    hipLaunchKernelGGL((K<L>), grid, block, 0, stream, grad, n, norm, s24, uint32_t(seed),   \
+#define GCQ_Q_LAUNCH(K, L, V, LDS)                                                            \
+    hipLaunchKernelGGL((K<L>), grid, block, LDS, stream, grad, n, norm, s24, uint32_t(seed), \
                        uint32_t(seed >> 32), worker, levels, V)
     if (dword && loop)
-        GCQ_Q_LAUNCH(qsgd_quantize_dword_kernel, true, vec);
+        GCQ_Q_LAUNCH(qsgd_quantize_dword_kernel, true, vec, 0);
     else if (dword)
-        GCQ_Q_LAUNCH(qsgd_quantize_dword_kernel, false, vec);
+        GCQ_Q_LAUNCH(qsgd_quantize_dword_kernel, false, vec, 0);
     else if (loop)
-        GCQ_Q_LAUNCH(qsgd_quantize_kernel, true, vec_kernel);
+        GCQ_Q_LAUNCH(qsgd_quantize_kernel, true, vec_kernel,
+                     lds_cap(qsgd_quantize_kernel<true>, kQuantizeWgPerCu));
     else
-        GCQ_Q_LAUNCH(qsgd_quantize_kernel, false, vec_kernel);
+        GCQ_Q_LAUNCH(qsgd_quantize_kernel, false, vec_kernel,
+                     lds_cap(qsgd_quantize_kernel<false>, kQuantizeWgPerCu));
 #undef GCQ_Q_LAUNCH
     return check_launch("qsgd_maxnorm_quantize");
 }
@@ -1528,8 +1542,10 @@ GCQ_API int qsgd_dequant_sum(const int8_t* const* levels, int W, size_t n, const
             hipLaunchKernelGGL((qsgd_dequant_sum_dword_kernel<k>), grid, block, 0, stream,  \
                                tab, W, n, norm, s_f, sums, out, vec);                       \
         else                                                                                \
-            hipLaunchKernelGGL((qsgd_dequant_sum_kernel<k>), grid, block, 0, stream, tab, W, \
-                               n, norm, s_f, sums, out, out_aligned ? vec : 0);             \
+            hipLaunchKernelGGL((qsgd_dequant_sum_kernel<k>), grid, block,                   \
+                               lds_cap(qsgd_dequant_sum_kernel<k>, kLevelSumWgPerCu),       \
+                               stream, tab, W, n, norm, s_f, sums, out,                     \
+                               out_aligned ? vec : 0);                                      \
         break;
             GCQ_DQ_CASE(1)
             GCQ_DQ_CASE(2)
@@ -1545,8 +1561,10 @@ GCQ_API int qsgd_dequant_sum(const int8_t* const* levels, int W, size_t n, const
                 hipLaunchKernelGGL((qsgd_dequant_sum_dword_kernel<0>), grid, block, 0, stream,
                                    tab, W, n, norm, s_f, sums, out, vec);
             else
-                hipLaunchKernelGGL((qsgd_dequant_sum_kernel<0>), grid, block, 0, stream, tab, W,
-                                   n, norm, s_f, sums, out, out_aligned ? vec : 0);
+                hipLaunchKernelGGL((qsgd_dequant_sum_kernel<0>), grid, block,
+                                   lds_cap(qsgd_dequant_sum_kernel<0>, kLevelSumWgPerCu),
+                                   stream, tab, W, n, norm, s_f, sums, out,
+                                   out_aligned ? vec : 0);
         }
         return check_launch("qsgd_dequant_sum");
     }

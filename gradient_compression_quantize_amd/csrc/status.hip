@@ -1,4 +1,4 @@
-// status.hip -- per-thread error state of libgcq.so.
+// status.hip -- per-thread error state of libgcq.so and its host launch helpers.
 #include "gcq_internal.h"
 
 #include <cstdlib>

@@ -41,6 +41,14 @@ constexpr int kSlots = 5;                              // float4 slots per lane 
 constexpr int kWordValues = 20;                        // values per 32-bit element
 constexpr size_t kTileF4 = size_t(kWave) * kSlots;     // 320 float4 slots
 constexpr size_t kTileElems = kTileF4 * 4;             // 1280 values
+// Resident workgroups per CU, held by an LDS reservation the kernels never
+// touch (0: what their registers and own LDS allow). The aligned compress
+// measured the same at 3 to 6 per CU (51.0-51.4 us), so it keeps its 8. The
+// dequantize-sum, which its own LDS holds to 7 per CU at W <= 8, runs at 6:
+// 28.5 against 29.3 us at W = 8 (21.9 against 21.6 at W = 2; 3 and 4 per CU
+// were slower).
+constexpr int kCompressWgPerCu = 0;
+constexpr int kDequantWgPerCu = 6;
 static_assert(kTileElems == size_t(kWave) * kWordValues, "one tile = one element per lane");
 
 __host__ __device__ inline size_t payload_words(size_t n)
@@ -559,7 +567,10 @@ void launch_decompress_vec(const PtrTable<uint32_t>& tab, int W, size_t n, float
                                block, 0, stream, tab, W, n, out, ntiles);                   \
         else                                                                                \
             hipLaunchKernelGGL((decompress_ternary_vec_kernel<k, false, kLoop>), grid,      \
-                               block, 0, stream, tab, W, n, out, ntiles);                   \
+                               block,                                                       \
+                               lds_cap((decompress_ternary_vec_kernel<k, false, kLoop>),    \
+                                       kDequantWgPerCu),                                    \
+                               stream, tab, W, n, out, ntiles);                             \
         break;
         GCQ_TDEC_CASE(1)
         GCQ_TDEC_CASE(2)
@@ -575,7 +586,9 @@ void launch_decompress_vec(const PtrTable<uint32_t>& tab, int W, size_t n, float
             hipLaunchKernelGGL((decompress_ternary_dword_kernel<0, false, kLoop>), grid, block, 0,
                                stream, tab, W, n, out, ntiles);
         else
-            hipLaunchKernelGGL((decompress_ternary_vec_kernel<0, false, kLoop>), grid, block, 0,
+            hipLaunchKernelGGL((decompress_ternary_vec_kernel<0, false, kLoop>), grid, block,
+                               lds_cap((decompress_ternary_vec_kernel<0, false, kLoop>),
+                                       kDequantWgPerCu),
                                stream, tab, W, n, out, ntiles);
     }
 }
@@ -626,17 +639,19 @@ GCQ_API int compress_ternary(const float* grad, float* residual, size_t n, float
     const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
     const bool loop = tiles_need_loop(ntiles);
     const bool dword = n > 0 && !(aligned16(grad) && aligned16(residual));
-#define GCQ_TCOMP(K, L)                                                                        \
-    hipLaunchKernelGGL((K<L>), grid, block, 0, stream, grad, residual, n, neg_threshold,     \
+#define GCQ_TCOMP(K, L, LDS)                                                                   \
+    hipLaunchKernelGGL((K<L>), grid, block, LDS, stream, grad, residual, n, neg_threshold,   \
                        pos_threshold, n_f, compr, ntiles)
     if (loop && dword)
-        GCQ_TCOMP(compress_ternary_dword_kernel, true);
+        GCQ_TCOMP(compress_ternary_dword_kernel, true, 0);
     else if (loop)
-        GCQ_TCOMP(compress_ternary_vec_kernel, true);
+        GCQ_TCOMP(compress_ternary_vec_kernel, true,
+                  lds_cap(compress_ternary_vec_kernel<true>, kCompressWgPerCu));
     else if (dword)
-        GCQ_TCOMP(compress_ternary_dword_kernel, false);
+        GCQ_TCOMP(compress_ternary_dword_kernel, false, 0);
     else
-        GCQ_TCOMP(compress_ternary_vec_kernel, false);
+        GCQ_TCOMP(compress_ternary_vec_kernel, false,
+                  lds_cap(compress_ternary_vec_kernel<false>, kCompressWgPerCu));
 #undef GCQ_TCOMP
     return check_launch("compress_ternary");
 }

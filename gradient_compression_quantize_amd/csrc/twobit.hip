@@ -36,6 +36,17 @@ constexpr int kUnroll = 4;                             // float4 per lane per ti
 constexpr size_t kTileF4 = size_t(kWave) * kUnroll;    // 256 float4 slots
 constexpr size_t kTileElems = kTileF4 * 4;             // 1024 values
 constexpr size_t kBlockElems = kTileElems * kWavesPerBlock;  // 4096 values
+// The aligned compress runs at most 3 workgroups (12 waves) per CU, held
+// there by an LDS reservation: measured ~1.4% faster over 8 x 25.6M values
+// than the 8 its registers allow (49.5 against 50.2 us per launch); 4 per
+// CU gained ~0.9%, 2 per CU nothing.
+constexpr int kCompressWgPerCu = 3;
+// The many-tensor compress likewise, at 3 per CU: 213 against 219 us over
+// the BERT-Base list (4 per CU: 215 us). The dequantize-sum keeps the 8 its
+// registers allow: every cap from 3 to 6 per CU made it 2-20% slower, its
+// LDS decode needing the waves to hide latency.
+constexpr int kMultiWgPerCu = 3;
+constexpr int kDequantWgPerCu = 0;
 // A tile is 64 words of codes, one per lane: the cross-lane moves that
 // gather and scatter words rely on it.
 static_assert(kUnroll == 4 && kTileF4 == 256, "one tile = 64 words of codes");
@@ -596,11 +607,15 @@ GCQ_API int compress_2bit(const float* grad, float* residual, size_t n, float ne
         const size_t ntiles = ceil_div(n, kTileElems);
         const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
         if (tiles_need_loop(ntiles))
-            hipLaunchKernelGGL(compress_2bit_vec_kernel<true>, grid, block, 0, stream, grad,
-                               residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles);
+            hipLaunchKernelGGL(compress_2bit_vec_kernel<true>, grid, block,
+                               lds_cap(compress_2bit_vec_kernel<true>, kCompressWgPerCu),
+                               stream, grad, residual, n, neg_threshold, pos_threshold, n_f,
+                               compr, ntiles);
         else
-            hipLaunchKernelGGL(compress_2bit_vec_kernel<false>, grid, block, 0, stream, grad,
-                               residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles);
+            hipLaunchKernelGGL(compress_2bit_vec_kernel<false>, grid, block,
+                               lds_cap(compress_2bit_vec_kernel<false>, kCompressWgPerCu),
+                               stream, grad, residual, n, neg_threshold, pos_threshold, n_f,
+                               compr, ntiles);
     } else {
         const size_t ntiles = ceil_div(n, kTileElems);
         const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
@@ -637,7 +652,9 @@ static void launch_decompress_vec(const PtrTable<uint32_t>& tab, int W, size_t n
                                block, 0, stream, tab, W, n, out, ntiles);                  \
         else                                                                               \
             hipLaunchKernelGGL((decompress_2bit_vec_kernel<k, false, kLoop>), grid, block, \
-                               0, stream, tab, W, n, out, ntiles);                         \
+                               lds_cap((decompress_2bit_vec_kernel<k, false, kLoop>),      \
+                                       kDequantWgPerCu),                                   \
+                               stream, tab, W, n, out, ntiles);                            \
         break;
         GCQ_DEC_CASE(1)
         GCQ_DEC_CASE(2)
@@ -653,7 +670,9 @@ static void launch_decompress_vec(const PtrTable<uint32_t>& tab, int W, size_t n
             hipLaunchKernelGGL((decompress_2bit_dword_kernel<0, false, kLoop>), grid, block, 0,
                                stream, tab, W, n, out, ntiles);
         else
-            hipLaunchKernelGGL((decompress_2bit_vec_kernel<0, false, kLoop>), grid, block, 0,
+            hipLaunchKernelGGL((decompress_2bit_vec_kernel<0, false, kLoop>), grid, block,
+                               lds_cap((decompress_2bit_vec_kernel<0, false, kLoop>),
+                                       kDequantWgPerCu),
                                stream, tab, W, n, out, ntiles);
     }
 }
@@ -809,12 +828,14 @@ GCQ_API int compress_2bit_multi(gc_plan* plan, float neg_threshold, float pos_th
                                    std::to_string(cur));
     const size_t blocks = std::min(plan->nchunks, max_grid_blocks());
     if (blocks < plan->nchunks)
-        hipLaunchKernelGGL(compress_2bit_multi_kernel<true>, dim3(blocks), dim3(kThreads), 0,
-                           stream, plan->d_chunks, plan->nchunks, neg_threshold, pos_threshold,
+        hipLaunchKernelGGL(compress_2bit_multi_kernel<true>, dim3(blocks), dim3(kThreads),
+                           lds_cap(compress_2bit_multi_kernel<true>, kMultiWgPerCu), stream,
+                           plan->d_chunks, plan->nchunks, neg_threshold, pos_threshold,
                            compr_base);
     else
-        hipLaunchKernelGGL(compress_2bit_multi_kernel<false>, dim3(blocks), dim3(kThreads), 0,
-                           stream, plan->d_chunks, plan->nchunks, neg_threshold, pos_threshold,
+        hipLaunchKernelGGL(compress_2bit_multi_kernel<false>, dim3(blocks), dim3(kThreads),
+                           lds_cap(compress_2bit_multi_kernel<false>, kMultiWgPerCu), stream,
+                           plan->d_chunks, plan->nchunks, neg_threshold, pos_threshold,
                            compr_base);
     return check_launch("compress_2bit_multi");
 }

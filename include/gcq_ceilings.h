@@ -45,6 +45,12 @@ const char* gcq_ceiling_last_error(void);
 /* n must be a multiple of this many values (16384). */
 size_t gcq_ceiling_quantum(void);
 
+/* Holds every later launch of the 256-thread kernels below (all but the
+ * dequantize burst pattern) to at most per_cu resident workgroups per CU,
+ * through an LDS reservation the kernels never touch; 0 restores what their
+ * registers allow. Process-wide. Returns -1 for per_cu < 0. */
+int gcq_ceiling_set_wg_per_cu(int per_cu);
+
 /* 32-bit words each block of gcq_ceiling_compress / gcq_ceiling_dequant
  * must hold for n values: the 2-bit block's 3 + n/16, plus 4 of padding
  * that the 16-byte-aligned patterns may read. */

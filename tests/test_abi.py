@@ -88,6 +88,10 @@ def test_ceilings_library_exports_exactly_its_header_and_refuses_bad_sizes():
     assert L.gcq_ceiling_levelsum(arr, 8, q - 16, FAKE, FAKE, None) == -1
     assert L.gcq_ceiling_dequant(arr, 8, q, 16, 0, FAKE, None) == -1
     assert L.gcq_ceiling_compress(FAKE, FAKE, q, FAKE, 16, None) == -1
+    # the occupancy cap: negative counts are refused, 0..n accepted (host state only)
+    assert L.gcq_ceiling_set_wg_per_cu(-1) == -1
+    assert "per_cu" in L.gcq_ceiling_last_error().decode()
+    assert L.gcq_ceiling_set_wg_per_cu(3) == 0 and L.gcq_ceiling_set_wg_per_cu(0) == 0
 
 
 @pytest.mark.parametrize("n", [0, 1, 15, 16, 17, 4096, 25_557_032, 2 ** 33 + 5, 2 ** 64 - 1])
