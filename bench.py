@@ -184,6 +184,20 @@ def _read_counters(path: pathlib.Path):
     return per
 
 
+def _read_counters_fewest_lds(path: pathlib.Path):
+    """{kernel: [value per dispatch]} keeping, for each kernel, only the
+    dispatches of the instantiation that declares the least LDS of its own
+    (the counter CSV's LDS_Block_Size). The dequantize-sums declare more for
+    run-time W than for compile-time W <= 8, so this keeps the W = 8
+    launches of the workloads' steps and drops the many-worker runs'."""
+    import csv
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        per[r["Kernel_Name"]][int(r.get("LDS_Block_Size") or 0)].append(float(r["Counter_Value"]))
+    return {k: v[min(v)] for k, v in per.items()}
+
+
 def copy_calibration(d: pathlib.Path):
     """(FETCH scale, WRITE scale, copy kernel, FETCH KiB, WRITE KiB) from the
     1 GiB device copy of --calibrate-copy: bytes = counter KiB x 1024 x
@@ -200,13 +214,17 @@ def copy_calibration(d: pathlib.Path):
 
 
 def _read_counters_by_name(path: pathlib.Path):
-    """{kernel: {counter: [value per dispatch]}} from a rocprofv3 counter CSV."""
+    """{kernel: {counter: [value per dispatch]}} from a rocprofv3 counter CSV,
+    for each kernel only the dispatches of the instantiation that declares
+    the least LDS of its own (as _read_counters_fewest_lds)."""
     import csv
     import collections
-    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    per = collections.defaultdict(
+        lambda: collections.defaultdict(lambda: collections.defaultdict(list)))
     for r in csv.DictReader(open(path)):
-        per[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
-    return per
+        per[r["Kernel_Name"]][int(r.get("LDS_Block_Size") or 0)][r["Counter_Name"]].append(
+            float(r["Counter_Value"]))
+    return {k: v[min(v)] for k, v in per.items()}
 
 
 def summarize_valu(d: pathlib.Path) -> pathlib.Path | None:
@@ -232,7 +250,9 @@ def summarize_valu(d: pathlib.Path) -> pathlib.Path | None:
         "max(GRBM_GUI_ACTIVE): the share of the kernel's GPU time in which the CUs issue vector "
         "ALU work. SQ_INSTS_VALU and SQ_INSTS_LDS count wave-level instructions per dispatch. "
         "A kernel near its HBM roofline shows a low VALUBusy; one bound by its arithmetic "
-        "shows a high one.",
+        "shows a high one. Each row counts one instantiation of its kernel, the one that "
+        "declares the least LDS of its own: for the dequantize-sums the W = 8 launches, not "
+        "the many-worker runs' run-time-W ones.",
         "",
         "| kernel | dispatches | VALUBusy % | SQ_INSTS_VALU per dispatch | SQ_INSTS_LDS per dispatch |",
         "|---|---|---|---|---|",
@@ -274,33 +294,34 @@ def ceiling_kernel_bytes() -> dict:
     }
 
 
-def wg_per_cu_of_lds(lds_bytes: int) -> int:
-    """Resident workgroups per CU that a dispatch's LDS allocation allows on
-    a 160 KB CU (0: no reservation, so the registers decide). Allocations
-    are whole 1280-byte units."""
-    if lds_bytes <= 256:
-        return 0
-    unit = 1280
-    return 163840 // ((lds_bytes + unit - 1) // unit * unit)
-
-
 def summarize_ceilings(d: pathlib.Path) -> pathlib.Path | None:
     """profiles/hbm_ceilings.md from the kernel trace of --calibrate-ceilings:
-    the average duration of each ceiling kernel at each occupancy cap (the
-    dispatch's LDS reservation)."""
+    the average duration of each ceiling kernel at each occupancy cap.
+    measure_ceilings times every pattern once per cap of CEILING_WG_PER_CU,
+    in that order, with the same number of launches each time, so a
+    kernel's launches in time order fall into that many equal runs, one per
+    cap (the trace's LDS_Block_Size shows the kernel's own LDS only). A
+    kernel timed uncapped only (the burst pattern) has one run."""
     import csv
     root = d / "prof_ceilings"
     files = list(root.glob("*kernel_trace.csv")) if root.exists() else []
     if not files:
         return None
-    durs: dict = {}
+    launches: dict = {}
     for r in csv.DictReader(open(files[0])):
         name = r["Kernel_Name"].split("(")[0].split("::")[-1].strip()
-        if not name.startswith("ceil_"):
-            continue
-        cap = wg_per_cu_of_lds(int(r.get("LDS_Block_Size") or 0))
-        durs.setdefault((name, cap), []).append(
-            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        if name.startswith("ceil_"):
+            launches.setdefault(name, []).append(
+                (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    durs: dict = {}
+    for name, v in launches.items():
+        v.sort()
+        caps = CEILING_WG_PER_CU if name != "ceil_dequant_burst_kernel" else (0,)
+        if len(v) % len(caps):
+            raise ValueError(f"{name}: {len(v)} launches do not split into {len(caps)} caps")
+        m = len(v) // len(caps)
+        for i, cap in enumerate(caps):
+            durs[(name, cap)] = [us for _, us in v[i * m:(i + 1) * m]]
     Q = 16384
     lines = [
         "# HBM ceilings of the hot path's access mixes (rocprofv3 kernel trace)",
@@ -536,12 +557,14 @@ def summarize_profiles(out_dir: str) -> None:
     }
     f_scale, w_scale, copy_name, f_kib, w_kib = copy_calibration(d)
     copy_bytes = 4 << 28
-    fetch = _read_counters(next((d / "pmc_fetch").glob("*counter_collection.csv")))
-    write = _read_counters(next((d / "pmc_write").glob("*counter_collection.csv")))
+    fetch = _read_counters_fewest_lds(next((d / "pmc_fetch").glob("*counter_collection.csv")))
+    write = _read_counters_fewest_lds(next((d / "pmc_write").glob("*counter_collection.csv")))
     sizes = [int(v) for v in __import__("synthetic_inputs").bert_base_sizes()]
     if (d / "pmc_fetch_extra").exists() and (d / "pmc_write_extra").exists():
-        fx = _read_counters(next((d / "pmc_fetch_extra").glob("*counter_collection.csv")))
-        wx = _read_counters(next((d / "pmc_write_extra").glob("*counter_collection.csv")))
+        fx = _read_counters_fewest_lds(
+            next((d / "pmc_fetch_extra").glob("*counter_collection.csv")))
+        wx = _read_counters_fewest_lds(
+            next((d / "pmc_write_extra").glob("*counter_collection.csv")))
         tw = ternary_words(n2)
         extra_algo = {
             "compress_2bit_multi_kernel": (8 * sum(sizes), multi_bytes(sizes) - 8 * sum(sizes)),
@@ -590,7 +613,9 @@ def summarize_profiles(out_dir: str) -> None:
               "block); dequantize-sum reads W blocks and writes "
               "n fp32; max-norm reads W n fp32; quantize reads n fp32 and writes n int8; the "
               "level sum reads W n int8 and writes n int32 + n fp32; the fused quantize-sum "
-              "reads W n fp32 and writes n int32 + n fp32.", "",
+              "reads W n fp32 and writes n int32 + n fp32. The dequantize-sum rows count the "
+              "W = 8 launches only (told apart from the many-worker runs' run-time-W "
+              "instantiation by the LDS the kernel declares).", "",
               "Machine-readable (bench.py reads these while the kernel sources are unchanged):",
               "", f"kernel_source_sha256: {kernel_source_hash()}", *machine, ""]
     PROFILE_TRAFFIC.write_text("\n".join(lines))

@@ -8,6 +8,8 @@ import pathlib
 import subprocess
 import sys
 
+import pytest
+
 ROOT = pathlib.Path(__file__).resolve().parent.parent
 
 
@@ -114,3 +116,56 @@ def test_grandk_summary_needs_the_trace(tmp_path):
     sys.path.insert(0, str(ROOT))
     import bench
     assert bench.summarize_grandk_path(tmp_path) is None
+
+
+def test_ceiling_summary_splits_each_kernel_by_cap(tmp_path, monkeypatch):
+    """measure_ceilings times each pattern once per cap, in the order of
+    CEILING_WG_PER_CU, with equal launch counts: the summary assigns a
+    kernel's launches in time order to the caps in equal runs, and the burst
+    pattern (uncapped only) to one run."""
+    sys.path.insert(0, str(ROOT))
+    import bench
+    rows, t = [], 0
+    caps = bench.CEILING_WG_PER_CU
+    for i, _ in enumerate(caps):
+        for _ in range(4):  # 4 launches per cap, 10, 20, 30, ... us
+            rows.append(("ceil_compress_mix_kernel", t, t + 10_000 * (i + 1), 6240))
+            t += 100_000
+    rows.append(("ceil_dequant_burst_kernel", t, t + 7_000, 1560))
+    _write_trace(tmp_path / "prof_ceilings" / "ceil_kernel_trace.csv", rows)
+    out = tmp_path / "ceil.md"
+    monkeypatch.setattr(bench, "PROFILE_CEILINGS", out)
+    assert bench.summarize_ceilings(tmp_path) == out
+    text = out.read_text()
+    for i, cap in enumerate(caps):
+        assert f"| ceil_compress_mix_kernel | compress mix | {cap or '-'} | 4 | {10.0 * (i + 1):.2f} |" in text
+    assert "| ceil_dequant_burst_kernel | dequantize-sum mix, workgroup bursts | - | 1 | 7.00 |" in text
+    # launches that do not split evenly over the caps are an error, not a guess
+    rows.append(("ceil_compress_mix_kernel", t, t + 5_000, 6240))
+    _write_trace(tmp_path / "prof_ceilings" / "ceil_kernel_trace.csv", rows)
+    with pytest.raises(ValueError):
+        bench.summarize_ceilings(tmp_path)
+
+
+def test_counter_rows_keep_the_instantiation_with_the_least_own_lds(tmp_path):
+    """A counter CSV's dispatches of one kernel name but different template
+    instantiations (told apart by the LDS the kernel declares) are not
+    averaged together: the W = 8 dequantize-sum keeps its own rows."""
+    sys.path.insert(0, str(ROOT))
+    import bench
+    import csv
+    p = tmp_path / "c.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "LDS_Block_Size", "Counter_Name",
+                                          "Counter_Value"])
+        w.writeheader()
+        for lds, v in ((21504, 10.0), (29696, 80.0), (21504, 12.0), (29696, 40.0)):
+            w.writerow({"Kernel_Name": "decompress_ternary_vec_kernel", "LDS_Block_Size": lds,
+                        "Counter_Name": "FETCH_SIZE", "Counter_Value": v})
+        w.writerow({"Kernel_Name": "compress_ternary_vec_kernel", "LDS_Block_Size": 5120,
+                    "Counter_Name": "FETCH_SIZE", "Counter_Value": 3.0})
+    got = bench._read_counters_fewest_lds(p)
+    assert got == {"decompress_ternary_vec_kernel": [10.0, 12.0],
+                   "compress_ternary_vec_kernel": [3.0]}
+    by_name = bench._read_counters_by_name(p)
+    assert by_name["decompress_ternary_vec_kernel"]["FETCH_SIZE"] == [10.0, 12.0]
