@@ -289,6 +289,11 @@ constexpr size_t kQTile = size_t(kWave) * kQUnroll;
 // LDS reservation: 106 against 116 us per 138M values with the 8 its
 // registers allow (7 and 6 per CU: 115-116 us; 4: 107 us; 3: 121 us).
 constexpr int kQuantizeWgPerCu = 5;
+// Levels 1-3 bytes off 4-byte alignment: 6 per CU, 112-113 against 115-116
+// us (5 per CU: 112-114; 3 and 4: 118-133). The kernels for gradients only
+// 4-byte aligned gained nothing from a cap and keep what their own LDS
+// allows.
+constexpr int kQuantizeBytesWgPerCu = 6;
 
 // Float4 slots tb + u kWave + lane (u < U) of g, one per lane per u. kDword:
 // g is only 4-byte aligned, so the tile's 4 U kWave values come in as
@@ -521,6 +526,10 @@ constexpr size_t kDqTile = size_t(kWave) * kDqUnroll;
 // Over 138M values: W = 8, 359-360 against 366 us (4 per CU: 358; 3: 359-363);
 // W = 2, 219-220 against 224-228 us (4 per CU: 227; 3: 257).
 constexpr int kLevelSumWgPerCu = 5;
+// Sums and outputs only 4-byte aligned (their tiles staged through LDS): 3
+// per CU, 399-400 against 424-429 us at W = 8. Levels at byte offsets
+// 1-3 keep what their registers allow: a cap made them up to 60% slower.
+constexpr int kLevelSumDwordWgPerCu = 3;
 
 __device__ __forceinline__ void dequant_store(float norm, float s_f, i32x4 S, int32_t* sums,
                                               float* out, size_t q)
@@ -1432,8 +1441,10 @@ GCQ_API int qsgd_maxnorm_quantize(const float* grad, size_t n, const float* norm
         const uint32_t sh = uint32_t(reinterpret_cast<uintptr_t>(levels) & 3u);
         const bool g16 = aligned16(grad);
 #define GCQ_QB_LAUNCH(L, D)                                                                     \
-    hipLaunchKernelGGL((qsgd_quantize_bytes_kernel<L, D>), grid, block, 0, stream, grad, n, norm, \
-                       s24, uint32_t(seed), uint32_t(seed >> 32), worker, levels, sh)
+    hipLaunchKernelGGL((qsgd_quantize_bytes_kernel<L, D>), grid, block,                           \
+                       lds_cap((qsgd_quantize_bytes_kernel<L, D>), kQuantizeBytesWgPerCu),        \
+                       stream, grad, n, norm, s24, uint32_t(seed), uint32_t(seed >> 32), worker,  \
+                       levels, sh)
         if (loop && g16)
             GCQ_QB_LAUNCH(true, false);
         else if (loop)
@@ -1539,8 +1550,10 @@ GCQ_API int qsgd_dequant_sum(const int8_t* const* levels, int W, size_t n, const
 #define GCQ_DQ_CASE(k)                                                                      \
     case k:                                                                                 \
         if (dword)                                                                          \
-            hipLaunchKernelGGL((qsgd_dequant_sum_dword_kernel<k>), grid, block, 0, stream,  \
-                               tab, W, n, norm, s_f, sums, out, vec);                       \
+            hipLaunchKernelGGL((qsgd_dequant_sum_dword_kernel<k>), grid, block,             \
+                               lds_cap(qsgd_dequant_sum_dword_kernel<k>,                    \
+                                       kLevelSumDwordWgPerCu),                              \
+                               stream, tab, W, n, norm, s_f, sums, out, vec);               \
         else                                                                                \
             hipLaunchKernelGGL((qsgd_dequant_sum_kernel<k>), grid, block,                   \
                                lds_cap(qsgd_dequant_sum_kernel<k>, kLevelSumWgPerCu),       \
@@ -1558,8 +1571,10 @@ GCQ_API int qsgd_dequant_sum(const int8_t* const* levels, int W, size_t n, const
 #undef GCQ_DQ_CASE
         default:
             if (dword)
-                hipLaunchKernelGGL((qsgd_dequant_sum_dword_kernel<0>), grid, block, 0, stream,
-                                   tab, W, n, norm, s_f, sums, out, vec);
+                hipLaunchKernelGGL((qsgd_dequant_sum_dword_kernel<0>), grid, block,
+                                   lds_cap(qsgd_dequant_sum_dword_kernel<0>,
+                                           kLevelSumDwordWgPerCu),
+                                   stream, tab, W, n, norm, s_f, sums, out, vec);
             else
                 hipLaunchKernelGGL((qsgd_dequant_sum_kernel<0>), grid, block,
                                    lds_cap(qsgd_dequant_sum_kernel<0>, kLevelSumWgPerCu),

@@ -36,10 +36,11 @@ constexpr int kUnroll = 4;                             // float4 per lane per ti
 constexpr size_t kTileF4 = size_t(kWave) * kUnroll;    // 256 float4 slots
 constexpr size_t kTileElems = kTileF4 * 4;             // 1024 values
 constexpr size_t kBlockElems = kTileElems * kWavesPerBlock;  // 4096 values
-// The aligned compress runs at most 3 workgroups (12 waves) per CU, held
-// there by an LDS reservation: measured ~1.4% faster over 8 x 25.6M values
-// than the 8 its registers allow (49.5 against 50.2 us per launch); 4 per
-// CU gained ~0.9%, 2 per CU nothing.
+// The compress runs at most 3 workgroups (12 waves) per CU, held there by
+// an LDS reservation: measured ~1.4% faster over 8 x 25.6M values than the
+// 8 its registers allow (49.5 against 50.2 us per launch); 4 per CU gained
+// ~0.9%, 2 per CU nothing. Buffers only 4-byte aligned: 54.8-54.9 against
+// 55.3-55.6 us.
 constexpr int kCompressWgPerCu = 3;
 // The many-tensor compress likewise, at 3 per CU: 213 against 219 us over
 // the BERT-Base list (4 per CU: 215 us). The dequantize-sum keeps the 8 its
@@ -620,11 +621,15 @@ GCQ_API int compress_2bit(const float* grad, float* residual, size_t n, float ne
         const size_t ntiles = ceil_div(n, kTileElems);
         const dim3 grid(grid_for_tiles(ntiles)), block(kThreads);
         if (tiles_need_loop(ntiles))
-            hipLaunchKernelGGL(compress_2bit_dword_kernel<true>, grid, block, 0, stream, grad,
-                               residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles);
+            hipLaunchKernelGGL(compress_2bit_dword_kernel<true>, grid, block,
+                               lds_cap(compress_2bit_dword_kernel<true>, kCompressWgPerCu),
+                               stream, grad, residual, n, neg_threshold, pos_threshold, n_f,
+                               compr, ntiles);
         else
-            hipLaunchKernelGGL(compress_2bit_dword_kernel<false>, grid, block, 0, stream, grad,
-                               residual, n, neg_threshold, pos_threshold, n_f, compr, ntiles);
+            hipLaunchKernelGGL(compress_2bit_dword_kernel<false>, grid, block,
+                               lds_cap(compress_2bit_dword_kernel<false>, kCompressWgPerCu),
+                               stream, grad, residual, n, neg_threshold, pos_threshold, n_f,
+                               compr, ntiles);
     }
     return check_launch("compress_2bit");
 }
