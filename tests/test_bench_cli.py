@@ -1,7 +1,8 @@
 """bench.py's command-line contract, on the CPU: more than one GPU is
 refused with a message (this library runs on one GPU), and a run with no
 GPU visible fails with a message instead of printing a result line. Also
-the rule that names a kernel's roofline bound."""
+the rule that names a kernel's roofline bound, and the profile summaries
+read from synthetic rocprofv3 CSV files."""
 import json
 import os
 import pathlib
