@@ -202,3 +202,19 @@ def test_qsgd_step_in_hip_graph(gcq):
         graph.replay()
         gu.sync()
         check(t, grads)
+
+
+def test_capture_before_any_eager_call(gcq):
+    """The launch paths' one-time queries (each capped kernel's own LDS, the
+    device's LDS size) first run inside a graph capture, in a fresh child
+    process (capture_first_check.py): the capture succeeds and its replays
+    match the oracle."""
+    import os
+    import subprocess
+    import sys
+    announce("graph captured before any eager library call (child process)")
+    script = os.path.join(os.path.dirname(__file__), "capture_first_check.py")
+    res = subprocess.run([sys.executable, "-u", script], capture_output=True, text=True,
+                         timeout=110)
+    print(res.stdout[-2000:], res.stderr[-2000:])
+    assert res.returncode == 0 and res.stdout.strip().endswith("OK")
