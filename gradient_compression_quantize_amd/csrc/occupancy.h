@@ -12,20 +12,39 @@
 
 namespace gcq {
 
-// Dynamic LDS, in bytes, whose reservation holds a kernel that declares
-// `own` bytes of LDS of its own to `per_cu` resident workgroups per CU of the
-// current device; 0 (no limit) when per_cu < 1 or the device's LDS cannot
-// express that cap. The kernel never touches the reservation. Some streaming
-// kernels move HBM faster with fewer waves in flight per CU than their
-// registers allow.
+// Dynamic LDS, in bytes, that holds a workgroup declaring `own` bytes of LDS
+// of its own to `per_cu` resident workgroups on a CU with `lds_per_cu` bytes
+// of LDS and at most `lds_per_block` per workgroup; 0 (no limit) when
+// per_cu < 1 or those sizes cannot express that cap.
+//
+// The CU hands out LDS in units coarser than 512 bytes: 27,136 bytes per
+// workgroup left room for 5 of them in 160 KB, not 6. A workgroup's LDS (its
+// own plus the reservation) is made 256 bytes short of a multiple of 2560
+// bytes, which rounds up to that multiple in any unit from 512 to 2560 bytes
+// that divides it; at 256-byte units it is taken as is, and one more
+// workgroup still does not fit.
+constexpr size_t lds_reservation(size_t lds_per_cu, size_t lds_per_block, int per_cu,
+                                 size_t own)
+{
+    constexpr size_t kUnit = 2560, kSlack = 256;
+    if (per_cu < 1)
+        return 0;
+    const size_t whole = lds_per_cu / size_t(per_cu) / kUnit * kUnit;
+    if (whole <= kSlack + own || whole > lds_per_block)
+        return 0;
+    const size_t total = whole - kSlack;  // own + reservation
+    // per_cu fit (each takes at most `whole`); one more does not
+    if (size_t(per_cu + 1) * total <= lds_per_cu)
+        return 0;
+    return total - own;
+}
+
+// lds_reservation for the current device (its LDS sizes read once per
+// device). The kernel never touches the reservation. Some streaming kernels
+// move HBM faster with fewer waves in flight per CU than their registers
+// allow.
 inline size_t lds_for_wg_per_cu(int per_cu, size_t own = 0)
 {
-    // The CU hands out LDS in units coarser than 512 bytes: 27,136 bytes per
-    // workgroup left room for 5 of them in 160 KB, not 6. A workgroup's LDS
-    // (its own plus the reservation) is made 256 bytes short of a multiple
-    // of 2560 bytes, which rounds up to that multiple in any unit from 512
-    // to 2560 bytes that divides it.
-    constexpr size_t kUnit = 2560, kSlack = 256;
     constexpr int kMaxDevices = 64;
     static std::atomic<int> lds_per_cu[kMaxDevices] = {};
     static std::atomic<int> lds_per_block[kMaxDevices] = {};
@@ -34,24 +53,17 @@ inline size_t lds_for_wg_per_cu(int per_cu, size_t own = 0)
         return 0;
     int cu = lds_per_cu[dev].load(std::memory_order_relaxed);
     int blk = lds_per_block[dev].load(std::memory_order_relaxed);
-    if (cu == 0 || blk == 0) {
+    if (cu <= 0 || blk <= 0) {
         if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
                 hipSuccess ||
             hipDeviceGetAttribute(&blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
-                hipSuccess)
+                hipSuccess ||
+            cu <= 0 || blk <= 0)
             return 0;
         lds_per_cu[dev].store(cu, std::memory_order_relaxed);
         lds_per_block[dev].store(blk, std::memory_order_relaxed);
     }
-    const size_t L = size_t(cu > 0 ? cu : 0);
-    const size_t whole = L / size_t(per_cu) / kUnit * kUnit;
-    if (whole <= kSlack + own)
-        return 0;
-    const size_t total = whole - kSlack;  // own + reservation
-    // per_cu fit (each takes at most `whole`); one more does not
-    if (whole > size_t(blk > 0 ? blk : 0) || size_t(per_cu + 1) * total <= L)
-        return 0;
-    return total - own;
+    return lds_reservation(size_t(cu), size_t(blk), per_cu, own);
 }
 
 // LDS a kernel declares itself (hipFuncGetAttributes), cached per kernel;
