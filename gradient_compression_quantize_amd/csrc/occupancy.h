@@ -49,7 +49,13 @@ inline size_t lds_for_wg_per_cu(int per_cu, size_t own = 0)
     static std::atomic<int> lds_per_cu[kMaxDevices] = {};
     static std::atomic<int> lds_per_block[kMaxDevices] = {};
     int dev = 0;
-    if (per_cu < 1 || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    if (per_cu < 1)
+        return 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();  // the launch that follows reports its own status
+        return 0;
+    }
+    if (dev < 0 || dev >= kMaxDevices)
         return 0;
     int cu = lds_per_cu[dev].load(std::memory_order_relaxed);
     int blk = lds_per_block[dev].load(std::memory_order_relaxed);
@@ -58,8 +64,10 @@ inline size_t lds_for_wg_per_cu(int per_cu, size_t own = 0)
                 hipSuccess ||
             hipDeviceGetAttribute(&blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
                 hipSuccess ||
-            cu <= 0 || blk <= 0)
+            cu <= 0 || blk <= 0) {
+            (void)hipGetLastError();  // the launch that follows reports its own status
             return 0;
+        }
         lds_per_cu[dev].store(cu, std::memory_order_relaxed);
         lds_per_block[dev].store(blk, std::memory_order_relaxed);
     }
@@ -76,8 +84,11 @@ inline bool kernel_own_lds(const void* fn, size_t* own)
     auto it = cache.find(fn);
     if (it == cache.end()) {
         hipFuncAttributes a{};
-        const long long v =
-            hipFuncGetAttributes(&a, fn) == hipSuccess ? (long long)a.sharedSizeBytes : -1;
+        long long v = -1;
+        if (hipFuncGetAttributes(&a, fn) == hipSuccess)
+            v = (long long)a.sharedSizeBytes;
+        else
+            (void)hipGetLastError();  // the launch that follows reports its own status
         it = cache.emplace(fn, v).first;
     }
     if (it->second < 0)
